@@ -1,0 +1,179 @@
+"""fp64 CPU oracle for vertical-slash sparse prefill -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It is independent of the HIP path: it
+shares no kernels, headers, helpers or constants with
+``vertical_slash_sparse_amd`` and neither imports the other.  The arithmetic
+lives in ``vs_oracle.c`` (plain C, fp64, OpenMP over rows); this module only
+builds that file with gcc and marshals numpy arrays to it.
+
+Every function here is pinned by ``tests/test_oracle.py`` against brute
+force, closed forms, library routines or hand-derived values.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vs_oracle.c")
+_LIB = os.path.join(_HERE, "libvs_oracle.so")
+
+BF16, F32, F64 = 0, 1, 2
+VERTICAL, SLASH = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile vs_oracle.c with gcc (fp64, no FMA contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                               "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.vso_attn_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, P, P, i32, P, P, i32,
+                                    P, P, i64, P, P, i32]
+        L.vso_attn_rows.restype = i32
+        L.vso_index.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, i32, P, P, i32]
+        L.vso_index.restype = i32
+        L.vso_select.argtypes = [P, i32, i32, i32, f64, i32, P, P, P, P]
+        L.vso_select.restype = i32
+        L.vso_exp_spec.argtypes = [ctypes.c_float]
+        L.vso_exp_spec.restype = ctypes.c_float
+        L.vso_mass_u.argtypes = [ctypes.c_float]
+        L.vso_mass_u.restype = ctypes.c_uint64
+        L.vso_row_set.argtypes = [P, P, i32, P, P, i32, i32, i32, P]
+        L.vso_row_set.restype = i32
+        L.vso_pair_count.argtypes = [P, P, i32, P, P, i32, i32, i32]
+        L.vso_pair_count.restype = i64
+        L.vso_num_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"unsupported oracle input dtype {a.dtype}")
+
+
+def _c(a, dtype=None):
+    return np.ascontiguousarray(a if dtype is None else np.asarray(a, dtype=dtype))
+
+
+def num_threads() -> int:
+    return int(lib().vso_num_threads())
+
+
+def attn(q, k, v, vidx, vcnt, soff, scnt, scale=None, rows=None, nthreads=0):
+    """Sparse causal attention over the vertical-slash index sets.
+
+    q [hq,n,d], k/v [hkv,n,d] as bf16 bits (uint16), fp32 or fp64; index lists
+    int32 [hkv, cap] ascending with counts [hkv].  ``rows`` is None (every row)
+    or an int array [m, 2] of (head, row).  Returns (out [m, d], lse [m]) in
+    fp64, or ([hq, n, d], [hq, n]) when ``rows`` is None."""
+    q, k, v = _c(q), _c(k), _c(v)
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    assert k.shape == v.shape == (hkv, n, d) and q.dtype == k.dtype == v.dtype
+    vidx, vcnt, soff, scnt = (_c(x, np.int32) for x in (vidx, vcnt, soff, scnt))
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    full = rows is None
+    if full:
+        hh, ii = np.meshgrid(np.arange(hq), np.arange(n), indexing="ij")
+        rows = np.stack([hh.ravel(), ii.ravel()], axis=1)
+    rows = _c(rows, np.int32).reshape(-1, 2)
+    rh, ri = _c(rows[:, 0]), _c(rows[:, 1])
+    m = rows.shape[0]
+    out = np.empty((m, d), dtype=np.float64)
+    lse = np.empty(m, dtype=np.float64)
+    rc = lib().vso_attn_rows(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), hq, hkv, n, d, scale,
+                             _ptr(vidx), _ptr(vcnt), vidx.shape[1], _ptr(soff), _ptr(scnt),
+                             soff.shape[1], _ptr(rh), _ptr(ri), m, _ptr(out), _ptr(lse),
+                             int(nthreads))
+    if rc:
+        raise ValueError("oracle attn: invalid arguments")
+    if full:
+        return out.reshape(hq, n, d), lse.reshape(hq, n)
+    return out, lse
+
+
+def index(k, v, w1, w2, nthreads=0):
+    """VSIndexer logits (vlog, slog) [hkv, n] fp64 from k/v [hkv,n,d]."""
+    k, v, w1, w2 = _c(k), _c(v), _c(w1), _c(w2)
+    hkv, n, d = k.shape
+    hidden = w1.shape[0]
+    assert w1.shape == (hidden, 2 * d) and w2.shape == (2, hidden)
+    vlog = np.empty((hkv, n), dtype=np.float64)
+    slog = np.empty((hkv, n), dtype=np.float64)
+    rc = lib().vso_index(_ptr(k), _ptr(v), _dtype_code(k), hkv, n, d, hidden, _ptr(w1), _ptr(w2),
+                         _dtype_code(w1), _ptr(vlog), _ptr(slog), int(nthreads))
+    if rc:
+        raise ValueError("oracle index: invalid arguments")
+    return vlog, slog
+
+
+def select(logit, kind, mass, cap, return_ut=False):
+    """Cumulative-mass selection per head.  logit fp32 [heads, n].
+    Returns (idx int32 [heads, cap], count int32 [heads])."""
+    logit = _c(logit, np.float32)
+    heads, n = logit.shape
+    idx = np.empty((heads, cap), dtype=np.int32)
+    cnt = np.empty(heads, dtype=np.int32)
+    U = np.empty(heads, dtype=np.uint64)
+    T = np.empty(heads, dtype=np.uint64)
+    rc = lib().vso_select(_ptr(logit), heads, n, int(kind), float(mass), int(cap), _ptr(idx),
+                          _ptr(cnt), _ptr(U), _ptr(T))
+    if rc:
+        raise ValueError("oracle select: invalid arguments")
+    return (idx, cnt, U, T) if return_ut else (idx, cnt)
+
+
+def exp_spec(x) -> np.ndarray:
+    f = lib().vso_exp_spec
+    return np.array([f(float(t)) for t in np.asarray(x, dtype=np.float32).ravel()],
+                    dtype=np.float32).reshape(np.shape(x))
+
+
+def mass_u(x) -> np.ndarray:
+    f = lib().vso_mass_u
+    return np.array([f(float(t)) for t in np.asarray(x, dtype=np.float32).ravel()],
+                    dtype=np.uint64).reshape(np.shape(x))
+
+
+def row_set(vidx, vcnt, soff, scnt, g, i):
+    vidx, vcnt, soff, scnt = (_c(x, np.int32) for x in (vidx, vcnt, soff, scnt))
+    buf = np.empty(i + 1, dtype=np.int32)
+    m = lib().vso_row_set(_ptr(vidx), _ptr(vcnt), vidx.shape[1], _ptr(soff), _ptr(scnt),
+                          soff.shape[1], int(g), int(i), _ptr(buf))
+    return buf[:m].copy()
+
+
+def pair_count(vidx, vcnt, soff, scnt, g, n) -> int:
+    vidx, vcnt, soff, scnt = (_c(x, np.int32) for x in (vidx, vcnt, soff, scnt))
+    return int(lib().vso_pair_count(_ptr(vidx), _ptr(vcnt), vidx.shape[1], _ptr(soff),
+                                    _ptr(scnt), soff.shape[1], int(g), int(n)))

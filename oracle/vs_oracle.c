@@ -1,0 +1,330 @@
+/*
+ * vs_oracle.c -- plain, slow, fp64 CPU oracle for vertical-slash sparse prefill.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant with the HIP path and must never be used to
+ * produce a product result.
+ *
+ * What it follows (VSPrefill summary pages on gist.science, paper 2603.04460):
+ *  - the pattern: "Technical Summary, 2. Methodology, Core Concept:
+ *    Vertical-Slash Pattern" (English page) and "2. Methodik, A. Das
+ *    Vertical-Slash-Muster" (German page, which writes the slash as a
+ *    relative shift i-j): a query attends to selected key columns and to
+ *    keys at selected relative offsets;
+ *  - the indexer: "Key Components, 1. VSIndexer": a shared-weight two-layer
+ *    linear net over concat(K with RoPE, V) with separate vertical and slash
+ *    output heads;
+ *  - selection: "3. Adaptive Inference Pipeline, Dynamic Budgeting": the
+ *    fewest top-scored indices whose cumulative predicted mass reaches a
+ *    threshold;
+ *  - attention: "Fused Kernel Execution": attention restricted to the merged
+ *    index set.  Here that is written out as its plain definition (two-pass
+ *    softmax per row), not as a tiled kernel.
+ *
+ * Readings where the pages are silent (all documented with the build):
+ *  scale is a caller argument (1/sqrt(d) by default); index sets belong to a KV
+ *  head and are shared by its query heads (h -> g = h / (hq/hkv)); the slash
+ *  offset is o = i - j >= 0 and applies to row i only when o <= i; a key in
+ *  both sets counts once; a vertical column c is visible to row i only if
+ *  c <= i; a row with no visible key gets out = 0 and lse = -inf.
+ *
+ * Selection arithmetic is fixed exactly so that an integer decision (the
+ * budget K) has one answer: m = max score in fp32; x = score - m in fp32;
+ * u = 0 if x < -32 else rint(exp_spec(x) * 2^32) as an unsigned 64-bit
+ * integer; U = sum u; T = ceil(mass * U) in IEEE double; order by (score
+ * descending, candidate index ascending); K = length of the shortest prefix
+ * with cumulative u >= T, then min(K, cap).  exp_spec is Cody and Waite's
+ * range reduction (W. J. Cody, W. Waite, "Software Manual for the Elementary
+ * Functions", 1980) with a two-piece ln 2, followed by the degree-7 Taylor
+ * polynomial of e^r evaluated by Horner's rule with fused multiply-adds, all
+ * in fp32.  Build with -ffp-contract=off so no other fusion happens.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { VSO_BF16 = 0, VSO_F32 = 1, VSO_F64 = 2 };
+enum { VSO_VERTICAL = 0, VSO_SLASH = 1 };
+
+/* ---------------------------------------------------------------- input decode */
+
+static double load_elem(const void* base, int dtype, int64_t i) {
+  if (dtype == VSO_BF16) {
+    uint32_t w = (uint32_t)((const uint16_t*)base)[i] << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+  }
+  if (dtype == VSO_F32) return (double)((const float*)base)[i];
+  return ((const double*)base)[i];
+}
+
+static void load_row(const void* base, int dtype, int64_t off, int len, double* dst) {
+  for (int t = 0; t < len; ++t) dst[t] = load_elem(base, dtype, off + t);
+}
+
+/* ---------------------------------------------------------------- the pattern */
+
+/* Index set of row i for one KV head: every j with 0 <= j <= i such that j is
+ * a selected column or i - j is a selected offset, each j once, ascending.
+ * Built by walking the two sorted lists together: columns <= i ascending, and
+ * keys i - o for offsets o <= i taken from the largest offset down.
+ * Returns |S_i|. */
+static int row_set(const int32_t* cols, int ncols, const int32_t* offs, int noffs, int i,
+                   int32_t* out) {
+  int nc = 0;
+  while (nc < ncols && cols[nc] <= i) ++nc;
+  int no = 0;
+  while (no < noffs && offs[no] <= i) ++no;
+  int a = 0, b = no - 1, m = 0;
+  while (a < nc || b >= 0) {
+    int ja = a < nc ? cols[a] : INT32_MAX;
+    int jb = b >= 0 ? i - offs[b] : INT32_MAX;
+    int j = ja < jb ? ja : jb;
+    if (ja == j) ++a;
+    if (jb == j) --b;
+    out[m++] = j;
+  }
+  return m;
+}
+
+int vso_row_set(const int32_t* vidx, const int32_t* vcnt, int cap_v, const int32_t* soff,
+                const int32_t* scnt, int cap_s, int g, int i, int32_t* out) {
+  return row_set(vidx + (int64_t)g * cap_v, vcnt[g], soff + (int64_t)g * cap_s, scnt[g], i, out);
+}
+
+/* sum over rows of |S_i| for one KV head, by building every row's set */
+int64_t vso_pair_count(const int32_t* vidx, const int32_t* vcnt, int cap_v, const int32_t* soff,
+                       const int32_t* scnt, int cap_s, int g, int n) {
+  int32_t* buf = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) total += vso_row_set(vidx, vcnt, cap_v, soff, scnt, cap_s, g, i, buf);
+  free(buf);
+  return total;
+}
+
+/* ---------------------------------------------------------------- attention */
+
+/* For every requested (head, row): out_r = sum_{j in S_i} softmax_j(scale*q_i.k_j) v_j
+ * and lse_r = log sum_{j in S_i} exp(scale*q_i.k_j), in fp64, two passes. */
+int vso_attn_rows(const void* q, const void* k, const void* v, int dtype, int hq, int hkv, int n,
+                  int d, double scale, const int32_t* vidx, const int32_t* vcnt, int cap_v,
+                  const int32_t* soff, const int32_t* scnt, int cap_s, const int32_t* row_h,
+                  const int32_t* row_i, int64_t nrows, double* out, double* lse, int nthreads) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || n <= 0 || d <= 0) return 1;
+  const int group = hq / hkv;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int err = 0;
+#pragma omp parallel
+  {
+    int32_t* set = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    double* qi = (double*)malloc(sizeof(double) * (size_t)d);
+    double* kj = (double*)malloc(sizeof(double) * (size_t)d);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; ++r) {
+      int h = row_h[r], i = row_i[r];
+      if (h < 0 || h >= hq || i < 0 || i >= n) {
+        err = 1;
+        continue;
+      }
+      int g = h / group;
+      int m = vso_row_set(vidx, vcnt, cap_v, soff, scnt, cap_s, g, i, set);
+      double* o = out + r * d;
+      if (m == 0) {
+        for (int t = 0; t < d; ++t) o[t] = 0.0;
+        lse[r] = -INFINITY;
+        continue;
+      }
+      load_row(q, dtype, ((int64_t)h * n + i) * d, d, qi);
+      double mx = -INFINITY;
+      for (int a = 0; a < m; ++a) {
+        load_row(k, dtype, ((int64_t)g * n + set[a]) * d, d, kj);
+        double dot = 0.0;
+        for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];
+        s[a] = scale * dot;
+        if (s[a] > mx) mx = s[a];
+      }
+      double l = 0.0;
+      for (int t = 0; t < d; ++t) acc[t] = 0.0;
+      for (int a = 0; a < m; ++a) {
+        double p = exp(s[a] - mx);
+        l += p;
+        load_row(v, dtype, ((int64_t)g * n + set[a]) * d, d, kj);
+        for (int t = 0; t < d; ++t) acc[t] += p * kj[t];
+      }
+      for (int t = 0; t < d; ++t) o[t] = acc[t] / l;
+      lse[r] = mx + log(l);
+    }
+    free(set);
+    free(s);
+    free(qi);
+    free(kj);
+    free(acc);
+  }
+  return err;
+}
+
+/* ---------------------------------------------------------------- the indexer */
+
+/* Per KV head g and position j: x = [k_j | v_j] (2d values), h = max(0, W1 x)
+ * (W1 is [hidden][2d]), then vlog = W2[0].h and slog = W2[1].h (W2 is
+ * [2][hidden]); no biases; one weight set for every head; fp64 throughout. */
+int vso_index(const void* k, const void* v, int dtype, int hkv, int n, int d, int hidden,
+              const void* w1, const void* w2, int wdtype, double* vlog, double* slog,
+              int nthreads) {
+  if (hkv <= 0 || n <= 0 || d <= 0 || hidden <= 0) return 1;
+  const int d2 = 2 * d;
+  double* W1 = (double*)malloc(sizeof(double) * (size_t)hidden * d2);
+  double* W2 = (double*)malloc(sizeof(double) * 2 * (size_t)hidden);
+  load_row(w1, wdtype, 0, hidden * d2, W1);
+  load_row(w2, wdtype, 0, 2 * hidden, W2);
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  const int64_t total = (int64_t)hkv * n;
+#pragma omp parallel
+  {
+    double* x = (double*)malloc(sizeof(double) * (size_t)d2);
+    double* h = (double*)malloc(sizeof(double) * (size_t)hidden);
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < total; ++r) {
+      load_row(k, dtype, r * d, d, x);
+      load_row(v, dtype, r * d, d, x + d);
+      for (int t = 0; t < hidden; ++t) {
+        double a = 0.0;
+        for (int c = 0; c < d2; ++c) a += W1[(int64_t)t * d2 + c] * x[c];
+        h[t] = a > 0.0 ? a : 0.0;
+      }
+      double sv = 0.0, ss = 0.0;
+      for (int t = 0; t < hidden; ++t) {
+        sv += W2[t] * h[t];
+        ss += W2[hidden + t] * h[t];
+      }
+      vlog[r] = sv;
+      slog[r] = ss;
+    }
+    free(x);
+    free(h);
+  }
+  free(W1);
+  free(W2);
+  return 0;
+}
+
+/* ---------------------------------------------------------------- selection */
+
+/* e^x in fp32 for x in [-32, 0]: x = k ln2 + r with k = rint(x log2 e), r
+ * reduced against a two-piece ln 2 (the high piece has few enough bits that
+ * k * ln2_hi is exact); e^r by the degree-7 Taylor polynomial; then scale by
+ * 2^k.  Constants are the fp32 values nearest to log2 e, to ln 2 cut to its
+ * leading bits plus the fp32 remainder, and to 1/k!. */
+float vso_exp_spec(float x) {
+  const float log2e = 0x1.715476p+0f;
+  const float ln2_hi = 0x1.62e4p-1f;
+  const float ln2_lo = 0x1.7f7d1cp-20f;
+  float kf = rintf(x * log2e);
+  float r = fmaf(-kf, ln2_hi, x);
+  r = fmaf(-kf, ln2_lo, r);
+  float p = 0x1.a01a02p-13f;     /* 1/7! */
+  p = fmaf(p, r, 0x1.6c16c2p-10f); /* 1/6! */
+  p = fmaf(p, r, 0x1.111112p-7f);  /* 1/5! */
+  p = fmaf(p, r, 0x1.555556p-5f);  /* 1/4! */
+  p = fmaf(p, r, 0x1.555556p-3f);  /* 1/3! */
+  p = fmaf(p, r, 0.5f);            /* 1/2! */
+  p = fmaf(p, r, 1.0f);
+  p = fmaf(p, r, 1.0f);
+  return ldexpf(p, (int)kf);
+}
+
+/* quantised mass of a score that sits x below the maximum */
+uint64_t vso_mass_u(float x) {
+  if (x < -32.0f) return 0;
+  double e = (double)vso_exp_spec(x) * 4294967296.0;
+  return (uint64_t)nearbyint(e);
+}
+
+typedef struct {
+  float s;
+  int32_t c;
+} cand_t;
+
+static int cand_cmp(const void* pa, const void* pb) {
+  const cand_t* a = (const cand_t*)pa;
+  const cand_t* b = (const cand_t*)pb;
+  if (a->s > b->s) return -1;
+  if (a->s < b->s) return 1;
+  return (a->c > b->c) - (a->c < b->c);
+}
+
+static int int_cmp(const void* pa, const void* pb) {
+  int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+  return (a > b) - (a < b);
+}
+
+/* Per head: candidates c = 0..n-1 with score logit[c] (VERTICAL: c is a
+ * column) or logit[n-1-c] (SLASH: c is an offset, scored where its diagonal
+ * meets the last row).  Writes the selected candidates ascending into
+ * idx[h][0..K), -1 into idx[h][K..cap), and K into count[h].  Optionally
+ * returns U and T per head.  Returns 0, or 1 on invalid arguments. */
+int vso_select(const float* logit, int heads, int n, int kind, double mass, int cap, int32_t* idx,
+               int32_t* count, uint64_t* out_U, uint64_t* out_T) {
+  if (heads <= 0 || n <= 0 || !(mass > 0.0 && mass <= 1.0) || cap < 1 || cap > n) return 1;
+  if (kind != VSO_VERTICAL && kind != VSO_SLASH) return 1;
+  cand_t* cs = (cand_t*)malloc(sizeof(cand_t) * (size_t)n);
+  int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+  for (int h = 0; h < heads; ++h) {
+    const float* row = logit + (int64_t)h * n;
+    float mx = -INFINITY;
+    for (int c = 0; c < n; ++c) {
+      float s = kind == VSO_VERTICAL ? row[c] : row[n - 1 - c];
+      if (s == 0.0f) s = 0.0f; /* -0 and +0 are one score */
+      cs[c].s = s;
+      cs[c].c = c;
+      if (s > mx) mx = s;
+    }
+    uint64_t U = 0;
+    for (int c = 0; c < n; ++c) U += vso_mass_u(cs[c].s - mx);
+    uint64_t T = (uint64_t)ceil(mass * (double)U);
+    qsort(cs, (size_t)n, sizeof(cand_t), cand_cmp);
+    uint64_t cum = 0;
+    int K = n;
+    for (int a = 0; a < n; ++a) {
+      cum += vso_mass_u(cs[a].s - mx);
+      if (cum >= T) {
+        K = a + 1;
+        break;
+      }
+    }
+    if (K > cap) K = cap;
+    for (int a = 0; a < K; ++a) sel[a] = cs[a].c;
+    qsort(sel, (size_t)K, sizeof(int32_t), int_cmp);
+    for (int a = 0; a < cap; ++a) idx[(int64_t)h * cap + a] = a < K ? sel[a] : -1;
+    count[h] = K;
+    if (out_U) out_U[h] = U;
+    if (out_T) out_T[h] = T;
+  }
+  free(cs);
+  free(sel);
+  return 0;
+}
+
+int vso_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
