@@ -1,0 +1,146 @@
+/*
+ * vs.h -- C ABI of the vertical-slash sparse prefill library (libvs.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (VSPrefill; gist.science summaries of arXiv 2603.04460, English
+ * page, Technical Summary section 2 "Methodology") prefills causal attention
+ * over a per-head index set made of "vertical" key columns and "slash"
+ * diagonals (keys at a fixed relative offset i - j from the query, German
+ * page section 2.A).  The index sets come from a small indexer over
+ * concat(K with RoPE, V) (section 2, "Key Components 1. VSIndexer") followed
+ * by cumulative-threshold budgeting (section 2, "3. Adaptive Inference
+ * Pipeline, Dynamic Budgeting"), and attention runs over the merged index
+ * lists (same section, "Fused Kernel Execution").  The three calls below are
+ * those three steps.
+ *
+ * Conventions shared by every call
+ *  - All pointers except `ws_bytes`-style sizes are DEVICE pointers into
+ *    memory the caller allocated on the current HIP device.  The library
+ *    never allocates, frees or synchronises; every call only enqueues work
+ *    on `stream` (NULL = the default stream) and returns.
+ *  - Tensors are dense row-major with batch 1: Q [h_q][n][d], K and V
+ *    [h_kv][n][d]; nothing is strided.
+ *  - Inputs are never written.  Outputs are fully overwritten.
+ *  - Host-checkable problems (null pointers, bad sizes, unsupported shapes,
+ *    too-small workspace) return a status before anything is launched.  A
+ *    launch failure returns VS_ERR_HIP.  No C++ exception crosses the ABI.
+ *  - Calls are stateless and reentrant; two calls may run concurrently on
+ *    different streams if their outputs and workspaces do not overlap.
+ */
+#ifndef VS_H_
+#define VS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VS_OK = 0,
+  VS_ERR_INVALID = 1,     /* null pointer, size out of range, bad enum     */
+  VS_ERR_UNSUPPORTED = 2, /* valid but not built: head dim, group size     */
+  VS_ERR_WORKSPACE = 3,   /* workspace smaller than *_workspace_bytes()    */
+  VS_ERR_HIP = 4          /* a HIP launch or runtime call failed           */
+} vs_status;
+
+typedef enum { VS_BF16 = 0, VS_F32 = 1 } vs_dtype;
+
+typedef enum { VS_VERTICAL = 0, VS_SLASH = 1 } vs_kind;
+
+/* ------------------------------------------------------------------ indexer
+ * VSIndexer (English page, section 2, "Key Components 1. VSIndexer"): a
+ * shared-weight two-layer linear network over x_j = [K_rope[g][j][:] | V[g][j][:]]
+ * (2d values) with separate vertical and slash output heads:
+ *     h_j = max(0, W1 x_j)            (hidden values, no bias)
+ *     vlog[g][j] = W2[0] . h_j,  slog[g][j] = W2[1] . h_j
+ * One weight set serves every KV head.
+ *   k_rope, v : bf16 [h_kv][n][d]     (K after rotary embedding, and V)
+ *   w1        : bf16 [hidden][2d]     (columns 0..d-1 act on K, d..2d-1 on V)
+ *   w2        : bf16 [2][hidden]      (row 0 vertical head, row 1 slash head)
+ *   vlog,slog : fp32 [h_kv][n]        (outputs, indexed by position j)
+ * First layer: bf16 MFMA with fp32 accumulation.  Second layer: fp32.
+ * Supported: d == 128, hidden == 128.  n >= 1, h_kv >= 1. */
+vs_status vs_index(const void* k_rope, const void* v, int h_kv, int n, int d, int hidden,
+                   const void* w1, const void* w2, float* vlog, float* slog,
+                   hipStream_t stream);
+
+/* ---------------------------------------------------------------- selection
+ * Cumulative-threshold budgeting (English page, section 2, "3. Adaptive
+ * Inference Pipeline, Dynamic Budgeting"): per head, the fewest top-scored
+ * candidates whose softmax mass reaches `mass` of the total, capped at `cap`,
+ * found without a full sort.
+ *   VERTICAL: candidate c is key column c, its score is logit[h][c].
+ *   SLASH:    candidate c is the offset o = c, scored where its diagonal meets
+ *             the last query row: logit[h][n-1-o].  idx then holds offsets.
+ * The mass arithmetic is fixed exactly so that the budget is an exact
+ * integer decision: m = max score (fp32, -0 == +0); x = score - m (fp32);
+ * u = 0 if x < -32, else rint(e(x) * 2^32) as an unsigned 64-bit integer,
+ * where e(x) is Cody-Waite range reduction with a two-piece ln 2 followed by
+ * the degree-7 Taylor polynomial by fused multiply-adds in fp32; U = sum u;
+ * T = ceil(mass * U) in double.  Candidates are ordered by (score
+ * descending, candidate ascending); K is the length of the shortest prefix
+ * whose u sum reaches T, then min(K, cap).
+ *   logit : fp32 [heads][n] (finite values)
+ *   idx   : int32 [heads][cap] -- the K chosen candidates ascending, then -1
+ *   count : int32 [heads]       -- K
+ *   ws    : device workspace of at least vs_select_workspace_bytes(heads, n)
+ * Requires 0 < mass <= 1 and 1 <= cap <= n.  Bit-deterministic. */
+size_t vs_select_workspace_bytes(int heads, int n);
+vs_status vs_select(const float* logit, int heads, int n, vs_kind kind, double mass, int cap,
+                    int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* -------------------------------------------------------- sparse attention
+ * Causal prefill attention restricted to the vertical-slash index set
+ * (English page, section 2, "Core Concept: Vertical-Slash Pattern" and
+ * "3. Adaptive Inference Pipeline, Fused Kernel Execution").  For query head
+ * h, KV head g = h / (h_q / h_kv), row i:
+ *     S_i = { j : 0 <= j <= i, j in V_g  or  (i - j) in O_g }
+ *     out[h][i] = sum_{j in S_i} softmax_j(scale * q_i . k_j) v_j
+ *     lse[h][i] = log sum_{j in S_i} exp(scale * q_i . k_j)
+ * A key in both sets counts once.  A row with S_i empty gets out = 0 and
+ * lse = -inf.  The index lists are merged on the fly per query block into
+ * contiguous key tiles (slash ranges, with a per-element diagonal mask) and
+ * gathered tiles (verticals no slash range covers); no n x n mask is built.
+ *   q          : [h_q][n][d], k, v : [h_kv][n][d], all of dtype `dt`
+ *   v_idx      : int32 [h_kv][cap_v] vertical columns, strictly ascending
+ *   v_cnt      : int32 [h_kv] number of valid entries (clamped to [0, cap_v])
+ *   s_off      : int32 [h_kv][cap_s] slash offsets, strictly ascending
+ *   s_cnt      : int32 [h_kv]
+ *   out        : [h_q][n][d] of dtype `dt`;  lse : fp32 [h_q][n] or NULL
+ *   ws         : device workspace of at least
+ *                vs_attn_workspace_bytes(h_kv, n, cap_v, cap_s)
+ * Entries outside [0, n) are ignored; duplicates count once.  bf16 (or fp32
+ * rounded to bf16) MFMA products with fp32 softmax and accumulation.
+ * Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8, 16}. */
+size_t vs_attn_workspace_bytes(int h_kv, int n, int cap_v, int cap_s);
+vs_status vs_sparse_attn_prefill(const void* q, const void* k, const void* v, vs_dtype dt,
+                                 int h_q, int h_kv, int n, int d, float scale,
+                                 const int32_t* v_idx, const int32_t* v_cnt, int cap_v,
+                                 const int32_t* s_off, const int32_t* s_cnt, int cap_s,
+                                 void* out, float* lse, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* Work counters of the most recent vs_sparse_attn_prefill that used `ws`
+ * (read synchronously after `stream` finishes):
+ *   tiles[0] = contiguous key tiles computed, summed over KV heads and query
+ *              blocks; tiles[1] = gathered vertical tiles; tiles[2] = query
+ *              rows per tile (for every query head of a KV group together);
+ *              tiles[3] = keys per tile.
+ * The MFMA work issued is (tiles[0] + tiles[1]) * tiles[2] * tiles[3]
+ * query-key products, each 4*d flops. */
+vs_status vs_attn_tile_counts(const void* ws, int h_kv, int n, int cap_v, int cap_s,
+                              int h_q, int64_t tiles[4], hipStream_t stream);
+
+/* Static text for a status code. */
+const char* vs_status_str(vs_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VS_H_ */

@@ -1,0 +1,102 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function that include/vs.h declares,
+size its workspaces, and reject invalid arguments with a status code before
+anything would be enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import vertical_slash_sparse_amd as vsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "vs.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vs_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared_functions() == sorted(vsa.exported_symbols())
+
+
+def test_library_exports_every_declared_symbol():
+    L = vsa.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    # the dynamic symbol table, read with ctypes
+    raw = ctypes.CDLL(vsa.LIB_PATH)
+    for name in _declared_functions():
+        assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert vsa.status_str(vsa.VS_OK) == "ok"
+    assert "workspace" in vsa.status_str(vsa.VS_ERR_WORKSPACE)
+    assert vsa.status_str(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert vsa.vs_select_workspace_bytes(8, 131072) >= 8 * 131072 * 12
+    assert vsa.vs_select_workspace_bytes(0, 10) == 0
+    a = vsa.vs_attn_workspace_bytes(8, 131072, 4096, 8192)
+    b = vsa.vs_attn_workspace_bytes(8, 262144, 262144, 262144)
+    assert 0 < a < b
+    assert vsa.vs_attn_workspace_bytes(8, 0, 1, 1) == 0
+
+
+def _fake(addr=0x1000):
+    return ctypes.c_void_p(addr)
+
+
+def test_invalid_arguments_are_rejected_before_launch():
+    L = vsa.lib()
+    p = _fake()
+    # vs_select: null pointers, bad mass, bad cap, small workspace
+    assert L.vs_select(None, 1, 10, 0, 0.5, 5, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
+    assert L.vs_select(p, 1, 10, 0, 0.0, 5, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
+    assert L.vs_select(p, 1, 10, 0, 1.5, 5, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
+    assert L.vs_select(p, 1, 10, 0, 0.5, 11, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
+    assert L.vs_select(p, 1, 10, 0, 0.5, 0, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
+    assert L.vs_select(p, 1, 10, 7, 0.5, 5, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
+    assert L.vs_select(p, 1, 10, 0, 0.5, 5, p, p, p, 8, None) == vsa.VS_ERR_WORKSPACE
+    # vs_index: shapes
+    assert L.vs_index(p, p, 8, 100, 64, 128, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED
+    assert L.vs_index(p, p, 8, 100, 128, 64, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED
+    assert L.vs_index(p, p, 0, 100, 128, 128, p, p, p, p, None) == vsa.VS_ERR_INVALID
+    assert L.vs_index(None, p, 8, 100, 128, 128, p, p, p, p, None) == vsa.VS_ERR_INVALID
+
+    def attn(**kw):
+        a = dict(q=p, k=p, v=p, dt=0, h_q=32, h_kv=8, n=1024, d=128, scale=0.088, vi=p, vc=p,
+                 cap_v=16, so=p, sc=p, cap_s=16, out=p, lse=None, ws=p, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.vs_sparse_attn_prefill(a["q"], a["k"], a["v"], a["dt"], a["h_q"], a["h_kv"], a["n"],
+                                        a["d"], a["scale"], a["vi"], a["vc"], a["cap_v"], a["so"],
+                                        a["sc"], a["cap_s"], a["out"], a["lse"], a["ws"],
+                                        a["ws_bytes"], None)
+
+    assert attn(q=None) == vsa.VS_ERR_INVALID
+    assert attn(h_q=30) == vsa.VS_ERR_INVALID          # h_q % h_kv != 0
+    assert attn(h_q=24) == vsa.VS_ERR_UNSUPPORTED      # group 3
+    assert attn(d=96) == vsa.VS_ERR_UNSUPPORTED
+    assert attn(dt=5) == vsa.VS_ERR_INVALID
+    assert attn(scale=-1.0) == vsa.VS_ERR_INVALID
+    assert attn(scale=float("nan")) == vsa.VS_ERR_INVALID
+    assert attn(cap_v=0) == vsa.VS_ERR_INVALID
+    assert attn(n=0) == vsa.VS_ERR_INVALID
+    assert attn(ws_bytes=16) == vsa.VS_ERR_WORKSPACE
+    t = (ctypes.c_int64 * 4)()
+    assert L.vs_attn_tile_counts(None, 8, 1024, 16, 16, 32, ctypes.cast(t, ctypes.c_void_p), None) == vsa.VS_ERR_INVALID
+    assert L.vs_attn_tile_counts(p, 8, 1024, 16, 16, 24, ctypes.cast(t, ctypes.c_void_p), None) == vsa.VS_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        vsa.vs_index(x, x, torch.zeros(128, 256, dtype=torch.bfloat16), torch.zeros(2, 128, dtype=torch.bfloat16))

@@ -1,0 +1,62 @@
+"""Shared helpers for the GPU tests: moving seeded numpy inputs to the device
+and comparing against the oracle with the stated tolerances."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import workloads
+
+# attention output vs the fp64 oracle (bf16 inputs, fp32 accumulation)
+ATOL_MAX = 2e-2
+ATOL_MEAN = 2e-3
+# indexer logits vs the fp64 oracle (bf16 inputs, fp32 accumulation)
+INDEX_ATOL = 1e-3
+
+
+def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint16 arrays are bf16 bit patterns; everything else keeps its dtype."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def bits_f64(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return workloads.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def assert_attn_close(out_gpu: np.ndarray, lse_gpu: np.ndarray, out_ref: np.ndarray,
+                      lse_ref: np.ndarray, what: str = ""):
+    """max-abs <= 2e-2 and mean-abs <= 2e-3 on O and on finite lse; -inf lse
+    (empty rows) must match exactly with O == 0 there."""
+    assert out_gpu.shape == out_ref.shape
+    assert np.isfinite(out_gpu).all(), f"{what}: non-finite output"
+    err = np.abs(out_gpu - out_ref)
+    assert err.max() <= ATOL_MAX, f"{what}: O max-abs {err.max():.3e}"
+    assert err.mean() <= ATOL_MEAN, f"{what}: O mean-abs {err.mean():.3e}"
+    empty_ref = np.isneginf(lse_ref)
+    assert (np.isneginf(lse_gpu) == empty_ref).all(), f"{what}: empty-row pattern differs"
+    assert (out_gpu[empty_ref] == 0).all(), f"{what}: empty rows must be zero"
+    fin = ~empty_ref
+    if fin.any():
+        le = np.abs(lse_gpu[fin] - lse_ref[fin])
+        assert le.max() <= ATOL_MAX, f"{what}: lse max-abs {le.max():.3e}"
+        assert le.mean() <= ATOL_MEAN, f"{what}: lse mean-abs {le.mean():.3e}"
+
+
+def sample_rows(rng, hq: int, n: int, per_head: int, block: int = 64) -> np.ndarray:
+    """(head, row) pairs: first and last rows, both ends of the first and last
+    query blocks, plus random rows, for every head."""
+    fixed = sorted({0, 1, block - 1, block, n - block, n - 2, n - 1} & set(range(n)))
+    rows = []
+    for h in range(hq):
+        extra = rng.choice(n, size=max(per_head - len(fixed), 0), replace=False)
+        for i in sorted(set(fixed) | set(int(x) for x in extra)):
+            rows.append((h, i))
+    return np.array(rows, dtype=np.int32)

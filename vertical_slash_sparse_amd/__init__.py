@@ -1,0 +1,222 @@
+"""Python binding of libvs: vertical-slash sparse prefill on MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI in ``include/vs.h``; the functions
+keep the C names.  Every step of the computation runs in the HIP kernels of
+``libvs.so``; PyTorch only provides device memory and the current stream.
+There is no fallback: if the library is missing or cannot be loaded the
+calls raise.
+
+    vs_index(k_rope, v, w1, w2)                    -> (vlog, slog)
+    vs_select(logit, kind, mass, cap)              -> (idx, count)
+    vs_sparse_attn_prefill(q, k, v, v_idx, v_cnt, s_off, s_cnt, scale=None)
+                                                   -> (out, lse)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvs.so")
+
+VS_OK, VS_ERR_INVALID, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_HIP = range(5)
+VS_BF16, VS_F32 = 0, 1
+VS_VERTICAL, VS_SLASH = 0, 1
+
+_SYMBOLS = ("vs_index", "vs_select_workspace_bytes", "vs_select", "vs_attn_workspace_bytes",
+            "vs_sparse_attn_prefill", "vs_attn_tile_counts", "vs_status_str")
+
+
+class VSError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvs.so (built by ``vertical_slash_sparse_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m vertical_slash_sparse_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, f64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_float, ctypes.c_size_t
+        L.vs_index.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P]
+        L.vs_index.restype = i32
+        L.vs_select_workspace_bytes.argtypes = [i32, i32]
+        L.vs_select_workspace_bytes.restype = sz
+        L.vs_select.argtypes = [P, i32, i32, i32, f64, i32, P, P, P, sz, P]
+        L.vs_select.restype = i32
+        L.vs_attn_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.vs_attn_workspace_bytes.restype = sz
+        L.vs_sparse_attn_prefill.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P, i32, P, P,
+                                             i32, P, P, P, sz, P]
+        L.vs_sparse_attn_prefill.restype = i32
+        L.vs_attn_tile_counts.argtypes = [P, i32, i32, i32, i32, i32, P, P]
+        L.vs_attn_tile_counts.restype = i32
+        L.vs_status_str.argtypes = [i32]
+        L.vs_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().vs_status_str(int(status)).decode()
+
+
+vs_status_str = status_str
+
+
+def _check(fn: str, status: int):
+    if status != VS_OK:
+        raise VSError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor, stream=None):
+    s = torch.cuda.current_stream(t.device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def vs_index(k_rope: torch.Tensor, v: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
+             vlog: torch.Tensor | None = None, slog: torch.Tensor | None = None, stream=None):
+    """VSIndexer logits.  k_rope, v: bf16 [h_kv, n, d]; w1: bf16 [hidden, 2d];
+    w2: bf16 [2, hidden].  Returns fp32 (vlog, slog) [h_kv, n]."""
+    _need(k_rope, "k_rope", torch.bfloat16, 3)
+    dev = k_rope.device
+    _need(v, "v", torch.bfloat16, 3, dev)
+    _need(w1, "w1", torch.bfloat16, 2, dev)
+    _need(w2, "w2", torch.bfloat16, 2, dev)
+    h_kv, n, d = k_rope.shape
+    if v.shape != k_rope.shape or w1.shape[1] != 2 * d or w2.shape != (2, w1.shape[0]):
+        raise ValueError("vs_index: inconsistent shapes")
+    vlog = torch.empty((h_kv, n), dtype=torch.float32, device=dev) if vlog is None else vlog
+    slog = torch.empty((h_kv, n), dtype=torch.float32, device=dev) if slog is None else slog
+    for t, nm in ((vlog, "vlog"), (slog, "slog")):
+        _need(t, nm, torch.float32, 2, dev)
+        if t.shape != (h_kv, n):
+            raise ValueError(f"{nm} must be [h_kv, n]")
+    st = lib().vs_index(_ptr(k_rope), _ptr(v), h_kv, n, d, w1.shape[0], _ptr(w1), _ptr(w2),
+                        _ptr(vlog), _ptr(slog), _stream(k_rope, stream))
+    _check("vs_index", st)
+    return vlog, slog
+
+
+def vs_select_workspace_bytes(heads: int, n: int) -> int:
+    return int(lib().vs_select_workspace_bytes(heads, n))
+
+
+def vs_select(logit: torch.Tensor, kind: int, mass: float, cap: int, idx: torch.Tensor | None = None,
+              count: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Cumulative-mass selection.  logit: fp32 [heads, n].  kind: VS_VERTICAL
+    or VS_SLASH.  Returns int32 (idx [heads, cap] ascending then -1, count [heads])."""
+    _need(logit, "logit", torch.float32, 2)
+    dev = logit.device
+    heads, n = logit.shape
+    idx = torch.empty((heads, cap), dtype=torch.int32, device=dev) if idx is None else idx
+    count = torch.empty((heads,), dtype=torch.int32, device=dev) if count is None else count
+    _need(idx, "idx", torch.int32, 2, dev)
+    _need(count, "count", torch.int32, 1, dev)
+    if idx.shape != (heads, cap) or count.shape != (heads,):
+        raise ValueError("vs_select: idx must be [heads, cap] and count [heads]")
+    need = vs_select_workspace_bytes(heads, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = lib().vs_select(_ptr(logit), heads, n, int(kind), float(mass), int(cap), _ptr(idx),
+                         _ptr(count), _ptr(workspace), workspace.numel(), _stream(logit, stream))
+    _check("vs_select", st)
+    return idx, count
+
+
+def vs_attn_workspace_bytes(h_kv: int, n: int, cap_v: int, cap_s: int) -> int:
+    return int(lib().vs_attn_workspace_bytes(h_kv, n, cap_v, cap_s))
+
+
+def vs_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           v_idx: torch.Tensor, v_cnt: torch.Tensor, s_off: torch.Tensor,
+                           s_cnt: torch.Tensor, scale: float | None = None,
+                           out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                           want_lse: bool = True, workspace: torch.Tensor | None = None,
+                           stream=None):
+    """Vertical-slash sparse causal prefill.  q [h_q, n, d], k/v [h_kv, n, d]
+    (bf16 or fp32, all the same); index lists int32 [h_kv, cap] with counts
+    int32 [h_kv].  Returns (out [h_q, n, d] in the input dtype, lse fp32 [h_q, n])."""
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bf16 or fp32")
+    dt = VS_BF16 if q.dtype == torch.bfloat16 else VS_F32
+    _need(q, "q", q.dtype, 3)
+    dev = q.device
+    _need(k, "k", q.dtype, 3, dev)
+    _need(v, "v", q.dtype, 3, dev)
+    for t, nm in ((v_idx, "v_idx"), (s_off, "s_off")):
+        _need(t, nm, torch.int32, 2, dev)
+    for t, nm in ((v_cnt, "v_cnt"), (s_cnt, "s_cnt")):
+        _need(t, nm, torch.int32, 1, dev)
+    h_q, n, d = q.shape
+    h_kv = k.shape[0]
+    if k.shape != (h_kv, n, d) or v.shape != k.shape:
+        raise ValueError("vs_sparse_attn_prefill: k and v must be [h_kv, n, d]")
+    if v_idx.shape[0] != h_kv or s_off.shape[0] != h_kv or v_cnt.shape != (h_kv,) or s_cnt.shape != (h_kv,):
+        raise ValueError("vs_sparse_attn_prefill: index lists must have h_kv rows")
+    cap_v, cap_s = v_idx.shape[1], s_off.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", q.dtype, 3, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    if want_lse and lse is None:
+        lse = torch.empty((h_q, n), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+        if lse.shape != (h_q, n):
+            raise ValueError("lse must be [h_q, n]")
+    need = vs_attn_workspace_bytes(h_kv, n, cap_v, cap_s)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = lib().vs_sparse_attn_prefill(_ptr(q), _ptr(k), _ptr(v), dt, h_q, h_kv, n, d, scale,
+                                      _ptr(v_idx), _ptr(v_cnt), cap_v, _ptr(s_off), _ptr(s_cnt),
+                                      cap_s, _ptr(out), _ptr(lse), _ptr(workspace),
+                                      workspace.numel(), _stream(q, stream))
+    _check("vs_sparse_attn_prefill", st)
+    return out, lse
+
+
+def vs_attn_tile_counts(workspace: torch.Tensor, h_kv: int, n: int, cap_v: int, cap_s: int,
+                        h_q: int, stream=None):
+    """(contiguous tiles, gathered tiles, query rows per tile, keys per tile)
+    of the last vs_sparse_attn_prefill that used ``workspace`` (synchronous)."""
+    tiles = (ctypes.c_int64 * 4)()
+    st = lib().vs_attn_tile_counts(_ptr(workspace), h_kv, n, cap_v, cap_s, h_q,
+                                   ctypes.cast(tiles, ctypes.c_void_p), _stream(workspace, stream))
+    _check("vs_attn_tile_counts", st)
+    return tuple(int(x) for x in tiles)
+
+
+def exported_symbols():
+    return _SYMBOLS

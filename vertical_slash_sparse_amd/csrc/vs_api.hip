@@ -1,0 +1,108 @@
+// vs_api.hip -- the C ABI of libvs (declared in include/vs.h): argument
+// checks, workspace sizing, launches.  Everything that can be checked on the
+// host is checked before anything is enqueued; nothing here allocates,
+// frees or synchronises except vs_attn_tile_counts, which reads counters back.
+#include <math.h>
+
+#include "vs.h"
+#include "vs_internal.h"
+
+using namespace vs;
+
+namespace {
+
+bool group_ok(int h_q, int h_kv) {
+  if (h_q <= 0 || h_kv <= 0 || h_q % h_kv) return false;
+  const int g = h_q / h_kv;
+  return g == 1 || g == 2 || g == 4 || g == 8 || g == 16;
+}
+
+vs_status from_hip(hipError_t e) { return e == hipSuccess ? VS_OK : VS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* vs_status_str(vs_status s) {
+  switch (s) {
+    case VS_OK: return "ok";
+    case VS_ERR_INVALID: return "invalid argument";
+    case VS_ERR_UNSUPPORTED: return "unsupported shape";
+    case VS_ERR_WORKSPACE: return "workspace too small";
+    case VS_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+vs_status vs_index(const void* k_rope, const void* v, int h_kv, int n, int d, int hidden,
+                   const void* w1, const void* w2, float* vlog, float* slog,
+                   hipStream_t stream) {
+  if (!k_rope || !v || !w1 || !w2 || !vlog || !slog) return VS_ERR_INVALID;
+  if (h_kv <= 0 || n <= 0 || d <= 0 || hidden <= 0) return VS_ERR_INVALID;
+  if ((long long)h_kv * n > (1LL << 40)) return VS_ERR_INVALID;
+  if (d != 128 || hidden != 128) return VS_ERR_UNSUPPORTED;
+  return from_hip(launch_index(k_rope, v, h_kv, n, w1, w2, vlog, slog, stream));
+}
+
+size_t vs_select_workspace_bytes(int heads, int n) {
+  if (heads <= 0 || n <= 0) return 0;
+  return SelectWsLayout(heads, n).total;
+}
+
+vs_status vs_select(const float* logit, int heads, int n, vs_kind kind, double mass, int cap,
+                    int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  if (!logit || !idx || !count || !ws) return VS_ERR_INVALID;
+  if (heads <= 0 || n <= 0 || heads > 65535) return VS_ERR_INVALID;
+  if (kind != VS_VERTICAL && kind != VS_SLASH) return VS_ERR_INVALID;
+  if (!(mass > 0.0 && mass <= 1.0)) return VS_ERR_INVALID;
+  if (cap < 1 || cap > n) return VS_ERR_INVALID;
+  if (ws_bytes < vs_select_workspace_bytes(heads, n)) return VS_ERR_WORKSPACE;
+  return from_hip(launch_select(logit, heads, n, (int)kind, mass, cap, idx, count, ws, stream));
+}
+
+size_t vs_attn_workspace_bytes(int h_kv, int n, int cap_v, int cap_s) {
+  if (h_kv <= 0 || n <= 0 || cap_v < 1 || cap_s < 1) return 0;
+  return AttnWsLayout(h_kv, n, cap_v, cap_s).total;
+}
+
+vs_status vs_sparse_attn_prefill(const void* q, const void* k, const void* v, vs_dtype dt,
+                                 int h_q, int h_kv, int n, int d, float scale,
+                                 const int32_t* v_idx, const int32_t* v_cnt, int cap_v,
+                                 const int32_t* s_off, const int32_t* s_cnt, int cap_s,
+                                 void* out, float* lse, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  if (!q || !k || !v || !v_idx || !v_cnt || !s_off || !s_cnt || !out || !ws) return VS_ERR_INVALID;
+  if (dt != VS_BF16 && dt != VS_F32) return VS_ERR_INVALID;
+  if (h_q <= 0 || h_kv <= 0 || n <= 0 || d <= 0) return VS_ERR_INVALID;
+  if (h_q % h_kv) return VS_ERR_INVALID;
+  if (cap_v < 1 || cap_s < 1) return VS_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return VS_ERR_INVALID;
+  if ((long long)n > (1LL << 30) || (long long)h_kv * n * d > (1LL << 40)) return VS_ERR_INVALID;
+  if (!group_ok(h_q, h_kv)) return VS_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return VS_ERR_UNSUPPORTED;
+  if (ws_bytes < vs_attn_workspace_bytes(h_kv, n, cap_v, cap_s)) return VS_ERR_WORKSPACE;
+  return from_hip(launch_attn(q, k, v, dt == VS_F32, h_q, h_kv, n, d, scale, v_idx, v_cnt, cap_v,
+                              s_off, s_cnt, cap_s, out, lse, ws, stream));
+}
+
+vs_status vs_attn_tile_counts(const void* ws, int h_kv, int n, int cap_v, int cap_s, int h_q,
+                              int64_t tiles[4], hipStream_t stream) {
+  if (!ws || !tiles) return VS_ERR_INVALID;
+  if (h_kv <= 0 || n <= 0 || cap_v < 1 || cap_s < 1) return VS_ERR_INVALID;
+  if (!group_ok(h_q, h_kv)) return VS_ERR_UNSUPPORTED;
+  const AttnWsLayout L(h_kv, n, cap_v, cap_s);
+  unsigned long long host[2] = {0ull, 0ull};
+  hipError_t e = hipMemcpyAsync(host, static_cast<const char*>(ws) + L.off_stats, sizeof host,
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return VS_ERR_HIP;
+  const int group = h_q / h_kv;
+  tiles[0] = (int64_t)host[0];
+  tiles[1] = (int64_t)host[1];
+  tiles[2] = (int64_t)attn_query_rows_per_block(group);
+  tiles[3] = (int64_t)kBN;
+  return VS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,619 @@
+// vs_attn.hip -- index-to-tile builder and vertical-slash sparse prefill
+// attention for gfx950 (MI355X).
+//
+// What is computed (VSPrefill, gist.science summaries of arXiv 2603.04460:
+// English page, Technical Summary section 2, "Core Concept: Vertical-Slash
+// Pattern" and "3. Adaptive Inference Pipeline, Fused Kernel Execution";
+// German page section 2.A gives the slash as the relative shift i - j):
+// for query head h of KV group g and row i, attention over
+//     S_i = { j <= i : j in V_g  or  i - j in O_g }.
+//
+// How it is laid out on the chip
+//  * Builder (4 tiny launches per call): per KV head, bitmaps of the
+//    selected offsets and columns, a per-word prefix count of the offset
+//    bitmap, sorted duplicate-free lists, and "clusters": maximal runs of
+//    sorted offsets whose gaps are small enough that, for a block of BMP
+//    query rows, the keys they reach form one contiguous range of key tiles.
+//  * Attention: one workgroup per (KV head, block of BMP query positions);
+//    its waves are the G query heads of the group (and, for G < 4, several
+//    32-row sub-blocks), so every K/V tile staged in LDS feeds all G heads.
+//    The sorted cluster list is walked from the largest offset down, which
+//    yields the key-tile ranges of the block in ascending key order (a merge
+//    of the per-cluster ranges, no n x n structure).  Each contiguous tile is
+//    masked per element by (j <= i) and (offset bit or column bit); the lane
+//    masks come from wave-uniform bitmap windows, so a masked element costs
+//    one v_cndmask.  Columns that no processed tile covers are then gathered
+//    64 at a time into tiles of their own.
+//  * Math per 64-key tile and 32 query rows: S^T = K Q^T on
+//    v_mfma_f32_32x32x16_bf16 (K from LDS, Q^T held in registers), online
+//    softmax in fp32 on the transposed scores (each lane owns one query row,
+//    so row statistics need one cross-half exchange), P^T reused directly as
+//    the B operand of O^T += V^T P^T with V^T staged in LDS in a matching
+//    key order.  The running maximum is only moved when it grows by more
+//    than 2^8 (the result is unchanged; p stays below 2^8 in fp32/bf16).
+#include "vs_common.h"
+#include "vs_internal.h"
+
+namespace vs {
+
+namespace {
+
+constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNoMax = -1.0e30f;      // running max before any key was seen
+
+// ---------------------------------------------------------------- builder
+
+template <int NT>
+__device__ int block_excl_scan(int v, int* total, int* sh) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  constexpr int NWV = NT / 64;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  if (wv == 0) {
+    int t = lane < NWV ? sh[lane] : 0;
+    int s = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(s, o, 64);
+      if (lane >= o) s += y;
+    }
+    if (lane < NWV) sh[lane] = s - t;
+    if (lane == NWV - 1) sh[NWV] = s;
+  }
+  __syncthreads();
+  int res = sh[wv] + x - v;
+  *total = sh[NWV];
+  __syncthreads();
+  return res;
+}
+
+__global__ void ws_clear_kernel(uint32_t* bitO, uint32_t* bitV, size_t nwords,
+                                unsigned long long* stats) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t step = (size_t)gridDim.x * blockDim.x;
+  for (; i < nwords; i += step) {
+    bitO[i] = 0u;
+    bitV[i] = 0u;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < 4) stats[threadIdx.x] = 0ull;
+}
+
+__global__ void ws_setbits_kernel(const int32_t* __restrict__ v_idx, const int32_t* __restrict__ v_cnt,
+                                  int cap_v, const int32_t* __restrict__ s_off,
+                                  const int32_t* __restrict__ s_cnt, int cap_s, int n,
+                                  uint32_t* bitO, uint32_t* bitV, int stride) {
+  const int g = blockIdx.y;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int cv = min(max(v_cnt[g], 0), cap_v);
+  const int cs = min(max(s_cnt[g], 0), cap_s);
+  if (t < cv) {
+    int x = v_idx[(size_t)g * cap_v + t];
+    if (x >= 0 && x < n) atomicOr(&bitV[(size_t)g * stride + kPrePad + (x >> 5)], 1u << (x & 31));
+  }
+  if (t < cs) {
+    int x = s_off[(size_t)g * cap_s + t];
+    if (x >= 0 && x < n) atomicOr(&bitO[(size_t)g * stride + kPrePad + (x >> 5)], 1u << (x & 31));
+  }
+}
+
+// per head: prefix counts of the offset bitmap and sorted unique lists
+__global__ __launch_bounds__(1024) void ws_scan_kernel(const uint32_t* __restrict__ bitO,
+                                                       const uint32_t* __restrict__ bitV,
+                                                       int stride, int words, uint32_t* prefO,
+                                                       int32_t* cleanO, int cap_s,
+                                                       int32_t* cleanV, int cap_v,
+                                                       int32_t* counts) {
+  __shared__ int sh[17];
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const uint32_t* bo = bitO + (size_t)g * stride + kPrePad;
+  const uint32_t* bv = bitV + (size_t)g * stride + kPrePad;
+  const int per = (words + 1023) / 1024;
+  const int w0 = min(tid * per, words), w1 = min(w0 + per, words);
+  int co = 0, cv = 0;
+  for (int w = w0; w < w1; ++w) {
+    co += __popc(bo[w]);
+    cv += __popc(bv[w]);
+  }
+  int to, tv;
+  int ro = block_excl_scan<1024>(co, &to, sh);
+  int rv = block_excl_scan<1024>(cv, &tv, sh);
+  uint32_t* pf = prefO + (size_t)g * (words + 1);
+  int32_t* lo = cleanO + (size_t)g * cap_s;
+  int32_t* lv = cleanV + (size_t)g * cap_v;
+  for (int w = w0; w < w1; ++w) {
+    pf[w] = (uint32_t)ro;
+    uint32_t x = bo[w];
+    while (x) {
+      int bit = __ffs(x) - 1;
+      x &= x - 1;
+      if (ro < cap_s) lo[ro] = 32 * w + bit;
+      ++ro;
+    }
+    x = bv[w];
+    while (x) {
+      int bit = __ffs(x) - 1;
+      x &= x - 1;
+      if (rv < cap_v) lv[rv] = 32 * w + bit;
+      ++rv;
+    }
+  }
+  if (tid == 0) {
+    pf[words] = (uint32_t)to;
+    counts[4 * g + 0] = min(to, cap_s);
+    counts[4 * g + 1] = min(tv, cap_v);
+  }
+}
+
+// per head: clusters of sorted offsets whose neighbours are at most `gap` apart
+__global__ __launch_bounds__(1024) void ws_cluster_kernel(const int32_t* __restrict__ cleanO,
+                                                          int cap_s, int gap, int32_t* clLo,
+                                                          int32_t* clHi, int32_t* counts) {
+  __shared__ int sh[17];
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const int nO = counts[4 * g + 0];
+  const int32_t* c = cleanO + (size_t)g * cap_s;
+  const int per = (nO + 1023) / 1024;
+  const int t0 = min(tid * per, nO), t1 = min(t0 + per, nO);
+  int st = 0;
+  for (int t = t0; t < t1; ++t) st += (t == 0 || c[t] - c[t - 1] > gap) ? 1 : 0;
+  int tot;
+  int id = block_excl_scan<1024>(st, &tot, sh) - 1;
+  int32_t* lo = clLo + (size_t)g * cap_s;
+  int32_t* hi = clHi + (size_t)g * cap_s;
+  for (int t = t0; t < t1; ++t) {
+    if (t == 0 || c[t] - c[t - 1] > gap) lo[++id] = c[t];
+    if (t == nO - 1 || c[t + 1] - c[t] > gap) hi[id] = c[t];
+  }
+  if (tid == 0) counts[4 * g + 2] = tot;
+}
+
+// ---------------------------------------------------------------- attention
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int n, hkv, group, nblocks, bmp;
+  float c;  // scale * log2(e)
+  const uint32_t* bitO;
+  const uint32_t* bitV;
+  int stride;
+  const uint32_t* prefO;
+  int words;
+  const int32_t* cleanV;
+  int cap_v;
+  const int32_t* clLo;
+  const int32_t* clHi;
+  int cap_s;
+  const int32_t* counts;
+  unsigned long long* stats;
+};
+
+template <bool F32>
+__device__ __forceinline__ u32x4 load8(const void* base, size_t elem) {
+  if constexpr (F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+    float4 a = p[0], b = p[1];
+    return u32x4{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w)};
+  } else {
+    return *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
+  }
+}
+
+template <int D, bool F32, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = D / 16;     // k-steps of Q K^T
+  constexpr int DT = D / 32;     // 32-row tiles of O^T
+  constexpr int KROW = D + 8;    // padded LDS row of K (bf16 elements)
+  constexpr int VROW = kBN + 8;  // padded LDS row of V^T
+  __shared__ __align__(16) uint16_t k_lds[kBN * KROW];
+  __shared__ __align__(16) uint16_t vt_lds[D * VROW];
+  __shared__ __align__(16) int glist[kListCap];
+  __shared__ __align__(16) int gkeys[kBN];
+  __shared__ int wcnt[NW + 1];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, ql = lane & 31;
+  const int n = p.n, G = p.group;
+  const int g = blockIdx.x % p.hkv;                           // head g on XCD g (round-robin dispatch)
+  const int b = p.nblocks - 1 - (int)(blockIdx.x / p.hkv);    // longest causal rows first
+  const int i0 = b * p.bmp;
+  const int i1 = min(i0 + p.bmp, n) - 1;
+  const int head = g * G + (wave % G);
+  const int i0w = i0 + 32 * (wave / G);
+  const int qrow = i0w + ql;
+  const bool wave_rows = i0w < n;
+
+  const void* kg_base = p.k;
+  const size_t kv_head = (size_t)g * n;
+
+  // Q^T fragments (B operand): lane holds row qrow, head-dim 16s + 8*half .. +7
+  bf16x8 qf[KS];
+  {
+    const size_t ro = ((size_t)head * n + min(qrow, n - 1)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 raw = load8<F32>(p.q, ro + 16 * s + 8 * half);
+      if (qrow >= n) raw = u32x4{0u, 0u, 0u, 0u};
+      qf[s] = as_bf16x8(raw);
+    }
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+  float m_run = kNoMax, l_run = 0.f;
+  int n_dense = 0, n_gath = 0;
+
+  // ---- stage one 64-key tile of K (row-major) and V^T (key-permuted) into LDS
+  auto stage = [&](auto keyof) {
+    constexpr int KCH = D / 8;
+    for (int id = tid; id < kBN * KCH; id += NT) {
+      const int r = id / KCH, c8 = id % KCH;
+      const int key = keyof(r);
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (key >= 0) val = load8<F32>(kg_base, (kv_head + key) * D + 8 * c8);
+      *reinterpret_cast<u32x4*>(&k_lds[r * KROW + 8 * c8]) = val;
+    }
+    constexpr int VG = (kBN / 4) * (D / 8);
+    for (int id = tid; id < VG; id += NT) {
+      const int kgp = id & 15, dc = id >> 4;
+      u32x4 rows[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = keyof(4 * kgp + rr);
+        rows[rr] = key >= 0 ? load8<F32>(p.v, (kv_head + key) * D + 8 * dc) : u32x4{0u, 0u, 0u, 0u};
+      }
+      // storage slot inside each 16-key chunk: the order in which the two
+      // wave halves consume keys as the k index of O^T += V^T P^T
+      const int pos = 16 * (kgp >> 2) + 8 * (kgp & 1) + 4 * ((kgp >> 1) & 1);
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int w = dd >> 1, sh = (dd & 1) * 16;
+        const uint32_t lo = ((rows[0][w] >> sh) & 0xffffu) | (((rows[1][w] >> sh) & 0xffffu) << 16);
+        const uint32_t hi = ((rows[2][w] >> sh) & 0xffffu) | (((rows[3][w] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<u32x2*>(&vt_lds[(8 * dc + dd) * VROW + pos]) = u32x2{lo, hi};
+      }
+    }
+  };
+
+  // ---- one tile of online softmax attention for this wave's 32 rows
+  auto attend = [&](auto apply_mask) {
+    f32x16 s0, s1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&k_lds[ql * KROW + 16 * kk + 8 * half]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&k_lds[(32 + ql) * KROW + 16 * kk + 8 * half]);
+      s0 = mfma32(a0, qf[kk], s0);
+      s1 = mfma32(a1, qf[kk], s1);
+    }
+    apply_mask(s0, s1);
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+    mx = fmaxf(mx, swap_halves(mx));
+    const float mt = mx * p.c;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau)) {
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+      m_run = mn;
+    }
+    const float nm = -m_run;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], p.c, nm));
+      s1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], p.c, nm));
+      l_run += s0[e] + s1[e];
+    }
+    bf16x8 pf[4];
+    pf[0] = as_bf16x8(u32x4{pack_bf16(s0[0], s0[1]), pack_bf16(s0[2], s0[3]), pack_bf16(s0[4], s0[5]), pack_bf16(s0[6], s0[7])});
+    pf[1] = as_bf16x8(u32x4{pack_bf16(s0[8], s0[9]), pack_bf16(s0[10], s0[11]), pack_bf16(s0[12], s0[13]), pack_bf16(s0[14], s0[15])});
+    pf[2] = as_bf16x8(u32x4{pack_bf16(s1[0], s1[1]), pack_bf16(s1[2], s1[3]), pack_bf16(s1[4], s1[5]), pack_bf16(s1[6], s1[7])});
+    pf[3] = as_bf16x8(u32x4{pack_bf16(s1[8], s1[9]), pack_bf16(s1[10], s1[11]), pack_bf16(s1[12], s1[13]), pack_bf16(s1[14], s1[15])});
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vt_lds[(32 * dt + ql) * VROW + 16 * c4 + 8 * half]);
+        acc[dt] = mfma32(av, pf[c4], acc[dt]);
+      }
+  };
+
+  const uint32_t* bo = p.bitO + (size_t)g * p.stride + kPrePad;
+  const uint32_t* bv = p.bitV + (size_t)g * p.stride + kPrePad;
+  // bits [pos, pos + 64) of a bitmap; pos >= -128, words past the end are zero
+  auto win64 = [](const uint32_t* bm, int pos) -> uint64_t {
+    const int w = pos >> 5, sh = pos & 31;
+    const uint64_t lo = (uint64_t)bm[w] | ((uint64_t)bm[w + 1] << 32);
+    const uint64_t hi = bm[w + 2];
+    return sh ? (lo >> sh) | (hi << (64 - sh)) : lo;
+  };
+
+  // number of selected offsets below x (0 <= x <= n)
+  const uint32_t* pfo = p.prefO + (size_t)g * (p.words + 1);
+  auto prefix = [&](int x) -> int {
+    const int w = x >> 5, sh = x & 31;
+    return (int)pfo[w] + __popc(bo[w] & (sh ? ((1u << sh) - 1u) : 0u));
+  };
+  // key tile T holds a selected (row, key) pair of this block through some offset
+  auto tile_active = [&](int T) -> bool {
+    const int wl = max(0, i0 - (T + 1) * kBN + 1), wh = i1 - T * kBN;
+    return prefix(wh + 1) - prefix(wl) > 0;
+  };
+  // In a full block every tile of a cluster's key range is active; the last
+  // block may be shorter than BMP rows, so there the tiles are tested.
+  const bool partial = i1 < i0 + p.bmp - 1;
+
+  // ---------------- phase A: contiguous key tiles reached by slash clusters
+  {
+    const int32_t* clo = p.clLo + (size_t)g * p.cap_s;
+    const int32_t* chi = p.clHi + (size_t)g * p.cap_s;
+    const int ncl = p.counts[4 * g + 2];
+    int lo = 0, hi = ncl;  // first cluster whose smallest offset exceeds i1
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (clo[mid] <= i1) lo = mid + 1;
+      else hi = mid;
+    }
+    int next_t = 0;
+    for (int c = lo - 1; c >= 0; --c) {
+      const int olo = clo[c], ohi = chi[c];
+      const int klo = max(0, i0 - ohi), khi = i1 - olo;
+      const int tlo = max(klo / kBN, next_t), thi = khi / kBN;
+      for (int t = tlo; t <= thi; ++t) {
+        if (partial && !tile_active(t)) continue;
+        const int j0 = t * kBN;
+        __syncthreads();
+        stage([&](int r) { const int j = j0 + r; return j < n ? j : -1; });
+        __syncthreads();
+        ++n_dense;
+        if (!wave_rows || j0 > i0w + 31) continue;
+        // offsets i - j seen by this wave's tile: [i0w - j0 - 63, i0w - j0 + 31]
+        const int obase = i0w - j0 - (kBN - 1);
+        const uint64_t wlo = win64(bo, obase), whi = win64(bo, obase + 64) & 0x7fffffffull;
+        const uint64_t vcols = (uint64_t)bv[j0 >> 5] | ((uint64_t)bv[(j0 >> 5) + 1] << 32);
+        const bool below = j0 + kBN - 1 <= i0w;
+        if (below && ((wlo == ~0ull && whi == 0x7fffffffull) || vcols == ~0ull)) {
+          attend([](f32x16&, f32x16&) {});
+          continue;
+        }
+        const bool vert_hit = vcols != 0ull && (j0 + __builtin_ctzll(vcols | (1ull << 63))) <= i0w + 31;
+        if (wlo == 0ull && whi == 0ull && !vert_hit) continue;
+        attend([&](f32x16& s0, f32x16& s1) {
+#pragma unroll
+          for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              // window starting at the offset of lane 0, upper half, last of the 4 keys
+              const uint64_t wa = win64(bo, i0w - j0 - 32 * sk - 8 * a - 7);
+#pragma unroll
+              for (int bb = 0; bb < 4; ++bb) {
+                uint32_t lo32 = (uint32_t)(wa >> (7 - bb));
+                uint32_t hi32 = (uint32_t)(wa >> (3 - bb));
+                if (vcols) {
+                  const int kk0 = 32 * sk + 8 * a + bb;  // key index in tile, lower half
+                  if ((vcols >> kk0) & 1ull) {
+                    const int df = j0 + kk0 - i0w;
+                    lo32 |= df <= 0 ? ~0u : (df >= 32 ? 0u : (~0u << df));
+                  }
+                  if ((vcols >> (kk0 + 4)) & 1ull) {
+                    const int df = j0 + kk0 + 4 - i0w;
+                    hi32 |= df <= 0 ? ~0u : (df >= 32 ? 0u : (~0u << df));
+                  }
+                }
+                const uint64_t m = (uint64_t)lo32 | ((uint64_t)hi32 << 32);
+                const int e = 4 * a + bb;
+                if (sk == 0) s0[e] = select_mask(m, s0[e], -__builtin_inff());
+                else s1[e] = select_mask(m, s1[e], -__builtin_inff());
+              }
+            }
+        });
+      }
+      next_t = max(next_t, thi + 1);
+    }
+  }
+
+  // ---------------- phase B: selected columns outside every processed tile
+  {
+    const int32_t* cv = p.cleanV + (size_t)g * p.cap_v;
+    const int nv = p.counts[4 * g + 1];
+    int lo = 0, hi = nv;  // columns <= i1
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (cv[mid] <= i1) lo = mid + 1;
+      else hi = mid;
+    }
+    const int total = lo;
+    int cursor = 0;
+    while (cursor < total) {
+      int fill = 0;
+      while (cursor < total && fill + NT <= kListCap) {
+        const int idx = cursor + tid;
+        bool keep = false;
+        int col = 0;
+        if (idx < total) {
+          col = cv[idx];
+          keep = !tile_active(col / kBN);  // its tile was not processed in phase A
+        }
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (lane == 0) wcnt[wave] = __popcll(bal);
+        __syncthreads();
+        int before = 0, all = 0;
+        for (int w = 0; w < NW; ++w) {
+          const int c = wcnt[w];
+          before += w < wave ? c : 0;
+          all += c;
+        }
+        if (keep) glist[fill + before + below] = col;
+        fill += all;
+        cursor += NT;
+        __syncthreads();
+      }
+      for (int kb = 0; kb < fill; kb += kBN) {
+        const int cnt = min(kBN, fill - kb);
+        __syncthreads();
+        if (tid < kBN) gkeys[tid] = tid < cnt ? glist[kb + tid] : -1;
+        __syncthreads();
+        stage([&](int r) { return gkeys[r]; });
+        __syncthreads();
+        ++n_gath;
+        if (!wave_rows || gkeys[0] > i0w + 31) continue;
+        attend([&](f32x16& s0, f32x16& s1) {
+#pragma unroll
+          for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const int4 ks = *reinterpret_cast<const int4*>(&gkeys[32 * sk + 8 * a + 4 * half]);
+              const int kv4[4] = {ks.x, ks.y, ks.z, ks.w};
+#pragma unroll
+              for (int bb = 0; bb < 4; ++bb) {
+                const bool ok = kv4[bb] >= 0 && kv4[bb] <= qrow;
+                const int e = 4 * a + bb;
+                if (sk == 0) s0[e] = ok ? s0[e] : -__builtin_inff();
+                else s1[e] = ok ? s1[e] : -__builtin_inff();
+              }
+            }
+        });
+      }
+    }
+  }
+
+  // ---------------- finish: normalise, write O and lse
+  const float lt = l_run + swap_halves(l_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (wave_rows && qrow < n) {
+    const size_t ro = ((size_t)head * n + qrow) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * dt + 8 * a + 4 * half;
+        const float o0 = acc[dt][4 * a] * inv, o1 = acc[dt][4 * a + 1] * inv;
+        const float o2 = acc[dt][4 * a + 2] * inv, o3 = acc[dt][4 * a + 3] * inv;
+        if constexpr (F32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + ro + d0) = float4{o0, o1, o2, o3};
+        } else {
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + ro + d0) =
+              u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
+        }
+      }
+    if (half == 0 && p.lse)
+      p.lse[(size_t)head * n + qrow] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -__builtin_inff();
+  }
+  if (tid == 0) {
+    atomicAdd(&p.stats[0], (unsigned long long)n_dense);
+    atomicAdd(&p.stats[1], (unsigned long long)n_gath);
+  }
+}
+
+template <int D, bool F32>
+hipError_t launch_attn_kernel(const AttnParams& prm, int nw, hipStream_t stream) {
+  const dim3 grid((unsigned)prm.nblocks * (unsigned)prm.hkv);
+  switch (nw) {
+    case 4:
+      hipLaunchKernelGGL((attn_kernel<D, F32, 4>), grid, dim3(256), 0, stream, prm);
+      break;
+    case 8:
+      hipLaunchKernelGGL((attn_kernel<D, F32, 8>), grid, dim3(512), 0, stream, prm);
+      break;
+    case 16:
+      hipLaunchKernelGGL((attn_kernel<D, F32, 16>), grid, dim3(1024), 0, stream, prm);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int waves_for_group(int group) { return group < 4 ? 4 : group; }
+
+}  // namespace
+
+int attn_query_rows_per_block(int group) { return 32 * waves_for_group(group); }
+
+hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, int h_q, int h_kv,
+                       int n, int d, float scale, const int32_t* v_idx, const int32_t* v_cnt,
+                       int cap_v, const int32_t* s_off, const int32_t* s_cnt, int cap_s, void* out,
+                       float* lse, void* ws, hipStream_t stream) {
+  const AttnWsLayout L(h_kv, n, cap_v, cap_s);
+  char* base = static_cast<char*>(ws);
+  uint32_t* bitO = reinterpret_cast<uint32_t*>(base + L.off_bitO);
+  uint32_t* bitV = reinterpret_cast<uint32_t*>(base + L.off_bitV);
+  uint32_t* prefO = reinterpret_cast<uint32_t*>(base + L.off_prefO);
+  int32_t* cleanO = reinterpret_cast<int32_t*>(base + L.off_cleanO);
+  int32_t* cleanV = reinterpret_cast<int32_t*>(base + L.off_cleanV);
+  int32_t* clLo = reinterpret_cast<int32_t*>(base + L.off_clLo);
+  int32_t* clHi = reinterpret_cast<int32_t*>(base + L.off_clHi);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.off_counts);
+  unsigned long long* stats = reinterpret_cast<unsigned long long*>(base + L.off_stats);
+
+  const int group = h_q / h_kv;
+  const int nw = waves_for_group(group);
+  const int bmp = 32 * nw / group;  // query positions per workgroup
+
+  const size_t nwords = (size_t)h_kv * L.stride;
+  hipLaunchKernelGGL(ws_clear_kernel, dim3((unsigned)std::min<size_t>((nwords + 255) / 256, 2048)),
+                     dim3(256), 0, stream, bitO, bitV, nwords, stats);
+  const int capm = std::max(cap_v, cap_s);
+  hipLaunchKernelGGL(ws_setbits_kernel, dim3((unsigned)((capm + 255) / 256), (unsigned)h_kv),
+                     dim3(256), 0, stream, v_idx, v_cnt, cap_v, s_off, s_cnt, cap_s, n, bitO, bitV,
+                     L.stride);
+  hipLaunchKernelGGL(ws_scan_kernel, dim3((unsigned)h_kv), dim3(1024), 0, stream, bitO, bitV,
+                     L.stride, L.words, prefO, cleanO, cap_s, cleanV, cap_v, counts);
+  // offsets closer than bmp + 64 reach one contiguous run of 64-key tiles
+  hipLaunchKernelGGL(ws_cluster_kernel, dim3((unsigned)h_kv), dim3(1024), 0, stream, cleanO,
+                     cap_s, bmp + kBN - 1, clLo, clHi, counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  AttnParams prm;
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.out = out;
+  prm.lse = lse;
+  prm.n = n;
+  prm.hkv = h_kv;
+  prm.group = group;
+  prm.bmp = bmp;
+  prm.nblocks = (n + bmp - 1) / bmp;
+  prm.c = scale * kLog2e;
+  prm.bitO = bitO;
+  prm.bitV = bitV;
+  prm.stride = L.stride;
+  prm.prefO = prefO;
+  prm.words = L.words;
+  prm.cleanV = cleanV;
+  prm.cap_v = cap_v;
+  prm.clLo = clLo;
+  prm.clHi = clHi;
+  prm.cap_s = cap_s;
+  prm.counts = counts;
+  prm.stats = stats;
+  if (d == 128) return f32 ? launch_attn_kernel<128, true>(prm, nw, stream)
+                           : launch_attn_kernel<128, false>(prm, nw, stream);
+  return f32 ? launch_attn_kernel<64, true>(prm, nw, stream)
+             : launch_attn_kernel<64, false>(prm, nw, stream);
+}
+
+}  // namespace vs

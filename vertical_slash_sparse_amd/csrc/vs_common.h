@@ -1,0 +1,55 @@
+// vs_common.h -- internal helpers shared by the gfx950 kernels of libvs.
+//
+// Matrix-core operand layouts used throughout (measured on gfx950):
+//   v_mfma_f32_32x32x16_bf16:  A[i][k] lives in lane i + 32*(k/8), element k%8;
+//                              B[k][j] in lane j + 32*(k/8), element k%8;
+//                              D[i][j] in lane j + 32*((i/4)%2), element 4*(i/8) + i%4.
+// Only the products matter, so any permutation of k applied to both A and B
+// gives the same D; the attention kernel uses that freedom to feed the
+// softmax output straight back in as an operand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// value of lane (l ^ 32): exchange between the two halves of a wave
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+// per-lane select driven by a wave-uniform 64-bit lane mask
+__device__ __forceinline__ float select_mask(uint64_t m, float a, float b) {
+  return __builtin_amdgcn_inverse_ballot_w64(m) ? a : b;
+}
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace vs

@@ -1,0 +1,68 @@
+// vs_internal.h -- launch entry points and workspace layouts shared between
+// the C-ABI shim (vs_api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vs {
+
+constexpr int kBN = 64;          // keys per attention tile
+constexpr int kPrePad = 4;       // zero words before each bitmap (windows may start below 0)
+constexpr int kPostPad = 8;      // zero words after each bitmap (windows may run past n)
+constexpr int kListCap = 1024;   // LDS list of gathered verticals per refill
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Device workspace of vs_sparse_attn_prefill, per call.
+struct AttnWsLayout {
+  int words;        // bitmap words covering positions [0, n)
+  int stride;       // words per head in a bitmap array (pads included)
+  size_t off_bitO, off_bitV, off_prefO, off_cleanO, off_cleanV, off_clLo, off_clHi, off_counts,
+      off_stats, total;
+  AttnWsLayout(int h_kv, int n, int cap_v, int cap_s) {
+    words = (n + 31) / 32;
+    stride = kPrePad + words + kPostPad;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+    off_bitO = take(sizeof(uint32_t) * (size_t)h_kv * stride);
+    off_bitV = take(sizeof(uint32_t) * (size_t)h_kv * stride);
+    off_prefO = take(sizeof(uint32_t) * (size_t)h_kv * (words + 1));
+    off_cleanO = take(sizeof(int32_t) * (size_t)h_kv * cap_s);
+    off_cleanV = take(sizeof(int32_t) * (size_t)h_kv * cap_v);
+    off_clLo = take(sizeof(int32_t) * (size_t)h_kv * cap_s);
+    off_clHi = take(sizeof(int32_t) * (size_t)h_kv * cap_s);
+    off_counts = take(sizeof(int32_t) * 4 * (size_t)h_kv);
+    off_stats = take(sizeof(unsigned long long) * 4);
+    total = o;
+  }
+};
+
+// Device workspace of vs_select.
+struct SelectWsLayout {
+  size_t off_key, off_mass, total;
+  SelectWsLayout(int heads, int n) {
+    size_t o = 0;
+    off_key = o;
+    o = align_up(o + sizeof(uint32_t) * (size_t)heads * n, 256);
+    off_mass = o;
+    o = align_up(o + sizeof(uint64_t) * (size_t)heads * n, 256);
+    total = o;
+  }
+};
+
+hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, int h_q, int h_kv,
+                       int n, int d, float scale, const int32_t* v_idx, const int32_t* v_cnt,
+                       int cap_v, const int32_t* s_off, const int32_t* s_cnt, int cap_s, void* out,
+                       float* lse, void* ws, hipStream_t stream);
+
+int attn_query_rows_per_block(int group);
+
+hipError_t launch_select(const float* logit, int heads, int n, int kind, double mass, int cap,
+                         int32_t* idx, int32_t* count, void* ws, hipStream_t stream);
+
+hipError_t launch_index(const void* k, const void* v, int h_kv, int n, const void* w1,
+                        const void* w2, float* vlog, float* slog, hipStream_t stream);
+
+}  // namespace vs
