@@ -1,0 +1,283 @@
+"""Benchmark: one vertical-slash sparse prefill layer on one MI355X.
+
+Default workload ``zipf128k``: 32 query / 8 KV heads, d=128, n=131072, bf16
+Q/K/V with RoPE, Zipf(1.1) vertical and slash score vectors, budgets chosen by
+cumulative softmax mass 0.95 capped at 4096 columns / 8192 offsets per KV
+head.  One step = vs_select (columns) + vs_select (offsets) +
+vs_sparse_attn_prefill (tile build + attention) on inputs already resident in
+HBM.  Other workloads (``fixed32k``, ``indexer128k``, ``e2e256k``) can be
+timed with ``--workload``; ``e2e256k`` adds vs_index in front.
+
+Printed as one JSON line: ms per layer, effective (algorithmic) TFLOP/s =
+4*d*sum_h sum_i |S_i| / time, the computed-tile rate, a roofline object for
+the attention kernel and the fp64 oracle timed on a bounded sample on the
+host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "ms/layer + effective TFLOP/s (% bf16 MFMA peak), VS sparse prefill @128K"
+
+
+def pair_counts(vidx, vcnt, soff, scnt, n):
+    """sum_i |S_i| per KV head, by the closed form
+    sum_{c in V}(n-c) + sum_{o in O}(n-o) - #{(c,o): c+o <= n-1}."""
+    out = []
+    for g in range(vidx.shape[0]):
+        c = np.unique(vidx[g, :vcnt[g]].astype(np.int64))
+        o = np.unique(soff[g, :scnt[g]].astype(np.int64))
+        c = c[(c >= 0) & (c < n)]
+        o = o[(o >= 0) & (o < n)]
+        both = int(np.searchsorted(o, (n - 1) - c, side="right").sum()) if len(o) else 0
+        out.append(int((n - c).sum() + (n - o).sum()) - both)
+    return np.array(out, dtype=np.int64)
+
+
+def row_sizes(vidx, vcnt, soff, scnt, rows, group):
+    """|S_i| for each sampled (head, row)."""
+    sizes = []
+    for h, i in rows:
+        g = h // group
+        c = vidx[g, :vcnt[g]]
+        o = soff[g, :scnt[g]]
+        c = c[c <= i]
+        o = o[o <= i]
+        sizes.append(len(c) + len(o) - len(np.intersect1d(c, i - o)))
+    return np.array(sizes, dtype=np.int64)
+
+
+def _dev(a, torch):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def cpu_baseline(q, k, v, lists, group, d, n, budget_s=15.0, seed=5):
+    """The fp64 oracle on a bounded random sample of (head, row) pairs of the
+    same layer; returns its algorithmic TFLOP/s on the host cores."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    hq = q.shape[0]
+    total_rows, rows_done, flops, t_used = 0, 0, 0.0, 0.0
+    batch = 256
+    while t_used < budget_s and batch > 0:
+        rows = np.stack([rng.integers(0, hq, batch), rng.integers(0, n, batch)], axis=1).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.attn(q, k, v, *lists, rows=rows)
+        dt = time.perf_counter() - t0
+        t_used += dt
+        flops += 4.0 * d * float(row_sizes(*lists, rows, group).sum())
+        rows_done += batch
+        # grow the batch toward the budget
+        rate = batch / max(dt, 1e-6)
+        batch = int(min(max(rate * min(budget_s - t_used, 8.0), 0), 65536))
+        total_rows = rows_done
+    return {
+        "value": flops / t_used / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{total_rows} random (head, row) pairs of the same layer, fp64, "
+                  f"{t_used:.1f} s wall; value = 4*d*sum|S_i| over the sample / wall time",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="zipf128k",
+                    choices=["zipf128k", "fixed32k", "indexer128k", "e2e256k"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by KV head, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import vertical_slash_sparse_amd as vsa
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    print(f"[bench] generating {args.workload} inputs", file=sys.stderr, flush=True)
+
+    if args.workload == "indexer128k":
+        return bench_indexer(args, w, torch, vsa, workloads)
+
+    n, hq, hkv, d = w["n"], w["hq"], w["hkv"], w["d"]
+    group = hq // hkv
+    q, k, v = workloads.attention_inputs(args.workload)
+    qd, kd, vd = _dev(q, torch), _dev(k, torch), _dev(v, torch)
+    w1d = w2d = None
+    if args.workload == "zipf128k":
+        vlog, slog = workloads.zipf_scores(args.workload)
+        vlog_d, slog_d = _dev(vlog, torch), _dev(slog, torch)
+        cap_v, cap_s, mass = w["cap_v"], w["cap_s"], w["mass"]
+    elif args.workload == "e2e256k":
+        rs = workloads.streams(w["seed"])
+        w1, w2 = workloads.indexer_weights(rs["w"], 2 * d, w["hidden"])
+        w1d, w2d = _dev(w1, torch), _dev(w2, torch)
+        vlog_d = torch.empty((hkv, n), dtype=torch.float32, device="cuda")
+        slog_d = torch.empty((hkv, n), dtype=torch.float32, device="cuda")
+        cap_v, cap_s, mass = n, n, w["mass"]
+    else:
+        lists0 = [_dev(x, torch) for x in workloads.small_index_sets(args.workload)]
+        cap_v, cap_s, mass = lists0[0].shape[1], lists0[2].shape[1], None
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    vi = torch.empty((hkv, cap_v), dtype=torch.int32, device="cuda")
+    vc = torch.empty((hkv,), dtype=torch.int32, device="cuda")
+    si = torch.empty((hkv, cap_s), dtype=torch.int32, device="cuda")
+    sc = torch.empty((hkv,), dtype=torch.int32, device="cuda")
+    sel_ws = torch.empty(max(vsa.vs_select_workspace_bytes(hkv, n), 1), dtype=torch.uint8, device="cuda")
+    attn_ws = torch.empty(vsa.vs_attn_workspace_bytes(hkv, n, cap_v, cap_s), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(qd)
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i=None):
+        if mass is not None:
+            if w1d is not None:
+                vsa.vs_index(kd, vd, w1d, w2d, vlog_d, slog_d)
+            vsa.vs_select(vlog_d, vsa.VS_VERTICAL, mass, cap_v, vi, vc, sel_ws)
+            vsa.vs_select(slog_d, vsa.VS_SLASH, mass, cap_s, si, sc, sel_ws)
+            lists = (vi, vc, si, sc)
+        else:
+            lists = lists0
+        if i is not None:
+            ev_a0[i].record()
+        vsa.vs_sparse_attn_prefill(qd, kd, vd, *lists, out=out, lse=lse, workspace=attn_ws)
+        if i is not None:
+            ev_a1[i].record()
+        return lists
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        lists = step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in zip(ev_a0, ev_a1)]
+    attn_avg = float(np.mean(attn_ms))
+
+    lists_np = [x.cpu().numpy() for x in lists]
+    pairs = pair_counts(*lists_np, n)                   # per KV head
+    f_alg = 4.0 * d * group * float(pairs.sum())        # all query heads
+    dense_t, gath_t, rows_t, keys_t = vsa.vs_attn_tile_counts(attn_ws, hkv, n, cap_v, cap_s, hq)
+    f_tile = 4.0 * d * float(dense_t + gath_t) * rows_t * keys_t
+    causal_pairs = hkv * n * (n + 1) / 2
+    bmp = rows_t // group
+    causal_tiles = hkv * sum((min((b + 1) * bmp, n) - 1) // keys_t + 1 for b in range((n + bmp - 1) // bmp))
+
+    eff = f_alg / (ms_per_step * 1e-3) / 1e12
+    achieved = f_alg / (attn_avg * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(eff, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n": n, "h_q": hq, "h_kv": hkv, "d": d,
+                   "mass": mass, "cap_v": cap_v if mass else None, "cap_s": cap_s if mass else None,
+                   "seed": w["seed"]},
+        "pct_peak_effective": round(100.0 * eff / PEAK_BF16_TFLOPS, 3),
+        "attn_ms": round(attn_avg, 4),
+        "tile_tflops": round(f_tile / (attn_avg * 1e-3) / 1e12, 3),
+        "pct_peak_tile": round(100.0 * f_tile / (attn_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 3),
+        "pair_density": round(float(pairs.sum()) / causal_pairs, 5),
+        "tile_density": round((dense_t + gath_t) / causal_tiles, 5),
+        "tiles": {"contiguous": dense_t, "gathered": gath_t, "rows": rows_t, "keys": keys_t},
+        "flops_alg": f_alg,
+        "flops_tile": f_tile,
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel (vs_sparse_attn_prefill)",
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 5), "traffic": None},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        lists_np_full = lists_np
+        print("[bench] timing the oracle on a host sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(q, k, v, lists_np_full, group, d, n, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+def bench_indexer(args, w, torch, vsa, workloads):
+    """vs_index + vs_select (both kinds) at 8 KV heads x 131072 positions."""
+    n, hkv, d = w["n"], w["hkv"], w["d"]
+    k, v, w1, w2 = workloads.indexer_inputs(args.workload)
+    kd, vd, w1d, w2d = (_dev(x, torch) for x in (k, v, w1, w2))
+    vlog = torch.empty((hkv, n), dtype=torch.float32, device="cuda")
+    slog = torch.empty((hkv, n), dtype=torch.float32, device="cuda")
+    vi = torch.empty((hkv, n), dtype=torch.int32, device="cuda")
+    vc = torch.empty((hkv,), dtype=torch.int32, device="cuda")
+    si = torch.empty((hkv, n), dtype=torch.int32, device="cuda")
+    sc = torch.empty((hkv,), dtype=torch.int32, device="cuda")
+    ws = torch.empty(vsa.vs_select_workspace_bytes(hkv, n), dtype=torch.uint8, device="cuda")
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ti, ts = [], []
+    for it in range(args.warmup + args.steps):
+        e[0].record()
+        vsa.vs_index(kd, vd, w1d, w2d, vlog, slog)
+        e[1].record()
+        vsa.vs_select(vlog, vsa.VS_VERTICAL, w["mass"], n, vi, vc, ws)
+        vsa.vs_select(slog, vsa.VS_SLASH, w["mass"], n, si, sc, ws)
+        e[2].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            ti.append(e[0].elapsed_time(e[1]))
+            ts.append(e[1].elapsed_time(e[2]))
+    ms_i, ms_s = float(np.mean(ti)), float(np.mean(ts))
+    bytes_alg = hkv * n * (2 * d * 2) + hkv * n * 8   # read K,V rows; write two fp32 logits
+    flops = hkv * n * (2.0 * 2 * d * w["hidden"] + 2.0 * 2 * w["hidden"])
+    gbs = bytes_alg / (ms_i * 1e-3) / 1e9
+    res = {
+        "metric": "VSIndexer + selection ms @128K (8 KV heads)",
+        "value": round(ms_i + ms_s, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_i + ms_s, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "indexer128k", "n": n, "h_kv": hkv, "d": d, "hidden": w["hidden"],
+                   "mass": w["mass"], "seed": w["seed"]},
+        "index_ms": round(ms_i, 4), "select_ms": round(ms_s, 4),
+        "index_tflops": round(flops / (ms_i * 1e-3) / 1e12, 3),
+        "budgets": {"vertical": vc.cpu().tolist(), "slash": sc.cpu().tolist()},
+        "roofline": {"bound": "hbm", "kernel": "index_kernel (vs_index)", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
