@@ -165,7 +165,8 @@ def test_clustered_offsets_and_gathered_columns():
                                           to_dev(scnt), workspace=ws)
     tiles = vsa.vs_attn_tile_counts(ws, hkv, n, vidx.shape[1], soff.shape[1], hq)
     assert tiles[1] > 0, "the gathered path was not exercised"
-    causal_tiles = hkv * sum((min((b + 1) * 32, n) - 1) // 64 + 1 for b in range((n + 31) // 32))
+    bmp = tiles[2] // (hq // hkv)
+    causal_tiles = hkv * sum((min((b + 1) * bmp, n) - 1) // tiles[3] + 1 for b in range((n + bmp - 1) // bmp))
     assert tiles[0] < causal_tiles
     out, lse = to_f64(out), lse.cpu().numpy().astype(np.float64)
     rows = sample_rows(np.random.default_rng(1), hq, n, 160)

@@ -31,6 +31,9 @@
 //    the B operand of O^T += V^T P^T with V^T staged in LDS in a matching
 //    key order.  The running maximum is only moved when it grows by more
 //    than 2^8 (the result is unchanged; p stays below 2^8 in fp32/bf16).
+#include <algorithm>
+#include <climits>
+
 #include "vs_common.h"
 #include "vs_internal.h"
 
@@ -177,13 +180,16 @@ __global__ __launch_bounds__(1024) void ws_cluster_kernel(const int32_t* __restr
 
 // ---------------------------------------------------------------- attention
 
+constexpr int kWaves = 8;               // waves per workgroup (two per SIMD)
+constexpr int kThreads = kWaves * 64;
+
 struct AttnParams {
   const void* q;
   const void* k;
   const void* v;
   void* out;
   float* lse;
-  int n, hkv, group, nblocks, bmp;
+  int n, hkv, group, hpw, nsplit, nblocks, bmp;
   float c;  // scale * log2(e)
   const uint32_t* bitO;
   const uint32_t* bitV;
@@ -203,41 +209,78 @@ template <bool F32>
 __device__ __forceinline__ u32x4 load8(const void* base, size_t elem) {
   if constexpr (F32) {
     const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
-    float4 a = p[0], b = p[1];
+    const float4 a = p[0], b = p[1];
     return u32x4{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w)};
   } else {
     return *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
   }
 }
 
-template <int D, bool F32, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
-  constexpr int NT = NW * 64;
+// bits [pos, pos + 64) of a bitmap whose words below 0 and past the end are zero
+__device__ __forceinline__ uint64_t win64(const uint32_t* bm, int pos) {
+  const int w = pos >> 5, sh = pos & 31;
+  const uint64_t lo = (uint64_t)bm[w] | ((uint64_t)bm[w + 1] << 32);
+  const uint64_t hi = bm[w + 2];
+  return sh ? (lo >> sh) | (hi << (64 - sh)) : lo;
+}
+
+// Tile sequence of one workgroup: contiguous key tiles (code >= 0, the tile
+// index) reached by the slash clusters in ascending key order, then tiles of
+// gathered columns (code = -1 - chunk).  All state is wave-uniform.
+struct TileSeq {
+  const int32_t* clo;
+  const int32_t* chi;
+  int c, t, thi, next_t, i0, i1;
+  int chunk, nchunks;
+  bool dense;
+};
+
+template <int D, bool F32>
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   constexpr int KS = D / 16;     // k-steps of Q K^T
   constexpr int DT = D / 32;     // 32-row tiles of O^T
   constexpr int KROW = D + 8;    // padded LDS row of K (bf16 elements)
   constexpr int VROW = kBN + 8;  // padded LDS row of V^T
-  __shared__ __align__(16) uint16_t k_lds[kBN * KROW];
-  __shared__ __align__(16) uint16_t vt_lds[D * VROW];
+  constexpr int KCH = D / 8;     // 16-byte chunks per K row
+  __shared__ __align__(16) uint16_t k_lds[2][kBN * KROW];
+  __shared__ __align__(16) uint16_t vt_lds[2][D * VROW];
   __shared__ __align__(16) int glist[kListCap];
-  __shared__ __align__(16) int gkeys[kBN];
-  __shared__ int wcnt[NW + 1];
+  __shared__ int wcnt[kWaves + 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, ql = lane & 31;
-  const int n = p.n, G = p.group;
-  const int g = blockIdx.x % p.hkv;                           // head g on XCD g (round-robin dispatch)
-  const int b = p.nblocks - 1 - (int)(blockIdx.x / p.hkv);    // longest causal rows first
+  const int n = p.n;
+  // block -> (KV head, head split, query block); consecutive blocks go to
+  // different XCDs, so head g lands on XCD g and its K/V stays in that L2
+  const int g = blockIdx.x % p.hkv;
+  const int rest = blockIdx.x / p.hkv;
+  const int split = rest % p.nsplit;
+  const int b = p.nblocks - 1 - rest / p.nsplit;  // longest causal rows first
   const int i0 = b * p.bmp;
   const int i1 = min(i0 + p.bmp, n) - 1;
-  const int head = g * G + (wave % G);
-  const int i0w = i0 + 32 * (wave / G);
+  const int head = g * p.group + split * p.hpw + (wave % p.hpw);
+  const int i0w = i0 + 32 * (wave / p.hpw);
   const int qrow = i0w + ql;
   const bool wave_rows = i0w < n;
-
-  const void* kg_base = p.k;
   const size_t kv_head = (size_t)g * n;
 
-  // Q^T fragments (B operand): lane holds row qrow, head-dim 16s + 8*half .. +7
+  const uint32_t* bo = p.bitO + (size_t)g * p.stride + kPrePad;
+  const uint32_t* bv = p.bitV + (size_t)g * p.stride + kPrePad;
+  const uint32_t* pfo = p.prefO + (size_t)g * (p.words + 1);
+  // number of selected offsets below x (0 <= x <= n)
+  auto prefix = [&](int x) -> int {
+    const int w = x >> 5, sh = x & 31;
+    return (int)pfo[w] + __popc(bo[w] & (sh ? ((1u << sh) - 1u) : 0u));
+  };
+  // does some offset link a row of this block to key tile T?
+  auto tile_active = [&](int T) -> bool {
+    const int wl = max(0, i0 - (T + 1) * kBN + 1), wh = i1 - T * kBN;
+    return prefix(wh + 1) - prefix(wl) > 0;
+  };
+  // In a full block every tile of a cluster's key range is active; the last
+  // block may be shorter than BMP rows, so there tiles are tested.
+  const bool partial = i1 < i0 + p.bmp - 1;
+
+  // Q^T fragments (B operand): lane holds row qrow, head dims 16s + 8*half .. +7
   bf16x8 qf[KS];
   {
     const size_t ro = ((size_t)head * n + min(qrow, n - 1)) * D;
@@ -257,51 +300,187 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   float m_run = kNoMax, l_run = 0.f;
   int n_dense = 0, n_gath = 0;
 
-  // ---- stage one 64-key tile of K (row-major) and V^T (key-permuted) into LDS
-  auto stage = [&](auto keyof) {
-    constexpr int KCH = D / 8;
-    for (int id = tid; id < kBN * KCH; id += NT) {
-      const int r = id / KCH, c8 = id % KCH;
-      const int key = keyof(r);
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (key >= 0) val = load8<F32>(kg_base, (kv_head + key) * D + 8 * c8);
-      *reinterpret_cast<u32x4*>(&k_lds[r * KROW + 8 * c8]) = val;
+  // ---- tile sequence
+  TileSeq seq;
+  {
+    seq.clo = p.clLo + (size_t)g * p.cap_s;
+    seq.chi = p.clHi + (size_t)g * p.cap_s;
+    const int ncl = p.counts[4 * g + 2];
+    int lo = 0, hi = ncl;  // first cluster whose smallest offset exceeds i1
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (seq.clo[mid] <= i1) lo = mid + 1;
+      else hi = mid;
     }
-    constexpr int VG = (kBN / 4) * (D / 8);
-    for (int id = tid; id < VG; id += NT) {
-      const int kgp = id & 15, dc = id >> 4;
-      u32x4 rows[4];
+    seq.c = lo - 1;
+    seq.t = 1;
+    seq.thi = 0;
+    seq.next_t = 0;
+    seq.i0 = i0;
+    seq.i1 = i1;
+    seq.chunk = 0;
+    seq.nchunks = 0;
+    seq.dense = true;
+  }
+  // next tile code, or INT_MIN when the sequence is exhausted
+  auto next_tile = [&]() -> int {
+    if (seq.dense) {
+      while (true) {
+        if (seq.t <= seq.thi) {
+          const int t = seq.t++;
+          if (partial && !tile_active(t)) continue;
+          return t;
+        }
+        if (seq.c < 0) break;
+        const int olo = seq.clo[seq.c], ohi = seq.chi[seq.c];
+        --seq.c;
+        const int klo = max(0, i0 - ohi), khi = i1 - olo;
+        seq.t = max(klo / kBN, seq.next_t);
+        seq.thi = khi / kBN;
+        seq.next_t = max(seq.next_t, seq.thi + 1);
+      }
+      seq.dense = false;
+    }
+    if (seq.chunk < seq.nchunks) return -1 - seq.chunk++;
+    return INT_MIN;
+  };
+
+  // ---- staging: waves 0-3 stage V^T (transposed, key-permuted), waves 4-7 stage K
+  u32x4 pre[4];
+  auto key_of = [&](int code, int r) -> int {
+    if (code >= 0) {
+      const int j = code * kBN + r;
+      return j < n ? j : -1;
+    }
+    const int base = (-1 - code) * kBN;
+    return glist[base + r];
+  };
+  auto load_tile = [&](int code) {
+    if (wave >= 4) {
+      const int tt = tid - 256;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int id = tt + 256 * it;
+        pre[it] = u32x4{0u, 0u, 0u, 0u};
+        if (id < kBN * KCH) {
+          const int key = key_of(code, id / KCH);
+          if (key >= 0) pre[it] = load8<F32>(p.k, (kv_head + key) * D + 8 * (id % KCH));
+        }
+      }
+    } else {
+      const int kgp = tid & 15, dc = tid >> 4;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int key = keyof(4 * kgp + rr);
-        rows[rr] = key >= 0 ? load8<F32>(p.v, (kv_head + key) * D + 8 * dc) : u32x4{0u, 0u, 0u, 0u};
+        pre[rr] = u32x4{0u, 0u, 0u, 0u};
+        if (dc < D / 8) {
+          const int key = key_of(code, 4 * kgp + rr);
+          if (key >= 0) pre[rr] = load8<F32>(p.v, (kv_head + key) * D + 8 * dc);
+        }
       }
-      // storage slot inside each 16-key chunk: the order in which the two
-      // wave halves consume keys as the k index of O^T += V^T P^T
-      const int pos = 16 * (kgp >> 2) + 8 * (kgp & 1) + 4 * ((kgp >> 1) & 1);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    if (wave >= 4) {
+      const int tt = tid - 256;
 #pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int w = dd >> 1, sh = (dd & 1) * 16;
-        const uint32_t lo = ((rows[0][w] >> sh) & 0xffffu) | (((rows[1][w] >> sh) & 0xffffu) << 16);
-        const uint32_t hi = ((rows[2][w] >> sh) & 0xffffu) | (((rows[3][w] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2*>(&vt_lds[(8 * dc + dd) * VROW + pos]) = u32x2{lo, hi};
+      for (int it = 0; it < 4; ++it) {
+        const int id = tt + 256 * it;
+        if (id < kBN * KCH)
+          *reinterpret_cast<u32x4*>(&k_lds[buf][(id / KCH) * KROW + 8 * (id % KCH)]) = pre[it];
+      }
+    } else {
+      const int kgp = tid & 15, dc = tid >> 4;
+      if (dc < D / 8) {
+        // slot of these 4 keys inside their 16-key chunk: the order in which
+        // the two wave halves consume keys as the k index of O^T += V^T P^T
+        const int pos = 16 * (kgp >> 2) + 8 * (kgp & 1) + 4 * ((kgp >> 1) & 1);
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          const int w = dd >> 1, sh = (dd & 1) * 16;
+          const uint32_t lo = ((pre[0][w] >> sh) & 0xffffu) | (((pre[1][w] >> sh) & 0xffffu) << 16);
+          const uint32_t hi = ((pre[2][w] >> sh) & 0xffffu) | (((pre[3][w] >> sh) & 0xffffu) << 16);
+          *reinterpret_cast<u32x2*>(&vt_lds[buf][(8 * dc + dd) * VROW + pos]) = u32x2{lo, hi};
+        }
       }
     }
   };
 
-  // ---- one tile of online softmax attention for this wave's 32 rows
-  auto attend = [&](auto apply_mask) {
+  // ---- one tile of online-softmax attention for this wave's 32 rows
+  auto attend = [&](int code, int buf) {
+    const uint16_t* kb = k_lds[buf];
+    const uint16_t* vb = vt_lds[buf];
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&k_lds[ql * KROW + 16 * kk + 8 * half]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&k_lds[(32 + ql) * KROW + 16 * kk + 8 * half]);
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&kb[ql * KROW + 16 * kk + 8 * half]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&kb[(32 + ql) * KROW + 16 * kk + 8 * half]);
       s0 = mfma32(a0, qf[kk], s0);
       s1 = mfma32(a1, qf[kk], s1);
     }
-    apply_mask(s0, s1);
+    if (code >= 0) {
+      const int j0 = code * kBN;
+      // offsets i - j of this wave's rows and the tile's keys: [i0w - j0 - 63, i0w - j0 + 31]
+      const int obase = i0w - j0 - (kBN - 1);
+      const uint64_t wlo = win64(bo, obase);
+      const uint64_t whi = win64(bo, obase + 64) & 0x7fffffffull;
+      const uint64_t vcols = (uint64_t)bv[j0 >> 5] | ((uint64_t)bv[(j0 >> 5) + 1] << 32);
+      const bool below = j0 + kBN - 1 <= i0w;
+      const bool full = below && ((wlo == ~0ull && whi == 0x7fffffffull) || vcols == ~0ull);
+      if (!full) {
+#pragma unroll
+        for (int sk = 0; sk < 2; ++sk) {
+          const uint32_t vsk = (uint32_t)(vcols >> (32 * sk));
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            // window starting at the offset of lane 0 for the upper half's last key
+            const uint64_t wa = win64(bo, i0w - j0 - 32 * sk - 8 * a - 7);
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+              uint32_t lo32 = (uint32_t)(wa >> (7 - bb));
+              uint32_t hi32 = (uint32_t)(wa >> (3 - bb));
+              if (vsk) {
+                const int kk0 = 8 * a + bb;  // key of the lower half in this 32-key subtile
+                if (below) {
+                  lo32 |= (uint32_t)(-(int32_t)((vsk >> kk0) & 1u));
+                  hi32 |= (uint32_t)(-(int32_t)((vsk >> (kk0 + 4)) & 1u));
+                } else {
+                  if ((vsk >> kk0) & 1u) {
+                    const int df = j0 + 32 * sk + kk0 - i0w;
+                    lo32 |= df <= 0 ? ~0u : (df >= 32 ? 0u : (~0u << df));
+                  }
+                  if ((vsk >> (kk0 + 4)) & 1u) {
+                    const int df = j0 + 32 * sk + kk0 + 4 - i0w;
+                    hi32 |= df <= 0 ? ~0u : (df >= 32 ? 0u : (~0u << df));
+                  }
+                }
+              }
+              const uint64_t m = (uint64_t)lo32 | ((uint64_t)hi32 << 32);
+              const int e = 4 * a + bb;
+              if (sk == 0) s0[e] = select_mask(m, s0[e], -__builtin_inff());
+              else s1[e] = select_mask(m, s1[e], -__builtin_inff());
+            }
+          }
+        }
+      }
+    } else {
+      const int* keys = &glist[(-1 - code) * kBN];
+#pragma unroll
+      for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int4 ks = *reinterpret_cast<const int4*>(&keys[32 * sk + 8 * a + 4 * half]);
+          const int kv4[4] = {ks.x, ks.y, ks.z, ks.w};
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const bool ok = kv4[bb] >= 0 && kv4[bb] <= qrow;
+            const int e = 4 * a + bb;
+            if (sk == 0) s0[e] = ok ? s0[e] : -__builtin_inff();
+            else s1[e] = ok ? s1[e] : -__builtin_inff();
+          }
+        }
+    }
     float mx = -__builtin_inff();
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
@@ -318,123 +497,43 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
       m_run = mn;
     }
     const float nm = -m_run;
+    uint32_t pk[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      s0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], p.c, nm));
-      s1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], p.c, nm));
-      l_run += s0[e] + s1[e];
+    for (int e = 0; e < 8; ++e) {
+      pk[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s0[2 * e], p.c, nm)),
+                        __builtin_amdgcn_exp2f(fmaf(s0[2 * e + 1], p.c, nm)));
+      pk[8 + e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s1[2 * e], p.c, nm)),
+                            __builtin_amdgcn_exp2f(fmaf(s1[2 * e + 1], p.c, nm)));
     }
-    bf16x8 pf[4];
-    pf[0] = as_bf16x8(u32x4{pack_bf16(s0[0], s0[1]), pack_bf16(s0[2], s0[3]), pack_bf16(s0[4], s0[5]), pack_bf16(s0[6], s0[7])});
-    pf[1] = as_bf16x8(u32x4{pack_bf16(s0[8], s0[9]), pack_bf16(s0[10], s0[11]), pack_bf16(s0[12], s0[13]), pack_bf16(s0[14], s0[15])});
-    pf[2] = as_bf16x8(u32x4{pack_bf16(s1[0], s1[1]), pack_bf16(s1[2], s1[3]), pack_bf16(s1[4], s1[5]), pack_bf16(s1[6], s1[7])});
-    pf[3] = as_bf16x8(u32x4{pack_bf16(s1[8], s1[9]), pack_bf16(s1[10], s1[11]), pack_bf16(s1[12], s1[13]), pack_bf16(s1[14], s1[15])});
+    // row sum of the bf16 probabilities the PV product uses
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4)
+    for (int e = 0; e < 16; ++e)
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, l_run, false);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const bf16x8 pf = as_bf16x8(u32x4{pk[4 * c4], pk[4 * c4 + 1], pk[4 * c4 + 2], pk[4 * c4 + 3]});
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vt_lds[(32 * dt + ql) * VROW + 16 * c4 + 8 * half]);
-        acc[dt] = mfma32(av, pf[c4], acc[dt]);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vb[(32 * dt + ql) * VROW + 16 * c4 + 8 * half]);
+        acc[dt] = mfma32(av, pf, acc[dt]);
       }
-  };
-
-  const uint32_t* bo = p.bitO + (size_t)g * p.stride + kPrePad;
-  const uint32_t* bv = p.bitV + (size_t)g * p.stride + kPrePad;
-  // bits [pos, pos + 64) of a bitmap; pos >= -128, words past the end are zero
-  auto win64 = [](const uint32_t* bm, int pos) -> uint64_t {
-    const int w = pos >> 5, sh = pos & 31;
-    const uint64_t lo = (uint64_t)bm[w] | ((uint64_t)bm[w + 1] << 32);
-    const uint64_t hi = bm[w + 2];
-    return sh ? (lo >> sh) | (hi << (64 - sh)) : lo;
-  };
-
-  // number of selected offsets below x (0 <= x <= n)
-  const uint32_t* pfo = p.prefO + (size_t)g * (p.words + 1);
-  auto prefix = [&](int x) -> int {
-    const int w = x >> 5, sh = x & 31;
-    return (int)pfo[w] + __popc(bo[w] & (sh ? ((1u << sh) - 1u) : 0u));
-  };
-  // key tile T holds a selected (row, key) pair of this block through some offset
-  auto tile_active = [&](int T) -> bool {
-    const int wl = max(0, i0 - (T + 1) * kBN + 1), wh = i1 - T * kBN;
-    return prefix(wh + 1) - prefix(wl) > 0;
-  };
-  // In a full block every tile of a cluster's key range is active; the last
-  // block may be shorter than BMP rows, so there the tiles are tested.
-  const bool partial = i1 < i0 + p.bmp - 1;
-
-  // ---------------- phase A: contiguous key tiles reached by slash clusters
-  {
-    const int32_t* clo = p.clLo + (size_t)g * p.cap_s;
-    const int32_t* chi = p.clHi + (size_t)g * p.cap_s;
-    const int ncl = p.counts[4 * g + 2];
-    int lo = 0, hi = ncl;  // first cluster whose smallest offset exceeds i1
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (clo[mid] <= i1) lo = mid + 1;
-      else hi = mid;
     }
-    int next_t = 0;
-    for (int c = lo - 1; c >= 0; --c) {
-      const int olo = clo[c], ohi = chi[c];
-      const int klo = max(0, i0 - ohi), khi = i1 - olo;
-      const int tlo = max(klo / kBN, next_t), thi = khi / kBN;
-      for (int t = tlo; t <= thi; ++t) {
-        if (partial && !tile_active(t)) continue;
-        const int j0 = t * kBN;
-        __syncthreads();
-        stage([&](int r) { const int j = j0 + r; return j < n ? j : -1; });
-        __syncthreads();
-        ++n_dense;
-        if (!wave_rows || j0 > i0w + 31) continue;
-        // offsets i - j seen by this wave's tile: [i0w - j0 - 63, i0w - j0 + 31]
-        const int obase = i0w - j0 - (kBN - 1);
-        const uint64_t wlo = win64(bo, obase), whi = win64(bo, obase + 64) & 0x7fffffffull;
-        const uint64_t vcols = (uint64_t)bv[j0 >> 5] | ((uint64_t)bv[(j0 >> 5) + 1] << 32);
-        const bool below = j0 + kBN - 1 <= i0w;
-        if (below && ((wlo == ~0ull && whi == 0x7fffffffull) || vcols == ~0ull)) {
-          attend([](f32x16&, f32x16&) {});
-          continue;
-        }
-        const bool vert_hit = vcols != 0ull && (j0 + __builtin_ctzll(vcols | (1ull << 63))) <= i0w + 31;
-        if (wlo == 0ull && whi == 0ull && !vert_hit) continue;
-        attend([&](f32x16& s0, f32x16& s1) {
-#pragma unroll
-          for (int sk = 0; sk < 2; ++sk)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-              // window starting at the offset of lane 0, upper half, last of the 4 keys
-              const uint64_t wa = win64(bo, i0w - j0 - 32 * sk - 8 * a - 7);
-#pragma unroll
-              for (int bb = 0; bb < 4; ++bb) {
-                uint32_t lo32 = (uint32_t)(wa >> (7 - bb));
-                uint32_t hi32 = (uint32_t)(wa >> (3 - bb));
-                if (vcols) {
-                  const int kk0 = 32 * sk + 8 * a + bb;  // key index in tile, lower half
-                  if ((vcols >> kk0) & 1ull) {
-                    const int df = j0 + kk0 - i0w;
-                    lo32 |= df <= 0 ? ~0u : (df >= 32 ? 0u : (~0u << df));
-                  }
-                  if ((vcols >> (kk0 + 4)) & 1ull) {
-                    const int df = j0 + kk0 + 4 - i0w;
-                    hi32 |= df <= 0 ? ~0u : (df >= 32 ? 0u : (~0u << df));
-                  }
-                }
-                const uint64_t m = (uint64_t)lo32 | ((uint64_t)hi32 << 32);
-                const int e = 4 * a + bb;
-                if (sk == 0) s0[e] = select_mask(m, s0[e], -__builtin_inff());
-                else s1[e] = select_mask(m, s1[e], -__builtin_inff());
-              }
-            }
-        });
-      }
-      next_t = max(next_t, thi + 1);
-    }
-  }
+  };
 
-  // ---------------- phase B: selected columns outside every processed tile
+  // does this wave have rows that can see keys of the tile?
+  auto wave_sees = [&](int code) -> bool {
+    if (!wave_rows) return false;
+    if (code >= 0) return code * kBN <= i0w + 31;
+    return glist[(-1 - code) * kBN] <= i0w + 31;  // gathered keys ascend
+  };
+
+  // ---- rounds: each gathers up to kListCap uncovered columns; the first
+  //      round also walks the contiguous tiles
+  const int32_t* cv = p.cleanV + (size_t)g * p.cap_v;
+  int total_v;
   {
-    const int32_t* cv = p.cleanV + (size_t)g * p.cap_v;
     const int nv = p.counts[4 * g + 1];
     int lo = 0, hi = nv;  // columns <= i1
     while (lo < hi) {
@@ -442,60 +541,65 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
       if (cv[mid] <= i1) lo = mid + 1;
       else hi = mid;
     }
-    const int total = lo;
-    int cursor = 0;
-    while (cursor < total) {
-      int fill = 0;
-      while (cursor < total && fill + NT <= kListCap) {
-        const int idx = cursor + tid;
-        bool keep = false;
-        int col = 0;
-        if (idx < total) {
-          col = cv[idx];
-          keep = !tile_active(col / kBN);  // its tile was not processed in phase A
-        }
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
-        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-        if (lane == 0) wcnt[wave] = __popcll(bal);
-        __syncthreads();
-        int before = 0, all = 0;
-        for (int w = 0; w < NW; ++w) {
-          const int c = wcnt[w];
-          before += w < wave ? c : 0;
-          all += c;
-        }
-        if (keep) glist[fill + before + below] = col;
-        fill += all;
-        cursor += NT;
-        __syncthreads();
+    total_v = lo;
+  }
+  int cursor = 0;
+  bool first_round = true;
+  while (first_round || cursor < total_v) {
+    // gather the next batch of columns whose tile no offset reaches
+    int fill = 0;
+    while (cursor < total_v && fill + kThreads <= kListCap) {
+      const int idx = cursor + tid;
+      bool keep = false;
+      int col = 0;
+      if (idx < total_v) {
+        col = cv[idx];
+        keep = !tile_active(col / kBN);
       }
-      for (int kb = 0; kb < fill; kb += kBN) {
-        const int cnt = min(kBN, fill - kb);
-        __syncthreads();
-        if (tid < kBN) gkeys[tid] = tid < cnt ? glist[kb + tid] : -1;
-        __syncthreads();
-        stage([&](int r) { return gkeys[r]; });
-        __syncthreads();
-        ++n_gath;
-        if (!wave_rows || gkeys[0] > i0w + 31) continue;
-        attend([&](f32x16& s0, f32x16& s1) {
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+      const int below_l = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (lane == 0) wcnt[wave] = __popcll(bal);
+      __syncthreads();
+      int before = 0, all = 0;
 #pragma unroll
-          for (int sk = 0; sk < 2; ++sk)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-              const int4 ks = *reinterpret_cast<const int4*>(&gkeys[32 * sk + 8 * a + 4 * half]);
-              const int kv4[4] = {ks.x, ks.y, ks.z, ks.w};
-#pragma unroll
-              for (int bb = 0; bb < 4; ++bb) {
-                const bool ok = kv4[bb] >= 0 && kv4[bb] <= qrow;
-                const int e = 4 * a + bb;
-                if (sk == 0) s0[e] = ok ? s0[e] : -__builtin_inff();
-                else s1[e] = ok ? s1[e] : -__builtin_inff();
-              }
-            }
-        });
+      for (int w = 0; w < kWaves; ++w) {
+        const int cw = wcnt[w];
+        before += w < wave ? cw : 0;
+        all += cw;
       }
+      if (keep) glist[fill + before + below_l] = col;
+      fill += all;
+      cursor += kThreads;
+      __syncthreads();
     }
+    // pad the last gathered chunk
+    for (int r = fill + tid; r < ((fill + kBN - 1) / kBN) * kBN; r += kThreads) glist[r] = -1;
+    seq.chunk = 0;
+    seq.nchunks = (fill + kBN - 1) / kBN;
+    if (!first_round) seq.dense = false;
+    first_round = false;
+    __syncthreads();
+
+    // software pipeline: prefetch tile t+1 into registers while tile t computes
+    int cur = next_tile();
+    if (cur == INT_MIN) continue;
+    load_tile(cur);
+    store_tile(0);
+    __syncthreads();
+    int buf = 0;
+    while (true) {
+      const int nxt = next_tile();
+      if (nxt != INT_MIN) load_tile(nxt);
+      if (cur >= 0) ++n_dense;
+      else ++n_gath;
+      if (wave_sees(cur)) attend(cur, buf);
+      if (nxt == INT_MIN) break;
+      store_tile(buf ^ 1);
+      __syncthreads();
+      cur = nxt;
+      buf ^= 1;
+    }
+    __syncthreads();
   }
 
   // ---------------- finish: normalise, write O and lse
@@ -526,30 +630,14 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   }
 }
 
-template <int D, bool F32>
-hipError_t launch_attn_kernel(const AttnParams& prm, int nw, hipStream_t stream) {
-  const dim3 grid((unsigned)prm.nblocks * (unsigned)prm.hkv);
-  switch (nw) {
-    case 4:
-      hipLaunchKernelGGL((attn_kernel<D, F32, 4>), grid, dim3(256), 0, stream, prm);
-      break;
-    case 8:
-      hipLaunchKernelGGL((attn_kernel<D, F32, 8>), grid, dim3(512), 0, stream, prm);
-      break;
-    case 16:
-      hipLaunchKernelGGL((attn_kernel<D, F32, 16>), grid, dim3(1024), 0, stream, prm);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-int waves_for_group(int group) { return group < 4 ? 4 : group; }
+int heads_per_block(int group) { return group < kWaves ? group : kWaves; }
 
 }  // namespace
 
-int attn_query_rows_per_block(int group) { return 32 * waves_for_group(group); }
+int attn_query_rows_per_block(int group) {
+  (void)group;
+  return 32 * kWaves;
+}
 
 hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, int h_q, int h_kv,
                        int n, int d, float scale, const int32_t* v_idx, const int32_t* v_cnt,
@@ -568,8 +656,9 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
   unsigned long long* stats = reinterpret_cast<unsigned long long*>(base + L.off_stats);
 
   const int group = h_q / h_kv;
-  const int nw = waves_for_group(group);
-  const int bmp = 32 * nw / group;  // query positions per workgroup
+  const int hpw = heads_per_block(group);   // query heads per workgroup
+  const int nsplit = group / hpw;           // workgroups sharing one block of a group
+  const int bmp = 32 * (kWaves / hpw);      // query positions per workgroup
 
   const size_t nwords = (size_t)h_kv * L.stride;
   hipLaunchKernelGGL(ws_clear_kernel, dim3((unsigned)std::min<size_t>((nwords + 255) / 256, 2048)),
@@ -595,6 +684,8 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
   prm.n = n;
   prm.hkv = h_kv;
   prm.group = group;
+  prm.hpw = hpw;
+  prm.nsplit = nsplit;
   prm.bmp = bmp;
   prm.nblocks = (n + bmp - 1) / bmp;
   prm.c = scale * kLog2e;
@@ -610,10 +701,15 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
   prm.cap_s = cap_s;
   prm.counts = counts;
   prm.stats = stats;
-  if (d == 128) return f32 ? launch_attn_kernel<128, true>(prm, nw, stream)
-                           : launch_attn_kernel<128, false>(prm, nw, stream);
-  return f32 ? launch_attn_kernel<64, true>(prm, nw, stream)
-             : launch_attn_kernel<64, false>(prm, nw, stream);
+  const dim3 grid((unsigned)((long long)prm.nblocks * h_kv * nsplit));
+  if (d == 128) {
+    if (f32) hipLaunchKernelGGL((attn_kernel<128, true>), grid, dim3(kThreads), 0, stream, prm);
+    else hipLaunchKernelGGL((attn_kernel<128, false>), grid, dim3(kThreads), 0, stream, prm);
+  } else {
+    if (f32) hipLaunchKernelGGL((attn_kernel<64, true>), grid, dim3(kThreads), 0, stream, prm);
+    else hipLaunchKernelGGL((attn_kernel<64, false>), grid, dim3(kThreads), 0, stream, prm);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace vs

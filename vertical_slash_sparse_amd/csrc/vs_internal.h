@@ -11,7 +11,7 @@ namespace vs {
 constexpr int kBN = 64;          // keys per attention tile
 constexpr int kPrePad = 4;       // zero words before each bitmap (windows may start below 0)
 constexpr int kPostPad = 8;      // zero words after each bitmap (windows may run past n)
-constexpr int kListCap = 1024;   // LDS list of gathered verticals per refill
+constexpr int kListCap = 2048;   // LDS list of gathered columns per refill
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
