@@ -216,12 +216,11 @@ __device__ __forceinline__ u32x4 load8(const void* base, size_t elem) {
   }
 }
 
-// bits [pos, pos + 64) of a bitmap whose words below 0 and past the end are zero
-__device__ __forceinline__ uint64_t win64(const uint32_t* bm, int pos) {
-  const int w = pos >> 5, sh = pos & 31;
-  const uint64_t lo = (uint64_t)bm[w] | ((uint64_t)bm[w + 1] << 32);
-  const uint64_t hi = bm[w + 2];
-  return sh ? (lo >> sh) | (hi << (64 - sh)) : lo;
+// load through the scalar cache: the address must be wave-uniform and the
+// memory must not change while the kernel runs
+template <typename T>
+__device__ __forceinline__ T ldc(const T* ptr, long idx) {
+  return ((const __attribute__((address_space(4))) T*)ptr)[idx];
 }
 
 // Tile sequence of one workgroup: contiguous key tiles (code >= 0, the tile
@@ -247,7 +246,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   __shared__ __align__(16) int glist[kListCap];
   __shared__ int wcnt[kWaves + 1];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, ql = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, ql = lane & 31;
+  const int wave = wave_uniform(tid >> 6);  // keep everything derived from it in SGPRs
   const int n = p.n;
   // block -> (KV head, head split, query block); consecutive blocks go to
   // different XCDs, so head g lands on XCD g and its K/V stays in that L2
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   // number of selected offsets below x (0 <= x <= n)
   auto prefix = [&](int x) -> int {
     const int w = x >> 5, sh = x & 31;
-    return (int)pfo[w] + __popc(bo[w] & (sh ? ((1u << sh) - 1u) : 0u));
+    return (int)ldc(pfo, w) + __popc(ldc(bo, w) & (sh ? ((1u << sh) - 1u) : 0u));
   };
   // does some offset link a row of this block to key tile T?
   auto tile_active = [&](int T) -> bool {
@@ -305,11 +305,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   {
     seq.clo = p.clLo + (size_t)g * p.cap_s;
     seq.chi = p.clHi + (size_t)g * p.cap_s;
-    const int ncl = p.counts[4 * g + 2];
+    const int ncl = ldc(p.counts, 4 * g + 2);
     int lo = 0, hi = ncl;  // first cluster whose smallest offset exceeds i1
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (seq.clo[mid] <= i1) lo = mid + 1;
+      if (ldc(seq.clo, mid) <= i1) lo = mid + 1;
       else hi = mid;
     }
     seq.c = lo - 1;
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
           return t;
         }
         if (seq.c < 0) break;
-        const int olo = seq.clo[seq.c], ohi = seq.chi[seq.c];
+        const int olo = ldc(seq.clo, seq.c), ohi = ldc(seq.chi, seq.c);
         --seq.c;
         const int klo = max(0, i0 - ohi), khi = i1 - olo;
         seq.t = max(klo / kBN, seq.next_t);
@@ -345,7 +345,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     return INT_MIN;
   };
 
-  // ---- staging: waves 0-3 stage V^T (transposed, key-permuted), waves 4-7 stage K
+  // ---- staging: waves 0-3 stage V^T (transposed, key-permuted), waves 4-7 stage K;
+  //      every lane also fetches the offset-bitmap words its row needs for the tile
   u32x4 pre[4];
   auto key_of = [&](int code, int r) -> int {
     if (code >= 0) {
@@ -355,7 +356,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     const int base = (-1 - code) * kBN;
     return glist[base + r];
   };
-  auto load_tile = [&](int code) {
+  auto load_tile = [&](int code, uint32_t (&bw)[3]) {
+    if (code >= 0) {
+      // offsets qrow - j for the tile's keys: [qrow - j0 - 63, qrow - j0]
+      const int wq = max((qrow - code * kBN - (kBN - 1)) >> 5, -kPrePad);
+      bw[0] = bo[wq];
+      bw[1] = bo[wq + 1];
+      bw[2] = bo[wq + 2];
+    }
     if (wave >= 4) {
       const int tt = tid - 256;
 #pragma unroll
@@ -406,9 +414,41 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   };
 
   // ---- one tile of online-softmax attention for this wave's 32 rows
-  auto attend = [&](int code, int buf) {
+  auto attend = [&](int code, int buf, const uint32_t (&bw)[3]) {
     const uint16_t* kb = k_lds[buf];
     const uint16_t* vb = vt_lds[buf];
+    // Per lane, a 64-bit word K with bit kk set when key j0 + kk is in S_qrow.
+    // The lane's scores are keys kk = 32*sk + 8*a + 4*half + bb (sk, a, bb
+    // the element coordinates), so Kh = K >> (4*half) puts element (sk, a, bb)
+    // at bit 32*sk + 8*a + bb.
+    uint32_t kh0 = ~0u, kh1 = ~0u;
+    bool masked = true;
+    if (code >= 0) {
+      const int j0 = code * kBN;
+      const int dq = qrow - j0;  // largest causal key index of this row
+      // bits of the offset bitmap from offset dq - 63 upward: bit x <-> key 63 - x
+      const int sh = (dq - (kBN - 1)) & 31;
+      const uint32_t l0 = __builtin_amdgcn_alignbit(bw[1], bw[0], sh);
+      const uint32_t l1 = __builtin_amdgcn_alignbit(bw[2], bw[1], sh);
+      uint32_t k0 = __builtin_bitreverse32(l1), k1 = __builtin_bitreverse32(l0);
+      const uint32_t vw0 = ldc(bv, j0 >> 5), vw1 = ldc(bv, (j0 >> 5) + 1);
+      if (vw0 | vw1) {
+        if (j0 + kBN - 1 <= i0w) {
+          k0 |= vw0;
+          k1 |= vw1;
+        } else {
+          // columns are visible only up to key dq
+          const uint32_t c0 = dq >= 31 ? ~0u : (dq < 0 ? 0u : ((2u << dq) - 1u));
+          const uint32_t c1 = dq >= 63 ? ~0u : (dq < 32 ? 0u : ((2u << (dq - 32)) - 1u));
+          k0 |= vw0 & c0;
+          k1 |= vw1 & c1;
+        }
+      }
+      if (!__builtin_amdgcn_ballot_w64((k0 | k1) != 0u)) return;          // nothing to add
+      masked = __builtin_amdgcn_ballot_w64((k0 & k1) != ~0u) != 0ull;   // else every key counts
+      kh0 = __builtin_amdgcn_alignbit(k1, k0, 4 * half);
+      kh1 = k1 >> (4 * half);
+    }
     f32x16 s0, s1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
@@ -420,48 +460,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       s1 = mfma32(a1, qf[kk], s1);
     }
     if (code >= 0) {
-      const int j0 = code * kBN;
-      // offsets i - j of this wave's rows and the tile's keys: [i0w - j0 - 63, i0w - j0 + 31]
-      const int obase = i0w - j0 - (kBN - 1);
-      const uint64_t wlo = win64(bo, obase);
-      const uint64_t whi = win64(bo, obase + 64) & 0x7fffffffull;
-      const uint64_t vcols = (uint64_t)bv[j0 >> 5] | ((uint64_t)bv[(j0 >> 5) + 1] << 32);
-      const bool below = j0 + kBN - 1 <= i0w;
-      const bool full = below && ((wlo == ~0ull && whi == 0x7fffffffull) || vcols == ~0ull);
-      if (!full) {
+      if (masked) {
 #pragma unroll
-        for (int sk = 0; sk < 2; ++sk) {
-          const uint32_t vsk = (uint32_t)(vcols >> (32 * sk));
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            // window starting at the offset of lane 0 for the upper half's last key
-            const uint64_t wa = win64(bo, i0w - j0 - 32 * sk - 8 * a - 7);
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-              uint32_t lo32 = (uint32_t)(wa >> (7 - bb));
-              uint32_t hi32 = (uint32_t)(wa >> (3 - bb));
-              if (vsk) {
-                const int kk0 = 8 * a + bb;  // key of the lower half in this 32-key subtile
-                if (below) {
-                  lo32 |= (uint32_t)(-(int32_t)((vsk >> kk0) & 1u));
-                  hi32 |= (uint32_t)(-(int32_t)((vsk >> (kk0 + 4)) & 1u));
-                } else {
-                  if ((vsk >> kk0) & 1u) {
-                    const int df = j0 + 32 * sk + kk0 - i0w;
-                    lo32 |= df <= 0 ? ~0u : (df >= 32 ? 0u : (~0u << df));
-                  }
-                  if ((vsk >> (kk0 + 4)) & 1u) {
-                    const int df = j0 + 32 * sk + kk0 + 4 - i0w;
-                    hi32 |= df <= 0 ? ~0u : (df >= 32 ? 0u : (~0u << df));
-                  }
-                }
-              }
-              const uint64_t m = (uint64_t)lo32 | ((uint64_t)hi32 << 32);
-              const int e = 4 * a + bb;
-              if (sk == 0) s0[e] = select_mask(m, s0[e], -__builtin_inff());
-              else s1[e] = select_mask(m, s1[e], -__builtin_inff());
-            }
-          }
+        for (int e = 0; e < 16; ++e) {
+          const int b = 8 * (e >> 2) + (e & 3);
+          const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kh0, b, 1);
+          const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kh1, b, 1);
+          s0[e] = __uint_as_float((m0 & __float_as_uint(s0[e])) | (~m0 & 0xff800000u));
+          s1[e] = __uint_as_float((m1 & __float_as_uint(s1[e])) | (~m1 & 0xff800000u));
         }
       }
     } else {
@@ -474,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
           const int kv4[4] = {ks.x, ks.y, ks.z, ks.w};
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb) {
-            const bool ok = kv4[bb] >= 0 && kv4[bb] <= qrow;
+            const bool ok = (unsigned)kv4[bb] <= (unsigned)qrow;  // padding (-1) fails
             const int e = 4 * a + bb;
             if (sk == 0) s0[e] = ok ? s0[e] : -__builtin_inff();
             else s1[e] = ok ? s1[e] : -__builtin_inff();
@@ -534,11 +540,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   const int32_t* cv = p.cleanV + (size_t)g * p.cap_v;
   int total_v;
   {
-    const int nv = p.counts[4 * g + 1];
+    const int nv = ldc(p.counts, 4 * g + 1);
     int lo = 0, hi = nv;  // columns <= i1
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (cv[mid] <= i1) lo = mid + 1;
+      if (ldc(cv, mid) <= i1) lo = mid + 1;
       else hi = mid;
     }
     total_v = lo;
@@ -583,21 +589,24 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     // software pipeline: prefetch tile t+1 into registers while tile t computes
     int cur = next_tile();
     if (cur == INT_MIN) continue;
-    load_tile(cur);
+    uint32_t bwc[3] = {0u, 0u, 0u}, bwn[3] = {0u, 0u, 0u};
+    load_tile(cur, bwc);
     store_tile(0);
     __syncthreads();
     int buf = 0;
     while (true) {
       const int nxt = next_tile();
-      if (nxt != INT_MIN) load_tile(nxt);
+      if (nxt != INT_MIN) load_tile(nxt, bwn);
       if (cur >= 0) ++n_dense;
       else ++n_gath;
-      if (wave_sees(cur)) attend(cur, buf);
+      if (wave_sees(cur)) attend(cur, buf, bwc);
       if (nxt == INT_MIN) break;
       store_tile(buf ^ 1);
       __syncthreads();
       cur = nxt;
       buf ^= 1;
+#pragma unroll
+      for (int w = 0; w < 3; ++w) bwc[w] = bwn[w];
     }
     __syncthreads();
   }
