@@ -81,6 +81,8 @@ vs_status vs_sparse_attn_prefill(const void* q, const void* k, const void* v, vs
   if ((long long)n > (1LL << 30) || (long long)h_kv * n * d > (1LL << 40)) return VS_ERR_INVALID;
   if (!group_ok(h_q, h_kv)) return VS_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return VS_ERR_UNSUPPORTED;
+  // one KV head must fit a 32-bit buffer range
+  if ((long long)n * d * (dt == VS_F32 ? 4 : 2) >= (1LL << 31)) return VS_ERR_UNSUPPORTED;
   if (ws_bytes < vs_attn_workspace_bytes(h_kv, n, cap_v, cap_s)) return VS_ERR_WORKSPACE;
   return from_hip(launch_attn(q, k, v, dt == VS_F32, h_q, h_kv, n, d, scale, v_idx, v_cnt, cap_v,
                               s_off, s_cnt, cap_s, out, lse, ws, stream));

@@ -346,16 +346,32 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   };
 
   // ---- staging: waves 0-3 stage V^T (transposed, key-permuted), waves 4-7 stage K;
-  //      every lane also fetches the offset-bitmap words its row needs for the tile
-  u32x4 pre[4];
-  auto key_of = [&](int code, int r) -> int {
-    if (code >= 0) {
-      const int j = code * kBN + r;
-      return j < n ? j : -1;
+  //      every lane also fetches the offset-bitmap words its row needs for the tile.
+  // K and V rows are read through buffer resources that cover exactly this
+  // head's n rows: rows at or past n (the tail tile, gathered padding) read
+  // as zeros with no branch.
+  constexpr int ESZ = F32 ? 4 : 2;
+  constexpr int ROWB = D * ESZ;  // bytes per K/V row
+  const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(static_cast<const char*>(p.k) + kv_head * ROWB), (short)0, n * ROWB, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(static_cast<const char*>(p.v) + kv_head * ROWB), (short)0, n * ROWB, kBufferFlags);
+  auto bload8 = [&](const __amdgpu_buffer_rsrc_t& rs, unsigned off) -> u32x4 {
+    if constexpr (F32) {
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+      const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 16), 0, 0);
+      return u32x4{pack_bf16(__uint_as_float(a[0]), __uint_as_float(a[1])),
+                   pack_bf16(__uint_as_float(a[2]), __uint_as_float(a[3])),
+                   pack_bf16(__uint_as_float(c[0]), __uint_as_float(c[1])),
+                   pack_bf16(__uint_as_float(c[2]), __uint_as_float(c[3]))};
+    } else {
+      return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
     }
-    const int base = (-1 - code) * kBN;
-    return glist[base + r];
   };
+  constexpr int KRS = kThreads / 2 / KCH;  // K rows staged per pass of 256 threads
+  const int k_row0 = (tid - 256) / KCH, k_c8 = (tid - 256) % KCH;
+  const int v_kgp = tid & 15, v_dc = tid >> 4;
+  u32x4 pre[4];
   auto load_tile = [&](int code, uint32_t (&bw)[3]) {
     if (code >= 0) {
       // offsets qrow - j for the tile's keys: [qrow - j0 - 63, qrow - j0]
@@ -364,51 +380,55 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       bw[1] = bo[wq + 1];
       bw[2] = bo[wq + 2];
     }
+    const int* gk = glist + (code < 0 ? (-1 - code) * kBN : 0);
     if (wave >= 4) {
-      const int tt = tid - 256;
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int id = tt + 256 * it;
-        pre[it] = u32x4{0u, 0u, 0u, 0u};
-        if (id < kBN * KCH) {
-          const int key = key_of(code, id / KCH);
-          if (key >= 0) pre[it] = load8<F32>(p.k, (kv_head + key) * D + 8 * (id % KCH));
+        if (it * KRS < kBN) {
+          const int r = k_row0 + KRS * it;
+          int key = code >= 0 ? code * kBN + r : gk[r];
+          key = key < 0 ? n : key;  // padding: first row past the buffer
+          pre[it] = bload8(rsk, (unsigned)key * ROWB + k_c8 * 8 * ESZ);
         }
       }
-    } else {
-      const int kgp = tid & 15, dc = tid >> 4;
+    } else if (v_dc < D / 8) {
+      int4 keys4;
+      if (code >= 0) {
+        const int k0 = code * kBN + 4 * v_kgp;
+        keys4 = int4{k0, k0 + 1, k0 + 2, k0 + 3};
+      } else {
+        keys4 = *reinterpret_cast<const int4*>(&gk[4 * v_kgp]);
+      }
+      const int kk[4] = {keys4.x, keys4.y, keys4.z, keys4.w};
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        pre[rr] = u32x4{0u, 0u, 0u, 0u};
-        if (dc < D / 8) {
-          const int key = key_of(code, 4 * kgp + rr);
-          if (key >= 0) pre[rr] = load8<F32>(p.v, (kv_head + key) * D + 8 * dc);
-        }
+        const int key = kk[rr] < 0 ? n : kk[rr];
+        pre[rr] = bload8(rsv, (unsigned)key * ROWB + v_dc * 8 * ESZ);
       }
     }
   };
   auto store_tile = [&](int buf) {
     if (wave >= 4) {
-      const int tt = tid - 256;
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int id = tt + 256 * it;
-        if (id < kBN * KCH)
-          *reinterpret_cast<u32x4*>(&k_lds[buf][(id / KCH) * KROW + 8 * (id % KCH)]) = pre[it];
-      }
-    } else {
-      const int kgp = tid & 15, dc = tid >> 4;
-      if (dc < D / 8) {
-        // slot of these 4 keys inside their 16-key chunk: the order in which
-        // the two wave halves consume keys as the k index of O^T += V^T P^T
-        const int pos = 16 * (kgp >> 2) + 8 * (kgp & 1) + 4 * ((kgp >> 1) & 1);
+      for (int it = 0; it < 4; ++it)
+        if (it * KRS < kBN)
+          *reinterpret_cast<u32x4*>(&k_lds[buf][(k_row0 + KRS * it) * KROW + 8 * k_c8]) = pre[it];
+    } else if (v_dc < D / 8) {
+      // slot of these 4 keys inside their 16-key chunk: the order in which
+      // the two wave halves consume keys as the k index of O^T += V^T P^T
+      const int pos = 16 * (v_kgp >> 2) + 8 * (v_kgp & 1) + 4 * ((v_kgp >> 1) & 1);
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const int w = dd >> 1, sh = (dd & 1) * 16;
-          const uint32_t lo = ((pre[0][w] >> sh) & 0xffffu) | (((pre[1][w] >> sh) & 0xffffu) << 16);
-          const uint32_t hi = ((pre[2][w] >> sh) & 0xffffu) | (((pre[3][w] >> sh) & 0xffffu) << 16);
-          *reinterpret_cast<u32x2*>(&vt_lds[buf][(8 * dc + dd) * VROW + pos]) = u32x2{lo, hi};
+      for (int dd = 0; dd < 8; ++dd) {
+        const int w = dd >> 1;
+        uint32_t lo, hi;
+        if (dd & 1) {
+          lo = __builtin_amdgcn_perm(pre[1][w], pre[0][w], 0x07060302u);
+          hi = __builtin_amdgcn_perm(pre[3][w], pre[2][w], 0x07060302u);
+        } else {
+          lo = __builtin_amdgcn_perm(pre[1][w], pre[0][w], 0x05040100u);
+          hi = __builtin_amdgcn_perm(pre[3][w], pre[2][w], 0x05040100u);
         }
+        *reinterpret_cast<u32x2*>(&vt_lds[buf][(8 * v_dc + dd) * VROW + pos]) = u32x2{lo, hi};
       }
     }
   };
@@ -489,8 +509,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     }
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
-    mx = fmaxf(mx, swap_halves(mx));
+    for (int e = 0; e < 16; ++e)
+      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[e], s1[e]));
+    mx = half_max(mx);
     const float mt = mx * p.c;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau)) {
       const float mn = fmaxf(m_run, mt);
@@ -612,7 +633,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   }
 
   // ---------------- finish: normalise, write O and lse
-  const float lt = l_run + swap_halves(l_run);
+  const float lt = half_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (wave_rows && qrow < n) {
     const size_t ro = ((size_t)head * n + qrow) * D;

@@ -45,6 +45,22 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// x of this lane combined with x of lane (l ^ 32), via v_permlane32_swap:
+// after the swap one output holds the lower half's values and the other the
+// upper half's, in every lane
+__device__ __forceinline__ float half_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// word 3 of a raw buffer resource on gfx9-family parts (32-bit data format);
+// accesses at or past num_records return zero
+constexpr int kBufferFlags = 0x00020000;
+
 // per-lane select driven by a wave-uniform 64-bit lane mask
 __device__ __forceinline__ float select_mask(uint64_t m, float a, float b) {
   return __builtin_amdgcn_inverse_ballot_w64(m) ? a : b;
