@@ -345,8 +345,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     return INT_MIN;
   };
 
-  // ---- staging: waves 0-3 stage V^T (transposed, key-permuted), waves 4-7 stage K;
-  //      every lane also fetches the offset-bitmap words its row needs for the tile.
+  // ---- staging: waves 0-3 stage V^T (transposed, key-permuted), waves 4-7 stage K.
   // K and V rows are read through buffer resources that cover exactly this
   // head's n rows: rows at or past n (the tail tile, gathered padding) read
   // as zeros with no branch.
@@ -372,77 +371,73 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   const int k_row0 = (tid - 256) / KCH, k_c8 = (tid - 256) % KCH;
   const int v_kgp = tid & 15, v_dc = tid >> 4;
   u32x4 pre[4];
-  auto load_tile = [&](int code, uint32_t (&bw)[3]) {
-    if (code >= 0) {
-      // offsets qrow - j for the tile's keys: [qrow - j0 - 63, qrow - j0]
-      const int wq = max((qrow - code * kBN - (kBN - 1)) >> 5, -kPrePad);
-      bw[0] = bo[wq];
-      bw[1] = bo[wq + 1];
-      bw[2] = bo[wq + 2];
-    }
-    const int* gk = glist + (code < 0 ? (-1 - code) * kBN : 0);
+  // global -> registers: waves 4-7 fetch K of tile ck, waves 0-3 fetch V of tile cv
+  auto load_kv = [&](int ck, int cv) {
     if (wave >= 4) {
+      if (ck != INT_MIN) {
+        const int* gk = glist + (ck < 0 ? (-1 - ck) * kBN : 0);
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        if (it * KRS < kBN) {
-          const int r = k_row0 + KRS * it;
-          int key = code >= 0 ? code * kBN + r : gk[r];
-          key = key < 0 ? n : key;  // padding: first row past the buffer
-          pre[it] = bload8(rsk, (unsigned)key * ROWB + k_c8 * 8 * ESZ);
+        for (int it = 0; it < 4; ++it) {
+          if (it * KRS < kBN) {
+            const int r = k_row0 + KRS * it;
+            const int key = ck >= 0 ? ck * kBN + r : gk[r];
+            pre[it] = bload8(rsk, (unsigned)key * ROWB + k_c8 * 8 * ESZ);
+          }
         }
       }
-    } else if (v_dc < D / 8) {
+    } else if (cv != INT_MIN && v_dc < D / 8) {
       int4 keys4;
-      if (code >= 0) {
-        const int k0 = code * kBN + 4 * v_kgp;
+      if (cv >= 0) {
+        const int k0 = cv * kBN + 4 * v_kgp;
         keys4 = int4{k0, k0 + 1, k0 + 2, k0 + 3};
       } else {
-        keys4 = *reinterpret_cast<const int4*>(&gk[4 * v_kgp]);
+        keys4 = *reinterpret_cast<const int4*>(&glist[(-1 - cv) * kBN + 4 * v_kgp]);
       }
-      const int kk[4] = {keys4.x, keys4.y, keys4.z, keys4.w};
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = kk[rr] < 0 ? n : kk[rr];
-        pre[rr] = bload8(rsv, (unsigned)key * ROWB + v_dc * 8 * ESZ);
-      }
+      pre[0] = bload8(rsv, (unsigned)keys4.x * ROWB + v_dc * 8 * ESZ);
+      pre[1] = bload8(rsv, (unsigned)keys4.y * ROWB + v_dc * 8 * ESZ);
+      pre[2] = bload8(rsv, (unsigned)keys4.z * ROWB + v_dc * 8 * ESZ);
+      pre[3] = bload8(rsv, (unsigned)keys4.w * ROWB + v_dc * 8 * ESZ);
     }
   };
-  auto store_tile = [&](int buf) {
+  // registers -> LDS: K into k_lds[kb] (when has_k), V^T into vt_lds[vb] (when has_v)
+  auto store_kv = [&](int kb, bool has_k, int vb, bool has_v) {
     if (wave >= 4) {
+      if (has_k) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it)
-        if (it * KRS < kBN)
-          *reinterpret_cast<u32x4*>(&k_lds[buf][(k_row0 + KRS * it) * KROW + 8 * k_c8]) = pre[it];
-    } else if (v_dc < D / 8) {
+        for (int it = 0; it < 4; ++it)
+          if (it * KRS < kBN)
+            *reinterpret_cast<u32x4*>(&k_lds[kb][(k_row0 + KRS * it) * KROW + 8 * k_c8]) = pre[it];
+      }
+    } else if (has_v && v_dc < D / 8) {
       // slot of these 4 keys inside their 16-key chunk: the order in which
       // the two wave halves consume keys as the k index of O^T += V^T P^T
       const int pos = 16 * (v_kgp >> 2) + 8 * (v_kgp & 1) + 4 * ((v_kgp >> 1) & 1);
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
         const int w = dd >> 1;
-        uint32_t lo, hi;
-        if (dd & 1) {
-          lo = __builtin_amdgcn_perm(pre[1][w], pre[0][w], 0x07060302u);
-          hi = __builtin_amdgcn_perm(pre[3][w], pre[2][w], 0x07060302u);
-        } else {
-          lo = __builtin_amdgcn_perm(pre[1][w], pre[0][w], 0x05040100u);
-          hi = __builtin_amdgcn_perm(pre[3][w], pre[2][w], 0x05040100u);
-        }
-        *reinterpret_cast<u32x2*>(&vt_lds[buf][(8 * v_dc + dd) * VROW + pos]) = u32x2{lo, hi};
+        const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(pre[1][w], pre[0][w], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(pre[3][w], pre[2][w], sel);
+        *reinterpret_cast<u32x2*>(&vt_lds[vb][(8 * v_dc + dd) * VROW + pos]) = u32x2{lo, hi};
       }
     }
   };
-
-  // ---- one tile of online-softmax attention for this wave's 32 rows
-  auto attend = [&](int code, int buf, const uint32_t (&bw)[3]) {
-    const uint16_t* kb = k_lds[buf];
-    const uint16_t* vb = vt_lds[buf];
-    // Per lane, a 64-bit word K with bit kk set when key j0 + kk is in S_qrow.
-    // The lane's scores are keys kk = 32*sk + 8*a + 4*half + bb (sk, a, bb
-    // the element coordinates), so Kh = K >> (4*half) puts element (sk, a, bb)
-    // at bit 32*sk + 8*a + bb.
-    uint32_t kh0 = ~0u, kh1 = ~0u;
-    bool masked = true;
+  // offset-bitmap words this lane's row needs for a contiguous tile:
+  // offsets qrow - j for the tile's keys are [qrow - j0 - 63, qrow - j0]
+  auto load_bw = [&](int code, uint32_t (&bw)[3]) {
+    if (code >= 0) {
+      const int wq = max((qrow - code * kBN - (kBN - 1)) >> 5, -kPrePad);
+      bw[0] = bo[wq];
+      bw[1] = bo[wq + 1];
+      bw[2] = bo[wq + 2];
+    }
+  };
+  // Per lane, a 64-bit word K with bit kk set when key kk of the tile is in
+  // S_qrow.  The lane's scores are keys kk = 32*sk + 8*a + 4*half + bb (sk,
+  // a, bb the element coordinates), so Kh = K >> (4*half) puts element
+  // (sk, a, bb) at bit 8*a + bb of word sk.
+  auto key_word = [&](int code, const uint32_t (&bw)[3], uint32_t& kh0, uint32_t& kh1) {
+    uint32_t k0 = 0u, k1 = 0u;
     if (code >= 0) {
       const int j0 = code * kBN;
       const int dq = qrow - j0;  // largest causal key index of this row
@@ -450,110 +445,40 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       const int sh = (dq - (kBN - 1)) & 31;
       const uint32_t l0 = __builtin_amdgcn_alignbit(bw[1], bw[0], sh);
       const uint32_t l1 = __builtin_amdgcn_alignbit(bw[2], bw[1], sh);
-      uint32_t k0 = __builtin_bitreverse32(l1), k1 = __builtin_bitreverse32(l0);
+      k0 = __builtin_bitreverse32(l1);
+      k1 = __builtin_bitreverse32(l0);
       const uint32_t vw0 = ldc(bv, j0 >> 5), vw1 = ldc(bv, (j0 >> 5) + 1);
-      if (vw0 | vw1) {
-        if (j0 + kBN - 1 <= i0w) {
-          k0 |= vw0;
-          k1 |= vw1;
-        } else {
-          // columns are visible only up to key dq
-          const uint32_t c0 = dq >= 31 ? ~0u : (dq < 0 ? 0u : ((2u << dq) - 1u));
-          const uint32_t c1 = dq >= 63 ? ~0u : (dq < 32 ? 0u : ((2u << (dq - 32)) - 1u));
-          k0 |= vw0 & c0;
-          k1 |= vw1 & c1;
-        }
-      }
-      if (!__builtin_amdgcn_ballot_w64((k0 | k1) != 0u)) return;          // nothing to add
-      masked = __builtin_amdgcn_ballot_w64((k0 & k1) != ~0u) != 0ull;   // else every key counts
-      kh0 = __builtin_amdgcn_alignbit(k1, k0, 4 * half);
-      kh1 = k1 >> (4 * half);
-    }
-    f32x16 s0, s1;
+      // columns are visible up to key dq
+      const uint32_t c0 = dq >= 31 ? ~0u : (dq < 0 ? 0u : ((2u << dq) - 1u));
+      const uint32_t c1 = dq >= 63 ? ~0u : (dq < 32 ? 0u : ((2u << (dq - 32)) - 1u));
+      k0 |= vw0 & c0;
+      k1 |= vw1 & c1;
+    } else if (code != INT_MIN) {
+      // gathered keys ascend (padding n sorts last): the visible ones are a prefix
+      const int* keys = &glist[(-1 - code) * kBN];
+      int lo = 0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
+      for (int step = 32; step > 0; step >>= 1)
+        if (keys[lo + step - 1] <= qrow) lo += step;
+      // lo keys are <= qrow (0..63); one more probe decides 64
+      const int cnt = lo + (lo == 63 && keys[63] <= qrow ? 1 : 0);
+      k0 = cnt >= 32 ? ~0u : ((1u << cnt) - 1u);
+      k1 = cnt >= 64 ? ~0u : (cnt <= 32 ? 0u : ((1u << (cnt - 32)) - 1u));
+    }
+    kh0 = __builtin_amdgcn_alignbit(k1, k0, 4 * half);
+    kh1 = k1 >> (4 * half);
+  };
+  // S^T of this wave's rows against the 64 keys in k_lds[kb], k-steps [k_lo, k_hi)
+  auto qk_part = [&](int kb, f32x16& s0, f32x16& s1, int k_lo, int k_hi) {
+    const uint16_t* kp = k_lds[kb];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&kb[ql * KROW + 16 * kk + 8 * half]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&kb[(32 + ql) * KROW + 16 * kk + 8 * half]);
+      if (kk < k_lo || kk >= k_hi) continue;
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&kp[ql * KROW + 16 * kk + 8 * half]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&kp[(32 + ql) * KROW + 16 * kk + 8 * half]);
       s0 = mfma32(a0, qf[kk], s0);
       s1 = mfma32(a1, qf[kk], s1);
     }
-    if (code >= 0) {
-      if (masked) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int b = 8 * (e >> 2) + (e & 3);
-          const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kh0, b, 1);
-          const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kh1, b, 1);
-          s0[e] = __uint_as_float((m0 & __float_as_uint(s0[e])) | (~m0 & 0xff800000u));
-          s1[e] = __uint_as_float((m1 & __float_as_uint(s1[e])) | (~m1 & 0xff800000u));
-        }
-      }
-    } else {
-      const int* keys = &glist[(-1 - code) * kBN];
-#pragma unroll
-      for (int sk = 0; sk < 2; ++sk)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int4 ks = *reinterpret_cast<const int4*>(&keys[32 * sk + 8 * a + 4 * half]);
-          const int kv4[4] = {ks.x, ks.y, ks.z, ks.w};
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const bool ok = (unsigned)kv4[bb] <= (unsigned)qrow;  // padding (-1) fails
-            const int e = 4 * a + bb;
-            if (sk == 0) s0[e] = ok ? s0[e] : -__builtin_inff();
-            else s1[e] = ok ? s1[e] : -__builtin_inff();
-          }
-        }
-    }
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[e], s1[e]));
-    mx = half_max(mx);
-    const float mt = mx * p.c;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau)) {
-      const float mn = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
-      m_run = mn;
-    }
-    const float nm = -m_run;
-    uint32_t pk[16];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pk[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s0[2 * e], p.c, nm)),
-                        __builtin_amdgcn_exp2f(fmaf(s0[2 * e + 1], p.c, nm)));
-      pk[8 + e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s1[2 * e], p.c, nm)),
-                            __builtin_amdgcn_exp2f(fmaf(s1[2 * e + 1], p.c, nm)));
-    }
-    // row sum of the bf16 probabilities the PV product uses
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, l_run, false);
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      const bf16x8 pf = as_bf16x8(u32x4{pk[4 * c4], pk[4 * c4 + 1], pk[4 * c4 + 2], pk[4 * c4 + 3]});
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vb[(32 * dt + ql) * VROW + 16 * c4 + 8 * half]);
-        acc[dt] = mfma32(av, pf, acc[dt]);
-      }
-    }
-  };
-
-  // does this wave have rows that can see keys of the tile?
-  auto wave_sees = [&](int code) -> bool {
-    if (!wave_rows) return false;
-    if (code >= 0) return code * kBN <= i0w + 31;
-    return glist[(-1 - code) * kBN] <= i0w + 31;  // gathered keys ascend
   };
 
   // ---- rounds: each gathers up to kListCap uncovered columns; the first
@@ -599,35 +524,119 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       cursor += kThreads;
       __syncthreads();
     }
-    // pad the last gathered chunk
-    for (int r = fill + tid; r < ((fill + kBN - 1) / kBN) * kBN; r += kThreads) glist[r] = -1;
+    // pad the last gathered chunk with n: sorts after every key, reads as zeros
+    for (int r = fill + tid; r < ((fill + kBN - 1) / kBN) * kBN; r += kThreads) glist[r] = n;
     seq.chunk = 0;
     seq.nchunks = (fill + kBN - 1) / kBN;
     if (!first_round) seq.dense = false;
     first_round = false;
     __syncthreads();
 
-    // software pipeline: prefetch tile t+1 into registers while tile t computes
+    // Software pipeline over the round's tiles.  In step t the matrix cores
+    // compute S(t+1) = K(t+1) Q^T while the vector units run the softmax of
+    // tile t, then O += V(t) P(t).  K is staged two tiles ahead and V one,
+    // so two LDS buffers of each suffice with one barrier per step.
     int cur = next_tile();
     if (cur == INT_MIN) continue;
-    uint32_t bwc[3] = {0u, 0u, 0u}, bwn[3] = {0u, 0u, 0u};
-    load_tile(cur, bwc);
-    store_tile(0);
-    __syncthreads();
-    int buf = 0;
-    while (true) {
-      const int nxt = next_tile();
-      if (nxt != INT_MIN) load_tile(nxt, bwn);
-      if (cur >= 0) ++n_dense;
-      else ++n_gath;
-      if (wave_sees(cur)) attend(cur, buf, bwc);
-      if (nxt == INT_MIN) break;
-      store_tile(buf ^ 1);
+    int nxt = next_tile();
+    uint32_t bw_n[3] = {0u, 0u, 0u}, bw_nn[3] = {0u, 0u, 0u};
+    {
+      uint32_t bw_c[3] = {0u, 0u, 0u};
+      load_bw(cur, bw_c);
+      load_bw(nxt, bw_n);
+      load_kv(cur, cur);
+      store_kv(0, true, 0, true);
+      if (nxt != INT_MIN) {
+        load_kv(nxt, INT_MIN);
+        store_kv(1, true, 0, false);
+      }
       __syncthreads();
-      cur = nxt;
-      buf ^= 1;
+      uint32_t kc0, kc1;
+      key_word(cur, bw_c, kc0, kc1);
+      f32x16 c0, c1;
 #pragma unroll
-      for (int w = 0; w < 3; ++w) bwc[w] = bwn[w];
+      for (int e = 0; e < 16; ++e) c0[e] = c1[e] = 0.f;
+      qk_part(0, c0, c1, 0, KS);
+      int t = 0;
+      while (true) {
+        const int nn = nxt != INT_MIN ? next_tile() : INT_MIN;
+        load_kv(nn, nxt);
+        load_bw(nn, bw_nn);
+        uint32_t kn0, kn1;
+        key_word(nxt, bw_n, kn0, kn1);
+        if (cur >= 0) ++n_dense;
+        else ++n_gath;
+        const int kbn = (t + 1) & 1, vbc = t & 1;
+        f32x16 sn0, sn1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sn0[e] = sn1[e] = 0.f;
+
+        // -- softmax of tile t, with the first half of S(t+1) in flight
+        qk_part(kbn, sn0, sn1, 0, KS / 2);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int b = 8 * (e >> 2) + (e & 3);
+          const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, b, 1);
+          const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, b, 1);
+          c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
+          c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
+        }
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(c0[e], c1[e]));
+        mx = half_max(mx);
+        const float mt = mx * p.c;
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau)) {
+          const float mnew = fmaxf(m_run, mt);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+          m_run = mnew;
+        }
+        qk_part(kbn, sn0, sn1, KS / 2, KS);
+        const float nm = -m_run;
+        uint32_t pk[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pk[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c0[2 * e], p.c, nm)),
+                            __builtin_amdgcn_exp2f(fmaf(c0[2 * e + 1], p.c, nm)));
+          pk[8 + e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c1[2 * e], p.c, nm)),
+                                __builtin_amdgcn_exp2f(fmaf(c1[2 * e + 1], p.c, nm)));
+        }
+        // row sum of the bf16 probabilities the PV product uses
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, l_run, false);
+        // -- O^T += V^T(t) P^T(t)
+        const uint16_t* vp = vt_lds[vbc];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const bf16x8 pf = as_bf16x8(u32x4{pk[4 * c4], pk[4 * c4 + 1], pk[4 * c4 + 2], pk[4 * c4 + 3]});
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vp[(32 * dt + ql) * VROW + 16 * c4 + 8 * half]);
+            acc[dt] = mfma32(av, pf, acc[dt]);
+          }
+        }
+        if (nxt == INT_MIN) break;
+        store_kv(t & 1, nn != INT_MIN, (t + 1) & 1, true);
+        __syncthreads();
+        c0 = sn0;
+        c1 = sn1;
+        kc0 = kn0;
+        kc1 = kn1;
+#pragma unroll
+        for (int w = 0; w < 3; ++w) bw_n[w] = bw_nn[w];
+        cur = nxt;
+        nxt = nn;
+        ++t;
+      }
     }
     __syncthreads();
   }
