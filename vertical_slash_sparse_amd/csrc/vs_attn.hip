@@ -234,17 +234,32 @@ struct TileSeq {
   bool dense;
 };
 
+// XOR swizzle of the 16-byte chunks of LDS row r, chosen so that both the
+// MFMA operand reads of K (16 consecutive rows, one chunk) and the transposing
+// reads of V (4 consecutive rows, two adjacent chunks) hit distinct banks
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+
 template <int D, bool F32>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
-  constexpr int KS = D / 16;     // k-steps of Q K^T
-  constexpr int DT = D / 32;     // 32-row tiles of O^T
-  constexpr int KROW = D + 8;    // padded LDS row of K (bf16 elements)
-  constexpr int VROW = kBN + 8;  // padded LDS row of V^T
-  constexpr int KCH = D / 8;     // 16-byte chunks per K row
-  __shared__ __align__(16) uint16_t k_lds[2][kBN * KROW];
-  __shared__ __align__(16) uint16_t vt_lds[2][D * VROW];
+  constexpr int KS = D / 16;            // k-steps of Q K^T
+  constexpr int DT = D / 32;            // 32-row tiles of O^T
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int ROWB = D * 2;           // bytes per bf16 row
+  constexpr int TILEB = kBN * ROWB;     // bytes per K (or V) tile
+  constexpr int NST = 4;                // pipeline stages
+  constexpr int RPD = 1024 / ROWB;      // rows per 1 KiB DMA (one wave, 16 B per lane)
+  constexpr int NDMA = kBN / kWaves / RPD;  // DMAs per wave per matrix per tile
+  static_assert(NDMA >= 1 && NDMA * RPD * kWaves == kBN, "tile split");
+  // K stages at [0, NST*TILEB), V stages at [NST*TILEB, 2*NST*TILEB)
+  __shared__ __align__(16) uint8_t kv_lds[2 * NST * TILEB];
   __shared__ __align__(16) int glist[kListCap];
   __shared__ int wcnt[kWaves + 1];
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  lds_u8* const kv_base = (lds_u8*)kv_lds;
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, ql = lane & 31;
   const int wave = wave_uniform(tid >> 6);  // keep everything derived from it in SGPRs
@@ -345,106 +360,90 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     return INT_MIN;
   };
 
-  // ---- staging: waves 0-3 stage V^T (transposed, key-permuted), waves 4-7 stage K.
-  // K and V rows are read through buffer resources that cover exactly this
-  // head's n rows: rows at or past n (the tail tile, gathered padding) read
-  // as zeros with no branch.
-  constexpr int ESZ = F32 ? 4 : 2;
-  constexpr int ROWB = D * ESZ;  // bytes per K/V row
+  // ---- staging.  K and V tiles live row-major in LDS (bf16, chunk-swizzled)
+  // and are filled by LDS-DMA buffer loads: each wave moves NDMA KiB of K and
+  // of V per tile, lane l writing 16 bytes at the wave's base + 16 l.  The
+  // buffer resources cover exactly this head's n rows, so rows at or past n
+  // (the tail tile, gathered padding n, absent tiles) arrive as zeros.
+  constexpr int GROWB = D * (F32 ? 4 : 2);  // bytes per row in HBM
   const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(static_cast<const char*>(p.k) + kv_head * ROWB), (short)0, n * ROWB, kBufferFlags);
+      (void*)(static_cast<const char*>(p.k) + kv_head * GROWB), (short)0, n * GROWB, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(static_cast<const char*>(p.v) + kv_head * ROWB), (short)0, n * ROWB, kBufferFlags);
-  auto bload8 = [&](const __amdgpu_buffer_rsrc_t& rs, unsigned off) -> u32x4 {
-    if constexpr (F32) {
-      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
-      const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 16), 0, 0);
-      return u32x4{pack_bf16(__uint_as_float(a[0]), __uint_as_float(a[1])),
-                   pack_bf16(__uint_as_float(a[2]), __uint_as_float(a[3])),
-                   pack_bf16(__uint_as_float(c[0]), __uint_as_float(c[1])),
-                   pack_bf16(__uint_as_float(c[2]), __uint_as_float(c[3]))};
-    } else {
-      return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
-    }
-  };
-  constexpr int KRS = kThreads / 2 / KCH;  // K rows staged per pass of 256 threads
-  const int k_row0 = (tid - 256) / KCH, k_c8 = (tid - 256) % KCH;
-  const int v_kgp = tid & 15, v_dc = tid >> 4;
-  u32x4 pre[4];
-  // global -> registers: waves 4-7 fetch K of tile ck, waves 0-3 fetch V of tile cv
-  auto load_kv = [&](int ck, int cv) {
-    if (wave >= 4) {
-      if (ck != INT_MIN) {
-        const int* gk = glist + (ck < 0 ? (-1 - ck) * kBN : 0);
+      (void*)(static_cast<const char*>(p.v) + kv_head * GROWB), (short)0, n * GROWB, kBufferFlags);
+  const u32x4 wk = buffer_words(static_cast<const char*>(p.k) + kv_head * GROWB, (uint32_t)(n * GROWB));
+  const u32x4 wv = buffer_words(static_cast<const char*>(p.v) + kv_head * GROWB, (uint32_t)(n * GROWB));
+  int dma_row[NDMA], dma_chunk[NDMA];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          if (it * KRS < kBN) {
-            const int r = k_row0 + KRS * it;
-            const int key = ck >= 0 ? ck * kBN + r : gk[r];
-            pre[it] = bload8(rsk, (unsigned)key * ROWB + k_c8 * 8 * ESZ);
-          }
-        }
-      }
-    } else if (cv != INT_MIN && v_dc < D / 8) {
-      int4 keys4;
-      if (cv >= 0) {
-        const int k0 = cv * kBN + 4 * v_kgp;
-        keys4 = int4{k0, k0 + 1, k0 + 2, k0 + 3};
+  for (int i = 0; i < NDMA; ++i) {
+    const int r = wave * (kBN / kWaves) + i * RPD + lane / CH;
+    dma_row[i] = r;
+    dma_chunk[i] = (lane % CH) ^ swz<D>(r);  // the source chunk this lane's LDS slot holds
+  }
+  // fetch tile `code` into the stage at kdst / vdst (code INT_MIN: an absent
+  // tile, all zeros)
+  // The wait-count pass treats the DMA's address register as still in use
+  // until the load lands, so letting the register allocator hand it to the
+  // next LDS read costs a vmcnt(0) in the middle of the step.  Holding the
+  // offsets live to the end of the step avoids that.
+  unsigned dma_off[NDMA];
+  auto stage_into = [&](int code, lds_u8* __restrict__ kdst, lds_u8* __restrict__ vdst) {
+    const int* gk = glist + (code < 0 && code != INT_MIN ? (-1 - code) * kBN : 0);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int r = dma_row[i];
+      const int gkey = gk[r];  // read unconditionally so no branch splits the step
+      const int key = code >= 0 ? code * kBN + r : (code == INT_MIN ? n : gkey);
+      const int kbase = (wave * (kBN / kWaves) + i * RPD) * ROWB;
+      if constexpr (F32) {
+        const unsigned off = (unsigned)key * GROWB + dma_chunk[i] * 32;
+        const u32x4 k0 = __builtin_amdgcn_raw_buffer_load_b128(rsk, (int)off, 0, 0);
+        const u32x4 k1 = __builtin_amdgcn_raw_buffer_load_b128(rsk, (int)(off + 16), 0, 0);
+        const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rsv, (int)off, 0, 0);
+        const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rsv, (int)(off + 16), 0, 0);
+        auto cvt = [](const u32x4& a, const u32x4& c) {
+          return u32x4{pack_bf16(__uint_as_float(a[0]), __uint_as_float(a[1])),
+                       pack_bf16(__uint_as_float(a[2]), __uint_as_float(a[3])),
+                       pack_bf16(__uint_as_float(c[0]), __uint_as_float(c[1])),
+                       pack_bf16(__uint_as_float(c[2]), __uint_as_float(c[3]))};
+        };
+        *(__attribute__((address_space(3))) u32x4*)(kdst + kbase + 16 * lane) = cvt(k0, k1);
+        *(__attribute__((address_space(3))) u32x4*)(vdst + kbase + 16 * lane) = cvt(v0, v1);
       } else {
-        keys4 = *reinterpret_cast<const int4*>(&glist[(-1 - cv) * kBN + 4 * v_kgp]);
-      }
-      pre[0] = bload8(rsv, (unsigned)keys4.x * ROWB + v_dc * 8 * ESZ);
-      pre[1] = bload8(rsv, (unsigned)keys4.y * ROWB + v_dc * 8 * ESZ);
-      pre[2] = bload8(rsv, (unsigned)keys4.z * ROWB + v_dc * 8 * ESZ);
-      pre[3] = bload8(rsv, (unsigned)keys4.w * ROWB + v_dc * 8 * ESZ);
-    }
-  };
-  // registers -> LDS: K into k_lds[kb] (when has_k), V^T into vt_lds[vb] (when has_v)
-  auto store_kv = [&](int kb, bool has_k, int vb, bool has_v) {
-    if (wave >= 4) {
-      if (has_k) {
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-          if (it * KRS < kBN)
-            *reinterpret_cast<u32x4*>(&k_lds[kb][(k_row0 + KRS * it) * KROW + 8 * k_c8]) = pre[it];
-      }
-    } else if (has_v && v_dc < D / 8) {
-      // slot of these 4 keys inside their 16-key chunk: the order in which
-      // the two wave halves consume keys as the k index of O^T += V^T P^T
-      const int pos = 16 * (v_kgp >> 2) + 8 * (v_kgp & 1) + 4 * ((v_kgp >> 1) & 1);
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int w = dd >> 1;
-        const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(pre[1][w], pre[0][w], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(pre[3][w], pre[2][w], sel);
-        *reinterpret_cast<u32x2*>(&vt_lds[vb][(8 * v_dc + dd) * VROW + pos]) = u32x2{lo, hi};
+        const unsigned off = (unsigned)key * GROWB + dma_chunk[i] * 16;
+        dma16(wk, (uint32_t)(uintptr_t)(kdst + kbase), off);
+        dma16(wv, (uint32_t)(uintptr_t)(vdst + kbase), off);
+        dma_off[i] = off;
       }
     }
   };
-  // offset-bitmap words this lane's row needs for a contiguous tile:
-  // offsets qrow - j for the tile's keys are [qrow - j0 - 63, qrow - j0]
-  auto load_bw = [&](int code, uint32_t (&bw)[3]) {
-    if (code >= 0) {
-      const int wq = max((qrow - code * kBN - (kBN - 1)) >> 5, -kPrePad);
-      bw[0] = bo[wq];
-      bw[1] = bo[wq + 1];
-      bw[2] = bo[wq + 2];
-    }
+  lds_u8* const k_region = kv_base;
+  lds_u8* const v_region = kv_base + NST * TILEB;
+  auto stage_tile = [&](int code, int st) { stage_into(code, k_region + st * TILEB, v_region + st * TILEB); };
+  // Offset-bitmap words for a contiguous tile.  The wave's rows need offsets
+  // [i0w - j0 - 63, i0w - j0 + 31], which lie in four consecutive words; they
+  // come through the scalar cache and each lane picks its three.
+  auto load_sw = [&](int code, uint32_t (&sw)[4]) {
+    const int wq = code >= 0 ? (i0w - code * kBN - (kBN - 1)) >> 5 : 0;
+    const int wc = max(wq, -kPrePad);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sw[k] = ldc(bo, wc + k);
   };
   // Per lane, a 64-bit word K with bit kk set when key kk of the tile is in
   // S_qrow.  The lane's scores are keys kk = 32*sk + 8*a + 4*half + bb (sk,
   // a, bb the element coordinates), so Kh = K >> (4*half) puts element
   // (sk, a, bb) at bit 8*a + bb of word sk.
-  auto key_word = [&](int code, const uint32_t (&bw)[3], uint32_t& kh0, uint32_t& kh1) {
+  auto key_word = [&](int code, const uint32_t (&sw)[4], uint32_t& kh0, uint32_t& kh1) {
     uint32_t k0 = 0u, k1 = 0u;
     if (code >= 0) {
       const int j0 = code * kBN;
       const int dq = qrow - j0;  // largest causal key index of this row
       // bits of the offset bitmap from offset dq - 63 upward: bit x <-> key 63 - x
+      const int base = i0w - j0 - (kBN - 1);
+      const bool up = ((base & 31) + ql) >= 32;  // this lane's window starts one word on
+      const uint32_t b0 = up ? sw[1] : sw[0], b1 = up ? sw[2] : sw[1], b2 = up ? sw[3] : sw[2];
       const int sh = (dq - (kBN - 1)) & 31;
-      const uint32_t l0 = __builtin_amdgcn_alignbit(bw[1], bw[0], sh);
-      const uint32_t l1 = __builtin_amdgcn_alignbit(bw[2], bw[1], sh);
+      const uint32_t l0 = __builtin_amdgcn_alignbit(b1, b0, sh);
+      const uint32_t l1 = __builtin_amdgcn_alignbit(b2, b1, sh);
       k0 = __builtin_bitreverse32(l1);
       k1 = __builtin_bitreverse32(l0);
       const uint32_t vw0 = ldc(bv, j0 >> 5), vw1 = ldc(bv, (j0 >> 5) + 1);
@@ -460,7 +459,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int step = 32; step > 0; step >>= 1)
         if (keys[lo + step - 1] <= qrow) lo += step;
-      // lo keys are <= qrow (0..63); one more probe decides 64
       const int cnt = lo + (lo == 63 && keys[63] <= qrow ? 1 : 0);
       k0 = cnt >= 32 ? ~0u : ((1u << cnt) - 1u);
       k1 = cnt >= 64 ? ~0u : (cnt <= 32 ? 0u : ((1u << (cnt - 32)) - 1u));
@@ -468,18 +466,58 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     kh0 = __builtin_amdgcn_alignbit(k1, k0, 4 * half);
     kh1 = k1 >> (4 * half);
   };
-  // S^T of this wave's rows against the 64 keys in k_lds[kb], k-steps [k_lo, k_hi)
-  auto qk_part = [&](int kb, f32x16& s0, f32x16& s1, int k_lo, int k_hi) {
-    const uint16_t* kp = k_lds[kb];
+
+  // per-lane LDS byte offsets of the MFMA operand reads, for stage 0
+  int koff[KS];  // K rows ql (+32 via the immediate), chunk 2*kk + half
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) koff[kk] = ql * ROWB + 16 * ((2 * kk + half) ^ swz<D>(ql));
+  // V^T through ds_read_b64_tr_b16: in each 16-lane group, source lane
+  // j = 4r + pp reads 4 values of row r at columns 4*pp.., and output lane
+  // i = 4pp' + q receives column i of rows 0..3.  Group G16 = 2*h + dgrp
+  // covers head dims 32*dt + 16*dgrp .. +15 and keys 4h..4h+3 (part 0) or
+  // 8+4h.. (part 1) of each 16-key chunk: the slots the P^T operand uses.
+  int voff[2][DT];
+  {
+    const int g16 = lane >> 4, j = lane & 15, rr = j >> 2, pp = j & 3, hh = g16 >> 1, dgrp = g16 & 1;
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int row = 8 * part + 4 * hh + rr;
+        const int chunk = 4 * dt + 2 * dgrp + (pp >> 1);
+        voff[part][dt] = row * ROWB + 16 * (chunk ^ swz<D>(row)) + 8 * (pp & 1);
+      }
+  }
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+  auto qk_part = [&](const lds_u8* kr, f32x16& s0, f32x16& s1, int k_lo, int k_hi) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       if (kk < k_lo || kk >= k_hi) continue;
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&kp[ql * KROW + 16 * kk + 8 * half]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&kp[(32 + ql) * KROW + 16 * kk + 8 * half]);
+      const bf16x8 a0 = *(const lds_bf16x8*)(kr + koff[kk]);
+      const bf16x8 a1 = *(const lds_bf16x8*)(kr + koff[kk] + 32 * ROWB);
       s0 = mfma32(a0, qf[kk], s0);
       s1 = mfma32(a1, qf[kk], s1);
     }
   };
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  auto read_vt = [&](const lds_u8* vr, int part, int dt, int c4) -> v4i16 {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(vr + voff[part][dt] + c4 * 16 * ROWB));
+  };
+  // move the operand offsets one stage on (stage s -> s+1 mod NST)
+  auto advance = [&](int (&o)[KS], int from) {
+    const int delta = from == NST - 1 ? -(NST - 1) * TILEB : TILEB;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) o[kk] += delta;
+  };
+  auto advance_v = [&](int from) {
+    const int delta = from == NST - 1 ? -(NST - 1) * TILEB : TILEB;
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) voff[part][dt] += delta;
+  };
+  constexpr int kWaitAfter = 2 * NDMA;  // DMAs issued per step after the awaited tile
 
   // ---- rounds: each gathers up to kListCap uncovered columns; the first
   //      round also walks the contiguous tiles
@@ -532,113 +570,143 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     first_round = false;
     __syncthreads();
 
-    // Software pipeline over the round's tiles.  In step t the matrix cores
-    // compute S(t+1) = K(t+1) Q^T while the vector units run the softmax of
-    // tile t, then O += V(t) P(t).  K is staged two tiles ahead and V one,
-    // so two LDS buffers of each suffice with one barrier per step.
+    // Software pipeline over the round's tiles, NST stages deep.  Tile t lives
+    // in stage t % NST.  Step t: start the DMA of tile t+3, compute S(t+1) =
+    // K(t+1) Q^T on the matrix cores alongside the softmax of tile t, add
+    // V(t) P(t), then wait for this wave's share of tile t+2 and meet at the
+    // barrier, after which tile t+2 is complete and stage (t-1) % NST is free.
     int cur = next_tile();
     if (cur == INT_MIN) continue;
     int nxt = next_tile();
-    uint32_t bw_n[3] = {0u, 0u, 0u}, bw_nn[3] = {0u, 0u, 0u};
+    int n2 = nxt != INT_MIN ? next_tile() : INT_MIN;
+    uint32_t sw_n[4], sw_nn[4];
+    uint32_t kc0, kc1;
+    f32x16 c0, c1;
     {
-      uint32_t bw_c[3] = {0u, 0u, 0u};
-      load_bw(cur, bw_c);
-      load_bw(nxt, bw_n);
-      load_kv(cur, cur);
-      store_kv(0, true, 0, true);
-      if (nxt != INT_MIN) {
-        load_kv(nxt, INT_MIN);
-        store_kv(1, true, 0, false);
-      }
+      uint32_t sw_c[4];
+      load_sw(cur, sw_c);
+      load_sw(nxt, sw_n);
+      stage_tile(cur, 0);
+      stage_tile(nxt, 1);
+      stage_tile(n2, 2);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
-      uint32_t kc0, kc1;
-      key_word(cur, bw_c, kc0, kc1);
-      f32x16 c0, c1;
+      key_word(cur, sw_c, kc0, kc1);
 #pragma unroll
       for (int e = 0; e < 16; ++e) c0[e] = c1[e] = 0.f;
-      qk_part(0, c0, c1, 0, KS);
-      int t = 0;
-      while (true) {
-        const int nn = nxt != INT_MIN ? next_tile() : INT_MIN;
-        load_kv(nn, nxt);
-        load_bw(nn, bw_nn);
-        uint32_t kn0, kn1;
-        key_word(nxt, bw_n, kn0, kn1);
-        if (cur >= 0) ++n_dense;
-        else ++n_gath;
-        const int kbn = (t + 1) & 1, vbc = t & 1;
-        f32x16 sn0, sn1;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sn0[e] = sn1[e] = 0.f;
-
-        // -- softmax of tile t, with the first half of S(t+1) in flight
-        qk_part(kbn, sn0, sn1, 0, KS / 2);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int b = 8 * (e >> 2) + (e & 3);
-          const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, b, 1);
-          const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, b, 1);
-          c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
-          c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
-        }
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(c0[e], c1[e]));
-        mx = half_max(mx);
-        const float mt = mx * p.c;
-        if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau)) {
-          const float mnew = fmaxf(m_run, mt);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-          l_run *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
-          m_run = mnew;
-        }
-        qk_part(kbn, sn0, sn1, KS / 2, KS);
-        const float nm = -m_run;
-        uint32_t pk[16];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pk[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c0[2 * e], p.c, nm)),
-                            __builtin_amdgcn_exp2f(fmaf(c0[2 * e + 1], p.c, nm)));
-          pk[8 + e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c1[2 * e], p.c, nm)),
-                                __builtin_amdgcn_exp2f(fmaf(c1[2 * e + 1], p.c, nm)));
-        }
-        // row sum of the bf16 probabilities the PV product uses
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, l_run, false);
-        // -- O^T += V^T(t) P^T(t)
-        const uint16_t* vp = vt_lds[vbc];
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          const bf16x8 pf = as_bf16x8(u32x4{pk[4 * c4], pk[4 * c4 + 1], pk[4 * c4 + 2], pk[4 * c4 + 3]});
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vp[(32 * dt + ql) * VROW + 16 * c4 + 8 * half]);
-            acc[dt] = mfma32(av, pf, acc[dt]);
-          }
-        }
-        if (nxt == INT_MIN) break;
-        store_kv(t & 1, nn != INT_MIN, (t + 1) & 1, true);
-        __syncthreads();
-        c0 = sn0;
-        c1 = sn1;
-        kc0 = kn0;
-        kc1 = kn1;
-#pragma unroll
-        for (int w = 0; w < 3; ++w) bw_n[w] = bw_nn[w];
-        cur = nxt;
-        nxt = nn;
-        ++t;
-      }
+      qk_part(k_region, c0, c1, 0, KS);  // stage 0
     }
+    advance(koff, 0);  // K operand reads now point at stage 1
+    int t = 0;
+    // One step.  The four LDS pointers never overlap in what they touch (K
+    // and V of the stages being read, the stage being filled), which lets the
+    // compiler keep the DMA in flight across the operand reads.
+    auto step = [&](const lds_u8* __restrict__ krd, const lds_u8* __restrict__ vrd,
+                    lds_u8* __restrict__ kdma, lds_u8* __restrict__ vdma, int n3) {
+      // -- branchy part: key word of tile t+1, mask and row max of tile t, the
+      //    rare rescale.  No K/V reads or DMA happen here.
+      load_sw(n2, sw_nn);
+      uint32_t kn0, kn1;
+      key_word(nxt, sw_n, kn0, kn1);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int bpos = 8 * (e >> 2) + (e & 3);
+        const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, bpos, 1);
+        const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, bpos, 1);
+        c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
+        c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
+      }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(c0[e], c1[e]));
+      mx = half_max(mx);
+      const float mt = mx * p.c;
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau)) {
+        const float mnew = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+        m_run = mnew;
+      }
+      // -- straight-line part: start the DMA of tile t+3, then S(t+1) on the
+      //    matrix cores alongside exp/convert of tile t, then O += V(t) P(t)
+      stage_into(n3, kdma, vdma);
+      f32x16 sn0, sn1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sn0[e] = sn1[e] = 0.f;
+      qk_part(krd, sn0, sn1, 0, KS);
+      const float nm = -m_run;
+      uint32_t pk[16];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pk[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c0[2 * e], p.c, nm)),
+                          __builtin_amdgcn_exp2f(fmaf(c0[2 * e + 1], p.c, nm)));
+        pk[8 + e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c1[2 * e], p.c, nm)),
+                              __builtin_amdgcn_exp2f(fmaf(c1[2 * e + 1], p.c, nm)));
+      }
+      // row sum of the bf16 probabilities the PV product uses
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, l_run, false);
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const bf16x8 pf = as_bf16x8(u32x4{pk[4 * c4], pk[4 * c4 + 1], pk[4 * c4 + 2], pk[4 * c4 + 3]});
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const v4i16 lo4 = read_vt(vrd, 0, dt, c4), hi4 = read_vt(vrd, 1, dt, c4);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[dt] = mfma32(av, pf, acc[dt]);
+        }
+      }
+      if constexpr (!F32) {
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) asm volatile("" ::"v"(dma_off[i]));
+      }
+      c0 = sn0;
+      c1 = sn1;
+      kc0 = kn0;
+      kc1 = kn1;
+    };
+    while (true) {
+      const int n3 = n2 != INT_MIN ? next_tile() : INT_MIN;
+      if (cur >= 0) ++n_dense;
+      else ++n_gath;
+      const int sdma = (t + 3) % NST;
+      step(k_region, v_region, k_region + sdma * TILEB, v_region + sdma * TILEB, n3);
+      if (nxt == INT_MIN) break;
+      // this wave's share of tile t+2 has landed once at most the loads of
+      // this step are outstanding; the barrier then completes tile t+2 for all
+      if constexpr (F32) __builtin_amdgcn_s_waitcnt(0x0F70);
+      else __builtin_amdgcn_s_waitcnt(0x0F70 | kWaitAfter);
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < 4; ++w) sw_n[w] = sw_nn[w];
+      advance(koff, (t + 1) % NST);
+      advance_v(t % NST);
+      cur = nxt;
+      nxt = n2;
+      n2 = n3;
+      ++t;
+    }
+    // drain: every outstanding DMA lands before the next round reuses stages
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
+    // rewind the operand offsets to stage 0
+    {
+      const int kst = (t + 1) % NST, vst = t % NST;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) koff[kk] -= kst * TILEB;
+#pragma unroll
+      for (int part = 0; part < 2; ++part)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) voff[part][dt] -= vst * TILEB;
+    }
   }
 
   // ---------------- finish: normalise, write O and lse

@@ -61,6 +61,24 @@ __device__ __forceinline__ float half_sum(float x) {
 // accesses at or past num_records return zero
 constexpr int kBufferFlags = 0x00020000;
 
+// raw buffer resource words: base, stride 0, num_records bytes
+__device__ __forceinline__ u32x4 buffer_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kBufferFlags};
+}
+
+// LDS-DMA: every lane moves 16 bytes from the buffer at byte offset voff into
+// LDS at lds_addr + 16 * lane.  The instruction has no register results, so
+// nothing the compiler allocates depends on it; completion is tracked by the
+// caller with an explicit s_waitcnt vmcnt.  Offsets at or past num_records
+// deliver zeros.
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // per-lane select driven by a wave-uniform 64-bit lane mask
 __device__ __forceinline__ float select_mask(uint64_t m, float a, float b) {
   return __builtin_amdgcn_inverse_ballot_w64(m) ? a : b;
