@@ -95,6 +95,43 @@ def cpu_baseline(q, k, v, lists, group, d, n, budget_s=15.0, seed=5):
     }
 
 
+def copy_calibration(args, torch):
+    """Reads and writes exactly copy-calib-mib MiB per launch (torch's neg kernel)."""
+    if args.copy_calib_mib <= 0:
+        return
+    src = torch.ones(args.copy_calib_mib * (1 << 18), dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def source_digest(files):
+    """sha256 over kernel sources: a recorded counter reading is reported only
+    while the kernel it was taken on is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "vertical_slash_sparse_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# HBM bytes per launch read from the FETCH_SIZE / WRITE_SIZE counters (each
+# scaled by the same counter's reading for a copy of known size), keyed by the
+# workload and the digest of the kernel sources they were taken on.
+ATTN_SOURCES = ("vs_attn.hip", "vs_common.h", "vs_internal.h")
+INDEX_SOURCES = ("vs_index.hip", "vs_common.h", "vs_internal.h")
+MEASURED_TRAFFIC = {}
+
+
+def recorded_traffic(workload, sources):
+    rec = MEASURED_TRAFFIC.get(workload)
+    if rec is None or rec["digest"] != source_digest(sources):
+        return None
+    return rec["bytes"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +141,10 @@ def main():
                     choices=["zipf128k", "fixed32k", "indexer128k", "e2e256k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after the timed steps, run a plain fp32 copy-like kernel (out = -in) over "
+                         "this many MiB three times, so that hardware byte counters of the same run "
+                         "can be scaled against a known transfer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -223,9 +264,12 @@ def main():
         "flops_tile": f_tile,
         "roofline": {"bound": "mfma", "kernel": "attn_kernel (vs_sparse_attn_prefill)",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 5), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
+                     "traffic": recorded_traffic(args.workload, ATTN_SOURCES),
+                     "src_digest": source_digest(ATTN_SOURCES)},
         "wall_s": round(wall, 3),
     }
+    copy_calibration(args, torch)
     if not args.no_cpu_baseline:
         lists_np_full = lists_np
         print("[bench] timing the oracle on a host sample", file=sys.stderr, flush=True)
@@ -274,8 +318,10 @@ def bench_indexer(args, w, torch, vsa, workloads):
         "budgets": {"vertical": vc.cpu().tolist(), "slash": sc.cpu().tolist()},
         "roofline": {"bound": "hbm", "kernel": "index_kernel (vs_index)", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": None},
+                     "traffic": recorded_traffic("indexer128k", INDEX_SOURCES),
+                     "src_digest": source_digest(INDEX_SOURCES)},
     }
+    copy_calibration(args, torch)
     print(json.dumps(res), flush=True)
 
 

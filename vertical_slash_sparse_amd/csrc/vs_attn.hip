@@ -34,6 +34,8 @@
 #include <algorithm>
 #include <climits>
 
+#include <type_traits>
+
 #include "vs_common.h"
 #include "vs_internal.h"
 
@@ -223,17 +225,6 @@ __device__ __forceinline__ T ldc(const T* ptr, long idx) {
   return ((const __attribute__((address_space(4))) T*)ptr)[idx];
 }
 
-// Tile sequence of one workgroup: contiguous key tiles (code >= 0, the tile
-// index) reached by the slash clusters in ascending key order, then tiles of
-// gathered columns (code = -1 - chunk).  All state is wave-uniform.
-struct TileSeq {
-  const int32_t* clo;
-  const int32_t* chi;
-  int c, t, thi, next_t, i0, i1;
-  int chunk, nchunks;
-  bool dense;
-};
-
 // XOR swizzle of the 16-byte chunks of LDS row r, chosen so that both the
 // MFMA operand reads of K (16 consecutive rows, one chunk) and the transposing
 // reads of V (4 consecutive rows, two adjacent chunks) hit distinct banks
@@ -315,162 +306,122 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   float m_run = kNoMax, l_run = 0.f;
   int n_dense = 0, n_gath = 0;
 
-  // ---- tile sequence
-  TileSeq seq;
-  {
-    seq.clo = p.clLo + (size_t)g * p.cap_s;
-    seq.chi = p.clHi + (size_t)g * p.cap_s;
-    const int ncl = ldc(p.counts, 4 * g + 2);
-    int lo = 0, hi = ncl;  // first cluster whose smallest offset exceeds i1
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (ldc(seq.clo, mid) <= i1) lo = mid + 1;
-      else hi = mid;
-    }
-    seq.c = lo - 1;
-    seq.t = 1;
-    seq.thi = 0;
-    seq.next_t = 0;
-    seq.i0 = i0;
-    seq.i1 = i1;
-    seq.chunk = 0;
-    seq.nchunks = 0;
-    seq.dense = true;
-  }
-  // next tile code, or INT_MIN when the sequence is exhausted
-  auto next_tile = [&]() -> int {
-    if (seq.dense) {
-      while (true) {
-        if (seq.t <= seq.thi) {
-          const int t = seq.t++;
-          if (partial && !tile_active(t)) continue;
-          return t;
-        }
-        if (seq.c < 0) break;
-        const int olo = ldc(seq.clo, seq.c), ohi = ldc(seq.chi, seq.c);
-        --seq.c;
-        const int klo = max(0, i0 - ohi), khi = i1 - olo;
-        seq.t = max(klo / kBN, seq.next_t);
-        seq.thi = khi / kBN;
-        seq.next_t = max(seq.next_t, seq.thi + 1);
-      }
-      seq.dense = false;
-    }
-    if (seq.chunk < seq.nchunks) return -1 - seq.chunk++;
-    return INT_MIN;
-  };
-
-  // ---- staging.  K and V tiles live row-major in LDS (bf16, chunk-swizzled)
-  // and are filled by LDS-DMA buffer loads: each wave moves NDMA KiB of K and
-  // of V per tile, lane l writing 16 bytes at the wave's base + 16 l.  The
-  // buffer resources cover exactly this head's n rows, so rows at or past n
-  // (the tail tile, gathered padding n, absent tiles) arrive as zeros.
-  constexpr int GROWB = D * (F32 ? 4 : 2);  // bytes per row in HBM
+  // ---- LDS staging.  K and V tiles live row-major in LDS (bf16,
+  // chunk-swizzled) in two rings of NST stages.  bf16 tiles arrive by LDS-DMA
+  // buffer loads: each wave moves NDMA KiB of a tile, lane l writing 16 bytes
+  // at the wave's base + 16 l.  The buffer resources cover exactly this
+  // head's n rows, so rows at or past n (the tail tile, padding keys n, the
+  // tiles past the end of a list) arrive as zeros.  fp32 tiles go through
+  // registers and are rounded to bf16 on the way.
+  constexpr int GROWB = D * (F32 ? 4 : 2);     // bytes per row in HBM
+  constexpr int KREG = 0, VREG = NST * TILEB;  // ring offsets within kv_lds
   const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(static_cast<const char*>(p.k) + kv_head * GROWB), (short)0, n * GROWB, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(static_cast<const char*>(p.v) + kv_head * GROWB), (short)0, n * GROWB, kBufferFlags);
   const u32x4 wk = buffer_words(static_cast<const char*>(p.k) + kv_head * GROWB, (uint32_t)(n * GROWB));
   const u32x4 wv = buffer_words(static_cast<const char*>(p.v) + kv_head * GROWB, (uint32_t)(n * GROWB));
-  int dma_row[NDMA], dma_chunk[NDMA];
+  int dma_row[NDMA], dma_col[NDMA];  // tile row and byte offset within the row this lane moves
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
     const int r = wave * (kBN / kWaves) + i * RPD + lane / CH;
     dma_row[i] = r;
-    dma_chunk[i] = (lane % CH) ^ swz<D>(r);  // the source chunk this lane's LDS slot holds
+    dma_col[i] = ((lane % CH) ^ swz<D>(r)) * (F32 ? 32 : 16);  // the source chunk of this LDS slot
   }
-  // fetch tile `code` into the stage at kdst / vdst (code INT_MIN: an absent
-  // tile, all zeros)
-  // The wait-count pass treats the DMA's address register as still in use
-  // until the load lands, so letting the register allocator hand it to the
-  // next LDS read costs a vmcnt(0) in the middle of the step.  Holding the
-  // offsets live to the end of the step avoids that.
-  unsigned dma_off[NDMA];
-  auto stage_into = [&](int code, lds_u8* __restrict__ kdst, lds_u8* __restrict__ vdst) {
-    const int* gk = glist + (code < 0 && code != INT_MIN ? (-1 - code) * kBN : 0);
+  // The wait-count pass treats a DMA's address register as in use until the
+  // load lands, so letting the register allocator hand it to a later LDS read
+  // costs a vmcnt(0) in the middle of a step.  The offsets are held live to
+  // the end of each V half instead.
+  unsigned dma_off[2][NDMA];
+  // fetch matrix `which` (0 K, 1 V) of the keys key[i] (one per DMA slot)
+  // into LDS at byte `dst` of kv_lds
+  auto stage_keys = [&](int which, const int (&key)[NDMA], int dst) {
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
-      const int r = dma_row[i];
-      const int gkey = gk[r];  // read unconditionally so no branch splits the step
-      const int key = code >= 0 ? code * kBN + r : (code == INT_MIN ? n : gkey);
-      const int kbase = (wave * (kBN / kWaves) + i * RPD) * ROWB;
+      const int kbase = dst + (wave * (kBN / kWaves) + i * RPD) * ROWB;
+      const unsigned off = (unsigned)key[i] * GROWB + dma_col[i];
       if constexpr (F32) {
-        const unsigned off = (unsigned)key * GROWB + dma_chunk[i] * 32;
-        const u32x4 k0 = __builtin_amdgcn_raw_buffer_load_b128(rsk, (int)off, 0, 0);
-        const u32x4 k1 = __builtin_amdgcn_raw_buffer_load_b128(rsk, (int)(off + 16), 0, 0);
-        const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rsv, (int)off, 0, 0);
-        const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rsv, (int)(off + 16), 0, 0);
-        auto cvt = [](const u32x4& a, const u32x4& c) {
-          return u32x4{pack_bf16(__uint_as_float(a[0]), __uint_as_float(a[1])),
-                       pack_bf16(__uint_as_float(a[2]), __uint_as_float(a[3])),
-                       pack_bf16(__uint_as_float(c[0]), __uint_as_float(c[1])),
-                       pack_bf16(__uint_as_float(c[2]), __uint_as_float(c[3]))};
-        };
-        *(__attribute__((address_space(3))) u32x4*)(kdst + kbase + 16 * lane) = cvt(k0, k1);
-        *(__attribute__((address_space(3))) u32x4*)(vdst + kbase + 16 * lane) = cvt(v0, v1);
+        const __amdgpu_buffer_rsrc_t rs = which ? rsv : rsk;
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+        const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 16), 0, 0);
+        *(__attribute__((address_space(3))) u32x4*)(kv_base + kbase + 16 * lane) =
+            u32x4{pack_bf16(__uint_as_float(a[0]), __uint_as_float(a[1])),
+                  pack_bf16(__uint_as_float(a[2]), __uint_as_float(a[3])),
+                  pack_bf16(__uint_as_float(c[0]), __uint_as_float(c[1])),
+                  pack_bf16(__uint_as_float(c[2]), __uint_as_float(c[3]))};
       } else {
-        const unsigned off = (unsigned)key * GROWB + dma_chunk[i] * 16;
-        dma16(wk, (uint32_t)(uintptr_t)(kdst + kbase), off);
-        dma16(wv, (uint32_t)(uintptr_t)(vdst + kbase), off);
-        dma_off[i] = off;
+        dma16(which ? wv : wk, (uint32_t)(uintptr_t)(kv_base + kbase), off);
+        dma_off[which][i] = off;
       }
     }
   };
-  lds_u8* const k_region = kv_base;
-  lds_u8* const v_region = kv_base + NST * TILEB;
-  auto stage_tile = [&](int code, int st) { stage_into(code, k_region + st * TILEB, v_region + st * TILEB); };
-  // Offset-bitmap words for a contiguous tile.  The wave's rows need offsets
-  // [i0w - j0 - 63, i0w - j0 + 31], which lie in four consecutive words; they
-  // come through the scalar cache and each lane picks its three.
-  auto load_sw = [&](int code, uint32_t (&sw)[4]) {
-    const int wq = code >= 0 ? (i0w - code * kBN - (kBN - 1)) >> 5 : 0;
-    const int wc = max(wq, -kPrePad);
+  // contiguous tile `code` (keys code*64 ..)
+  auto stage_tile = [&](int which, int code, int dst) {
+    int key[NDMA];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sw[k] = ldc(bo, wc + k);
+    for (int i = 0; i < NDMA; ++i) key[i] = code * kBN + dma_row[i];
+    stage_keys(which, key, dst);
   };
-  // Per lane, a 64-bit word K with bit kk set when key kk of the tile is in
-  // S_qrow.  The lane's scores are keys kk = 32*sk + 8*a + 4*half + bb (sk,
-  // a, bb the element coordinates), so Kh = K >> (4*half) puts element
-  // (sk, a, bb) at bit 8*a + bb of word sk.
-  auto key_word = [&](int code, const uint32_t (&sw)[4], uint32_t& kh0, uint32_t& kh1) {
-    uint32_t k0 = 0u, k1 = 0u;
-    if (code >= 0) {
-      const int j0 = code * kBN;
-      const int dq = qrow - j0;  // largest causal key index of this row
-      // bits of the offset bitmap from offset dq - 63 upward: bit x <-> key 63 - x
-      const int base = i0w - j0 - (kBN - 1);
-      const bool up = ((base & 31) + ql) >= 32;  // this lane's window starts one word on
-      const uint32_t b0 = up ? sw[1] : sw[0], b1 = up ? sw[2] : sw[1], b2 = up ? sw[3] : sw[2];
-      const int sh = (dq - (kBN - 1)) & 31;
-      const uint32_t l0 = __builtin_amdgcn_alignbit(b1, b0, sh);
-      const uint32_t l1 = __builtin_amdgcn_alignbit(b2, b1, sh);
-      k0 = __builtin_bitreverse32(l1);
-      k1 = __builtin_bitreverse32(l0);
-      const uint32_t vw0 = ldc(bv, j0 >> 5), vw1 = ldc(bv, (j0 >> 5) + 1);
-      // columns are visible up to key dq
-      const uint32_t c0 = dq >= 31 ? ~0u : (dq < 0 ? 0u : ((2u << dq) - 1u));
-      const uint32_t c1 = dq >= 63 ? ~0u : (dq < 32 ? 0u : ((2u << (dq - 32)) - 1u));
-      k0 |= vw0 & c0;
-      k1 |= vw1 & c1;
-    } else if (code != INT_MIN) {
-      // gathered keys ascend (padding n sorts last): the visible ones are a prefix
-      const int* keys = &glist[(-1 - code) * kBN];
-      int lo = 0;
+
+  // ---- key words.  Per lane, a 64-bit word K with bit kk set when key kk
+  // of the tile is in S_qrow.  The lane's scores are keys kk = 32*sk + 8*a +
+  // 4*half + bb (sk, a, bb the element coordinates), so Kh = K >> (4*half)
+  // puts element (sk, a, bb) at bit 8*a + bb of word sk.
+  struct BitWords {
+    uint32_t o[4];  // offset-bitmap words covering the wave's windows
+    uint32_t v[2];  // column-bitmap words of the tile's keys
+  };
+  // scalar loads for contiguous tile `code`: the wave's rows need offsets
+  // [i0w - j0 - 63, i0w - j0 + 31], which lie in four consecutive words
+  auto load_words = [&](int code, BitWords& w) {
+    const int j0 = code * kBN;
+    const int wq = (i0w - j0 - (kBN - 1)) >> 5;
+    const int wc = max(wq, -kPrePad);  // further below, the window holds only zeros
 #pragma unroll
-      for (int step = 32; step > 0; step >>= 1)
-        if (keys[lo + step - 1] <= qrow) lo += step;
-      const int cnt = lo + (lo == 63 && keys[63] <= qrow ? 1 : 0);
-      k0 = cnt >= 32 ? ~0u : ((1u << cnt) - 1u);
-      k1 = cnt >= 64 ? ~0u : (cnt <= 32 ? 0u : ((1u << (cnt - 32)) - 1u));
-    }
+    for (int k = 0; k < 4; ++k) w.o[k] = ldc(bo, wc + k);
+    w.v[0] = ldc(bv, j0 >> 5);
+    w.v[1] = ldc(bv, (j0 >> 5) + 1);
+  };
+  auto key_word_tile = [&](int code, const BitWords& w, uint32_t& kh0, uint32_t& kh1) {
+    const int j0 = code * kBN;
+    const int dq = qrow - j0;  // largest causal key index of this row
+    // bits of the offset bitmap from offset dq - 63 upward: bit x <-> key 63 - x
+    const int base = i0w - j0 - (kBN - 1);
+    const bool up = ((base & 31) + ql) >= 32;  // this lane's window starts one word on
+    const uint32_t b0 = up ? w.o[1] : w.o[0], b1 = up ? w.o[2] : w.o[1], b2 = up ? w.o[3] : w.o[2];
+    const int sh = (dq - (kBN - 1)) & 31;
+    const uint32_t l0 = __builtin_amdgcn_alignbit(b1, b0, sh);
+    const uint32_t l1 = __builtin_amdgcn_alignbit(b2, b1, sh);
+    uint32_t k0 = __builtin_bitreverse32(l1);
+    uint32_t k1 = __builtin_bitreverse32(l0);
+    // columns are visible up to key dq
+    const uint32_t c0 = dq >= 31 ? ~0u : (dq < 0 ? 0u : ((2u << dq) - 1u));
+    const uint32_t c1 = dq >= 63 ? ~0u : (dq < 32 ? 0u : ((2u << (dq - 32)) - 1u));
+    k0 |= w.v[0] & c0;
+    k1 |= w.v[1] & c1;
+    kh0 = __builtin_amdgcn_alignbit(k1, k0, 4 * half);
+    kh1 = k1 >> (4 * half);
+  };
+  // gathered chunk: its 64 keys ascend (padding n sorts last), so the visible
+  // ones are a prefix
+  auto key_word_chunk = [&](const int* keys, uint32_t& kh0, uint32_t& kh1) {
+    int lo = 0;
+#pragma unroll
+    for (int step = 32; step > 0; step >>= 1)
+      if (keys[lo + step - 1] <= qrow) lo += step;
+    const int cnt = lo + (lo == 63 && keys[63] <= qrow ? 1 : 0);
+    const uint32_t k0 = cnt >= 32 ? ~0u : ((1u << cnt) - 1u);
+    const uint32_t k1 = cnt >= 64 ? ~0u : (cnt <= 32 ? 0u : ((1u << (cnt - 32)) - 1u));
     kh0 = __builtin_amdgcn_alignbit(k1, k0, 4 * half);
     kh1 = k1 >> (4 * half);
   };
 
-  // per-lane LDS byte offsets of the MFMA operand reads, for stage 0
+  // ---- matrix-core operands.  Per-lane LDS byte offsets (within kv_lds) of
+  // the reads in stage 0; other stages add a multiple of TILEB as an
+  // immediate.
   int koff[KS];  // K rows ql (+32 via the immediate), chunk 2*kk + half
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) koff[kk] = ql * ROWB + 16 * ((2 * kk + half) ^ swz<D>(ql));
+  for (int kk = 0; kk < KS; ++kk) koff[kk] = KREG + ql * ROWB + 16 * ((2 * kk + half) ^ swz<D>(ql));
   // V^T through ds_read_b64_tr_b16: in each 16-lane group, source lane
   // j = 4r + pp reads 4 values of row r at columns 4*pp.., and output lane
   // i = 4pp' + q receives column i of rows 0..3.  Group G16 = 2*h + dgrp
@@ -485,42 +436,285 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       for (int dt = 0; dt < DT; ++dt) {
         const int row = 8 * part + 4 * hh + rr;
         const int chunk = 4 * dt + 2 * dgrp + (pp >> 1);
-        voff[part][dt] = row * ROWB + 16 * (chunk ^ swz<D>(row)) + 8 * (pp & 1);
+        voff[part][dt] = VREG + row * ROWB + 16 * (chunk ^ swz<D>(row)) + 8 * (pp & 1);
       }
   }
   typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-  auto qk_part = [&](const lds_u8* kr, f32x16& s0, f32x16& s1, int k_lo, int k_hi) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  f32x16 c0, c1;  // S^T of the tile whose softmax is next
+  uint32_t pk[16];  // its probabilities as bf16 pairs (the P^T operand)
+  // S^T(K stage st) = K Q^T in two 32-key halves; the operands of k-step
+  // kk+1 are read while k-step kk multiplies
+  auto qk = [&](int st) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c0[e] = c1[e] = 0.f;
+    bf16x8 ka[2][2];
+    auto fetch = [&](int kk, bf16x8 (&dst)[2]) {
+      dst[0] = *(const lds_bf16x8*)(kv_base + koff[kk] + st * TILEB);
+      dst[1] = *(const lds_bf16x8*)(kv_base + koff[kk] + st * TILEB + 32 * ROWB);
+    };
+    fetch(0, ka[0]);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      if (kk < k_lo || kk >= k_hi) continue;
-      const bf16x8 a0 = *(const lds_bf16x8*)(kr + koff[kk]);
-      const bf16x8 a1 = *(const lds_bf16x8*)(kr + koff[kk] + 32 * ROWB);
-      s0 = mfma32(a0, qf[kk], s0);
-      s1 = mfma32(a1, qf[kk], s1);
+      if (kk + 1 < KS) fetch(kk + 1, ka[(kk + 1) & 1]);
+      c0 = mfma32(ka[kk & 1][0], qf[kk], c0);
+      c1 = mfma32(ka[kk & 1][1], qf[kk], c1);
     }
   };
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  auto read_vt = [&](const lds_u8* vr, int part, int dt, int c4) -> v4i16 {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(vr + voff[part][dt] + c4 * 16 * ROWB));
-  };
-  // move the operand offsets one stage on (stage s -> s+1 mod NST)
-  auto advance = [&](int (&o)[KS], int from) {
-    const int delta = from == NST - 1 ? -(NST - 1) * TILEB : TILEB;
+  // O^T += V^T P^T for V stage st; the operands of the next 16-key chunk are
+  // read while the current chunk's products run
+  auto pv = [&](int st) {
+    v4i16 vb[2][DT][2];
+    auto fetch = [&](int c4, v4i16 (&dst)[DT][2]) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) o[kk] += delta;
-  };
-  auto advance_v = [&](int from) {
-    const int delta = from == NST - 1 ? -(NST - 1) * TILEB : TILEB;
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int part = 0; part < 2; ++part)
+        for (int part = 0; part < 2; ++part)
+          dst[dt][part] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(kv_base + voff[part][dt] + st * TILEB + c4 * 16 * ROWB));
+    };
+    fetch(0, vb[0]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) voff[part][dt] += delta;
+    for (int c4 = 0; c4 < 4; ++c4) {
+      if (c4 + 1 < 4) fetch(c4 + 1, vb[(c4 + 1) & 1]);
+      const bf16x8 pf = as_bf16x8(u32x4{pk[4 * c4], pk[4 * c4 + 1], pk[4 * c4 + 2], pk[4 * c4 + 3]});
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 av = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(vb[c4 & 1][dt][0], vb[c4 & 1][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = mfma32(av, pf, acc[dt]);
+      }
+    }
   };
-  constexpr int kWaitAfter = 2 * NDMA;  // DMAs issued per step after the awaited tile
+  // online softmax of S = (c0, c1) under the key words: updates the running
+  // max and sum, rescales O when the max has grown past the lazy threshold,
+  // and leaves the probabilities in pk
+  auto softmax = [&](uint32_t kc0, uint32_t kc1) {
+    float pm[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+      for (int e = 4 * q4; e < 4 * q4 + 4; ++e) {
+        const int bpos = 8 * (e >> 2) + (e & 3);
+        const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, bpos, 1);
+        const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, bpos, 1);
+        c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
+        c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
+      }
+      const int e = 4 * q4;
+      pm[q4] = __builtin_elementwise_maximum(
+          __builtin_elementwise_maximum(__builtin_elementwise_maximum(c0[e], c0[e + 1]),
+                                        __builtin_elementwise_maximum(c0[e + 2], c0[e + 3])),
+          __builtin_elementwise_maximum(__builtin_elementwise_maximum(c1[e], c1[e + 1]),
+                                        __builtin_elementwise_maximum(c1[e + 2], c1[e + 3])));
+    }
+    float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(pm[0], pm[1]),
+                                             __builtin_elementwise_maximum(pm[2], pm[3]));
+    mx = half_max(mx);
+    const float mt = mx * p.c;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau)) {
+      const float mnew = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+      m_run = mnew;
+    }
+    const float nm = -m_run;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pk[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c0[2 * e], p.c, nm)),
+                        __builtin_amdgcn_exp2f(fmaf(c0[2 * e + 1], p.c, nm)));
+      pk[8 + e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c1[2 * e], p.c, nm)),
+                            __builtin_amdgcn_exp2f(fmaf(c1[2 * e + 1], p.c, nm)));
+    }
+    // row sum of the bf16 probabilities the PV product uses
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, l_run, false);
+  };
+  auto hold_dma_offsets = [&]() {
+    if constexpr (!F32) {
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) asm volatile("" ::"v"(dma_off[0][i]), "v"(dma_off[1][i]));
+    }
+  };
+  constexpr int kDmaPerStep = 2 * NDMA;  // K and V loads one step issues
+  const bool lead = wave < kWaves / 2;   // waves w and w + 4 share a SIMD
 
-  // ---- rounds: each gathers up to kListCap uncovered columns; the first
-  //      round also walks the contiguous tiles
+  // ---- ping-pong pipeline over T tiles.  Tile t's K sits in K stage t % NST
+  // and its V in V stage t % NST.  Work on a tile splits into
+  //   V(t): the softmax of S(t) into P(t), the key word of tile t+1, and the
+  //         loads of K(t+3) and V(t+2);
+  //   M(t): O += V(t) P(t) and S(t+1) = K(t+1) Q^T on the matrix cores.
+  // Waves 0-3 run V(t) then M(t); waves 4-7 run half a step behind, so each
+  // SIMD overlaps one wave's vector work with the other's matrix work.  Every
+  // half ends at a workgroup barrier, and after each M half a wave waits
+  // until at most its newest step of loads is in flight.  With the half-step
+  // offset this completes K(t+1) and V(t) at the barrier before either group
+  // first reads them, and no stage is refilled before both groups have
+  // finished reading it.
+  //
+  // `src` supplies the tiles: stage_first() loads K(0..2) and V(0..1),
+  // key_word_first() gives the key word of tile 0; within V(t), begin()
+  // starts the fetches step t needs, key_word() gives the key word of tile
+  // t+1, stage_k()/stage_v() load K(t+3) / V(t+2), and rotate() moves on.
+  // Tiles past the end read as zeros and have empty key words.
+  auto pipeline = [&](auto& src, int T) {
+    src.stage_first();
+    uint32_t kc0, kc1;
+    src.key_word_first(kc0, kc1);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    qk(0);
+    if (!lead) __syncthreads();  // the half-step offset
+    int t = 0;
+    auto step = [&](auto s_const) -> bool {
+      constexpr int S = decltype(s_const)::value;
+      // V(t)
+      src.begin();
+      softmax(kc0, kc1);
+      src.key_word(kc0, kc1);
+      src.stage_k(KREG + ((S + 3) % NST) * TILEB);
+      src.stage_v(VREG + ((S + 2) % NST) * TILEB);
+      hold_dma_offsets();
+      src.rotate();
+      __syncthreads();
+      // M(t)
+      pv(S);
+      qk((S + 1) % NST);
+      if constexpr (F32) __builtin_amdgcn_s_waitcnt(0x0F70);
+      else __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerStep);
+      __syncthreads();
+      return ++t < T;
+    };
+    while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{}) &&
+           step(std::integral_constant<int, 2>{}) && step(std::integral_constant<int, 3>{})) {
+    }
+    if (lead) __syncthreads();  // matches the trailing group's extra barrier
+    // drain: every outstanding load lands before the stages are reused
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+  };
+
+  // ---- contiguous tiles: the key ranges the slash clusters reach, in
+  // ascending key order.  Cluster ranges are disjoint (clusters are split
+  // wherever neighbouring offsets differ by more than bmp + 63), so the list
+  // is their concatenation; it is built in LDS windows of kListCap tiles.
+  const int32_t* clo = p.clLo + (size_t)g * p.cap_s;
+  const int32_t* chi = p.clHi + (size_t)g * p.cap_s;
+  int ncb;  // clusters whose smallest offset is at most i1
+  {
+    const int ncl = ldc(p.counts, 4 * g + 2);
+    int lo = 0, hi = ncl;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (ldc(clo, mid) <= i1) lo = mid + 1;
+      else hi = mid;
+    }
+    ncb = lo;
+  }
+  const int tend = (n + kBN - 1) / kBN;  // a tile index past the keys
+  // the j-th cluster in key order covers tiles [tlo, thi]; in a full block
+  // every one of them is active, in the short last block they are tested
+  auto cluster_tiles = [&](int j, int& tlo, int& thi) {
+    const int c = ncb - 1 - j;
+    tlo = max(0, i0 - p.clHi[(size_t)g * p.cap_s + c]) / kBN;
+    thi = (i1 - p.clLo[(size_t)g * p.cap_s + c]) / kBN;
+    if (j > 0) tlo = max(tlo, (i1 - p.clLo[(size_t)g * p.cap_s + c + 1]) / kBN + 1);
+  };
+  auto active_count = [&](int tlo, int thi) -> int {
+    if (!partial) return max(0, thi - tlo + 1);
+    int k = 0;
+    for (int t = tlo; t <= thi; ++t) k += tile_active(t) ? 1 : 0;
+    return k;
+  };
+  int T_total = 0;
+  for (int j0 = 0; j0 < ncb; j0 += kThreads) {
+    int cnt = 0;
+    if (j0 + tid < ncb) {
+      int tlo, thi;
+      cluster_tiles(j0 + tid, tlo, thi);
+      cnt = active_count(tlo, thi);
+    }
+    int tot;
+    block_excl_scan<kThreads>(cnt, &tot, wcnt);
+    T_total += tot;
+  }
+  // Tile codes for steps t+1, t+2, t+3 live in scalar registers; the code
+  // of t+4 is read from the LDS list one step ahead (unconditionally, from a
+  // clamped index) and the bitmap words of tile t+1 are requested at the
+  // start of the V half, so neither wait sits on the critical path.
+  struct TileSrc {
+    decltype(stage_tile)& stage_fn;
+    decltype(load_words)& load_fn;
+    decltype(key_word_tile)& key_fn;
+    const int* list;
+    int T, tend;
+    int t, c1, c2, c3, pref;
+    BitWords w;
+    __device__ int code(int i) const {
+      const int x = __builtin_amdgcn_readfirstlane(list[min(i, T - 1)]);
+      return i < T ? x : tend;
+    }
+    __device__ void stage_first() {
+      const int c0 = code(0);
+      c1 = code(1);
+      c2 = code(2);
+      c3 = code(3);
+      t = 0;
+      stage_fn(0, c0, KREG);
+      stage_fn(0, c1, KREG + TILEB);
+      stage_fn(0, c2, KREG + 2 * TILEB);
+      stage_fn(1, c0, VREG);
+      stage_fn(1, c1, VREG + TILEB);
+      load_fn(c0, w);
+    }
+    __device__ void key_word_first(uint32_t& k0, uint32_t& k1) { key_fn(code(0), w, k0, k1); }
+    __device__ void begin() {
+      load_fn(c1, w);
+      pref = list[min(t + 4, T - 1)];
+    }
+    __device__ void key_word(uint32_t& k0, uint32_t& k1) { key_fn(c1, w, k0, k1); }
+    __device__ void stage_k(int dst) { stage_fn(0, c3, dst); }
+    __device__ void stage_v(int dst) { stage_fn(1, c2, dst); }
+    __device__ void rotate() {
+      c1 = c2;
+      c2 = c3;
+      const int x = __builtin_amdgcn_readfirstlane(pref);
+      c3 = t + 4 < T ? x : tend;
+      ++t;
+    }
+  };
+  for (int wst = 0; wst < T_total; wst += kListCap) {
+    int base = 0;
+    for (int j0 = 0; j0 < ncb; j0 += kThreads) {
+      int cnt = 0, tlo = 0, thi = -1;
+      if (j0 + tid < ncb) {
+        cluster_tiles(j0 + tid, tlo, thi);
+        cnt = active_count(tlo, thi);
+      }
+      int tot;
+      int pos = base + block_excl_scan<kThreads>(cnt, &tot, wcnt) - wst;
+      for (int t = tlo; t <= thi && pos < kListCap; ++t) {
+        if (partial && !tile_active(t)) continue;
+        if (pos >= 0) glist[pos] = t;
+        ++pos;
+      }
+      base += tot;
+    }
+    __syncthreads();
+    const int T = min(T_total - wst, kListCap);
+    TileSrc src{stage_tile, load_words, key_word_tile, glist, T, tend, 0, 0, 0, 0, 0, {}};
+    pipeline(src, T);
+    n_dense += T;
+  }
+
+  // ---- gathered tiles: selected columns in no active tile, 64 per tile
   const int32_t* cv = p.cleanV + (size_t)g * p.cap_v;
   int total_v;
   {
@@ -533,9 +727,42 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     }
     total_v = lo;
   }
+  auto stage_chunk = [&](int which, int t, int nch, int dst) {
+    int key[NDMA];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) key[i] = t < nch ? glist[t * kBN + dma_row[i]] : n;
+    stage_keys(which, key, dst);
+  };
+  struct ChunkSrc {
+    decltype(stage_chunk)& stage_fn;
+    decltype(key_word_chunk)& key_fn;
+    const int* list;
+    int T, t;
+    __device__ void kw(int i, uint32_t& k0, uint32_t& k1) {
+      if (i < T) {
+        key_fn(list + i * kBN, k0, k1);
+      } else {
+        k0 = 0u;
+        k1 = 0u;
+      }
+    }
+    __device__ void stage_first() {
+      t = 0;
+      stage_fn(0, 0, T, KREG);
+      stage_fn(0, 1, T, KREG + TILEB);
+      stage_fn(0, 2, T, KREG + 2 * TILEB);
+      stage_fn(1, 0, T, VREG);
+      stage_fn(1, 1, T, VREG + TILEB);
+    }
+    __device__ void key_word_first(uint32_t& k0, uint32_t& k1) { kw(0, k0, k1); }
+    __device__ void begin() {}
+    __device__ void key_word(uint32_t& k0, uint32_t& k1) { kw(t + 1, k0, k1); }
+    __device__ void stage_k(int dst) { stage_fn(0, t + 3, T, dst); }
+    __device__ void stage_v(int dst) { stage_fn(1, t + 2, T, dst); }
+    __device__ void rotate() { ++t; }
+  };
   int cursor = 0;
-  bool first_round = true;
-  while (first_round || cursor < total_v) {
+  while (cursor < total_v) {
     // gather the next batch of columns whose tile no offset reaches
     int fill = 0;
     while (cursor < total_v && fill + kThreads <= kListCap) {
@@ -562,151 +789,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       cursor += kThreads;
       __syncthreads();
     }
-    // pad the last gathered chunk with n: sorts after every key, reads as zeros
+    if (fill == 0) continue;
+    // pad the last chunk with n: sorts after every key, reads as zeros
     for (int r = fill + tid; r < ((fill + kBN - 1) / kBN) * kBN; r += kThreads) glist[r] = n;
-    seq.chunk = 0;
-    seq.nchunks = (fill + kBN - 1) / kBN;
-    if (!first_round) seq.dense = false;
-    first_round = false;
     __syncthreads();
-
-    // Software pipeline over the round's tiles, NST stages deep.  Tile t lives
-    // in stage t % NST.  Step t: start the DMA of tile t+3, compute S(t+1) =
-    // K(t+1) Q^T on the matrix cores alongside the softmax of tile t, add
-    // V(t) P(t), then wait for this wave's share of tile t+2 and meet at the
-    // barrier, after which tile t+2 is complete and stage (t-1) % NST is free.
-    int cur = next_tile();
-    if (cur == INT_MIN) continue;
-    int nxt = next_tile();
-    int n2 = nxt != INT_MIN ? next_tile() : INT_MIN;
-    uint32_t sw_n[4], sw_nn[4];
-    uint32_t kc0, kc1;
-    f32x16 c0, c1;
-    {
-      uint32_t sw_c[4];
-      load_sw(cur, sw_c);
-      load_sw(nxt, sw_n);
-      stage_tile(cur, 0);
-      stage_tile(nxt, 1);
-      stage_tile(n2, 2);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      __syncthreads();
-      key_word(cur, sw_c, kc0, kc1);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) c0[e] = c1[e] = 0.f;
-      qk_part(k_region, c0, c1, 0, KS);  // stage 0
-    }
-    advance(koff, 0);  // K operand reads now point at stage 1
-    int t = 0;
-    // One step.  The four LDS pointers never overlap in what they touch (K
-    // and V of the stages being read, the stage being filled), which lets the
-    // compiler keep the DMA in flight across the operand reads.
-    auto step = [&](const lds_u8* __restrict__ krd, const lds_u8* __restrict__ vrd,
-                    lds_u8* __restrict__ kdma, lds_u8* __restrict__ vdma, int n3) {
-      // -- branchy part: key word of tile t+1, mask and row max of tile t, the
-      //    rare rescale.  No K/V reads or DMA happen here.
-      load_sw(n2, sw_nn);
-      uint32_t kn0, kn1;
-      key_word(nxt, sw_n, kn0, kn1);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int bpos = 8 * (e >> 2) + (e & 3);
-        const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, bpos, 1);
-        const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, bpos, 1);
-        c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
-        c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
-      }
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(c0[e], c1[e]));
-      mx = half_max(mx);
-      const float mt = mx * p.c;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau)) {
-        const float mnew = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
-        m_run = mnew;
-      }
-      // -- straight-line part: start the DMA of tile t+3, then S(t+1) on the
-      //    matrix cores alongside exp/convert of tile t, then O += V(t) P(t)
-      stage_into(n3, kdma, vdma);
-      f32x16 sn0, sn1;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sn0[e] = sn1[e] = 0.f;
-      qk_part(krd, sn0, sn1, 0, KS);
-      const float nm = -m_run;
-      uint32_t pk[16];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pk[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c0[2 * e], p.c, nm)),
-                          __builtin_amdgcn_exp2f(fmaf(c0[2 * e + 1], p.c, nm)));
-        pk[8 + e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c1[2 * e], p.c, nm)),
-                              __builtin_amdgcn_exp2f(fmaf(c1[2 * e + 1], p.c, nm)));
-      }
-      // row sum of the bf16 probabilities the PV product uses
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, l_run, false);
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const bf16x8 pf = as_bf16x8(u32x4{pk[4 * c4], pk[4 * c4 + 1], pk[4 * c4 + 2], pk[4 * c4 + 3]});
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const v4i16 lo4 = read_vt(vrd, 0, dt, c4), hi4 = read_vt(vrd, 1, dt, c4);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[dt] = mfma32(av, pf, acc[dt]);
-        }
-      }
-      if constexpr (!F32) {
-#pragma unroll
-        for (int i = 0; i < NDMA; ++i) asm volatile("" ::"v"(dma_off[i]));
-      }
-      c0 = sn0;
-      c1 = sn1;
-      kc0 = kn0;
-      kc1 = kn1;
-    };
-    while (true) {
-      const int n3 = n2 != INT_MIN ? next_tile() : INT_MIN;
-      if (cur >= 0) ++n_dense;
-      else ++n_gath;
-      const int sdma = (t + 3) % NST;
-      step(k_region, v_region, k_region + sdma * TILEB, v_region + sdma * TILEB, n3);
-      if (nxt == INT_MIN) break;
-      // this wave's share of tile t+2 has landed once at most the loads of
-      // this step are outstanding; the barrier then completes tile t+2 for all
-      if constexpr (F32) __builtin_amdgcn_s_waitcnt(0x0F70);
-      else __builtin_amdgcn_s_waitcnt(0x0F70 | kWaitAfter);
-      __syncthreads();
-#pragma unroll
-      for (int w = 0; w < 4; ++w) sw_n[w] = sw_nn[w];
-      advance(koff, (t + 1) % NST);
-      advance_v(t % NST);
-      cur = nxt;
-      nxt = n2;
-      n2 = n3;
-      ++t;
-    }
-    // drain: every outstanding DMA lands before the next round reuses stages
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-    __syncthreads();
-    // rewind the operand offsets to stage 0
-    {
-      const int kst = (t + 1) % NST, vst = t % NST;
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) koff[kk] -= kst * TILEB;
-#pragma unroll
-      for (int part = 0; part < 2; ++part)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) voff[part][dt] -= vst * TILEB;
-    }
+    const int nch = (fill + kBN - 1) / kBN;
+    ChunkSrc src{stage_chunk, key_word_chunk, glist, nch, 0};
+    pipeline(src, nch);
+    n_gath += nch;
   }
 
   // ---------------- finish: normalise, write O and lse

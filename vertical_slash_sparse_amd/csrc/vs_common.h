@@ -72,10 +72,17 @@ __device__ __forceinline__ u32x4 buffer_words(const void* base, uint32_t bytes) 
 // nothing the compiler allocates depends on it; completion is tracked by the
 // caller with an explicit s_waitcnt vmcnt.  Offsets at or past num_records
 // deliver zeros.
+// The LDS address and the resource must be wave-uniform; readfirstlane
+// states that to the compiler (it folds away when they already sit in SGPRs).
 __device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc[0]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc[1]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc[2]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc[3])};
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "s"(a), "v"(voff), "s"(r)
                : "memory", "m0");
 }
 
