@@ -234,6 +234,28 @@ __device__ __forceinline__ int swz(int r) {
   else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
 }
 
+// Scheduling groups for the matrix half: npv products whose operand takes
+// two LDS reads, then nqk taking one; each product's reads are issued
+// `ahead` products before it.
+template <int NPV, int NQK, int AHEAD>
+struct MhalfOrder {
+  static constexpr int reads(int i) { return i < NPV ? 2 : (i < NPV + NQK ? 1 : 0); }
+  static constexpr int prologue_reads() {
+    int r = 0;
+    for (int i = 0; i < AHEAD; ++i) r += reads(i);
+    return r;
+  }
+  template <int I>
+  static __device__ __forceinline__ void emit() {
+    if constexpr (I < NPV + NQK) {
+      constexpr int r = reads(I + AHEAD);
+      if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x080, r, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      emit<I + 1>();
+    }
+  }
+};
+
 template <int D, bool F32>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   constexpr int KS = D / 16;            // k-steps of Q K^T
@@ -444,47 +466,61 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   f32x16 c0, c1;  // S^T of the tile whose softmax is next
   uint32_t pk[16];  // its probabilities as bf16 pairs (the P^T operand)
-  // S^T(K stage st) = K Q^T in two 32-key halves; the operands of k-step
-  // kk+1 are read while k-step kk multiplies
-  auto qk = [&](int st) {
+  // M half: O^T += V^T(V stage vs) P^T, then S^T = K(K stage ks) Q^T, as
+  // one sequence of matrix products.  Product i's LDS operand goes into
+  // ring[i % (kAhead + 1)] kAhead products before it runs, so the reads stay
+  // ahead of the matrix cores across the switch from PV to QK.
+  constexpr int NPV = 4 * DT, NQK = 2 * KS, kAhead = 5;
+  auto mhalf = [&](int vs, int ks) {
+    u32x4 ring[kAhead + 1];
+    auto fetch = [&](int i) {
+      u32x4& dst = ring[i % (kAhead + 1)];
+      if (i < NPV) {  // PV product: 16-key chunk c4, head dims 32*dt ..
+        const int c4 = i / DT, dt = i % DT;
+        const int o = vs * TILEB + c4 * 16 * ROWB;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(kv_base + voff[0][dt] + o));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(kv_base + voff[1][dt] + o));
+        dst = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {  // QK product: k-step kk, key half h
+        const int j = i - NPV, kk = j >> 1, h = j & 1;
+        dst = *(const __attribute__((address_space(3))) u32x4*)(kv_base + koff[kk] + ks * TILEB + h * 32 * ROWB);
+      }
+    };
 #pragma unroll
     for (int e = 0; e < 16; ++e) c0[e] = c1[e] = 0.f;
-    bf16x8 ka[2][2];
-    auto fetch = [&](int kk, bf16x8 (&dst)[2]) {
-      dst[0] = *(const lds_bf16x8*)(kv_base + koff[kk] + st * TILEB);
-      dst[1] = *(const lds_bf16x8*)(kv_base + koff[kk] + st * TILEB + 32 * ROWB);
-    };
-    fetch(0, ka[0]);
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) fetch(i);
+#pragma unroll
+    for (int i = 0; i < NPV + NQK; ++i) {
+      if (i + kAhead < NPV + NQK) fetch(i + kAhead);
+      const bf16x8 a = as_bf16x8(ring[i % (kAhead + 1)]);
+      if (i < NPV) {
+        const int c4 = i / DT, dt = i % DT;
+        const bf16x8 pf = as_bf16x8(u32x4{pk[4 * c4], pk[4 * c4 + 1], pk[4 * c4 + 2], pk[4 * c4 + 3]});
+        acc[dt] = mfma32(a, pf, acc[dt]);
+      } else {
+        const int j = i - NPV, kk = j >> 1;
+        if (j & 1) c1 = mfma32(a, qf[kk], c1);
+        else c0 = mfma32(a, qf[kk], c0);
+      }
+    }
+    // keep that order through scheduling: the first kAhead operands' reads,
+    // then per product the reads kAhead ahead and the product itself
+    __builtin_amdgcn_sched_group_barrier(0x080, MhalfOrder<NPV, NQK, kAhead>::prologue_reads(), 0);
+    MhalfOrder<NPV, NQK, kAhead>::template emit<0>();
+  };
+  // S^T(K stage 0) alone, for the first tile of a run
+  auto qk0 = [&]() {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c0[e] = c1[e] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      if (kk + 1 < KS) fetch(kk + 1, ka[(kk + 1) & 1]);
-      c0 = mfma32(ka[kk & 1][0], qf[kk], c0);
-      c1 = mfma32(ka[kk & 1][1], qf[kk], c1);
-    }
-  };
-  // O^T += V^T P^T for V stage st; the operands of the next 16-key chunk are
-  // read while the current chunk's products run
-  auto pv = [&](int st) {
-    v4i16 vb[2][DT][2];
-    auto fetch = [&](int c4, v4i16 (&dst)[DT][2]) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int part = 0; part < 2; ++part)
-          dst[dt][part] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16*)(kv_base + voff[part][dt] + st * TILEB + c4 * 16 * ROWB));
-    };
-    fetch(0, vb[0]);
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      if (c4 + 1 < 4) fetch(c4 + 1, vb[(c4 + 1) & 1]);
-      const bf16x8 pf = as_bf16x8(u32x4{pk[4 * c4], pk[4 * c4 + 1], pk[4 * c4 + 2], pk[4 * c4 + 3]});
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 av = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(vb[c4 & 1][dt][0], vb[c4 & 1][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[dt] = mfma32(av, pf, acc[dt]);
-      }
+      const bf16x8 a0 = *(const lds_bf16x8*)(kv_base + koff[kk]);
+      const bf16x8 a1 = *(const lds_bf16x8*)(kv_base + koff[kk] + 32 * ROWB);
+      c0 = mfma32(a0, qf[kk], c0);
+      c1 = mfma32(a1, qf[kk], c1);
     }
   };
   // online softmax of S = (c0, c1) under the key words: updates the running
@@ -570,7 +606,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     src.key_word_first(kc0, kc1);
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
-    qk(0);
+    qk0();
     if (!lead) __syncthreads();  // the half-step offset
     int t = 0;
     auto step = [&](auto s_const) -> bool {
@@ -583,10 +619,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       src.stage_v(VREG + ((S + 2) % NST) * TILEB);
       hold_dma_offsets();
       src.rotate();
+      // P(t) is finished here, in the vector half, not under the products
+#pragma unroll
+      for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(pk[e]));
       __syncthreads();
       // M(t)
-      pv(S);
-      qk((S + 1) % NST);
+      mhalf(S, (S + 1) % NST);
+      // and S(t+1) is complete before the next vector half starts
+      asm volatile("" : "+v"(c0), "+v"(c1));
       if constexpr (F32) __builtin_amdgcn_s_waitcnt(0x0F70);
       else __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerStep);
       __syncthreads();
