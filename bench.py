@@ -122,7 +122,10 @@ def source_digest(files):
 # workload and the digest of the kernel sources they were taken on.
 ATTN_SOURCES = ("vs_attn.hip", "vs_common.h", "vs_internal.h")
 INDEX_SOURCES = ("vs_index.hip", "vs_common.h", "vs_internal.h")
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    "zipf128k": {"digest": "02af5647a3e41341", "bytes": 19640588978},
+    "indexer128k": {"digest": "f42d252619b51066", "bytes": 1152831848},
+}
 
 
 def recorded_traffic(workload, sources):
