@@ -63,7 +63,9 @@ typedef enum { VS_VERTICAL = 0, VS_SLASH = 1 } vs_kind;
  *   w2        : bf16 [2][hidden]      (row 0 vertical head, row 1 slash head)
  *   vlog,slog : fp32 [h_kv][n]        (outputs, indexed by position j)
  * First layer: bf16 MFMA with fp32 accumulation.  Second layer: fp32.
- * Supported: d == 128, hidden == 128.  n >= 1, h_kv >= 1. */
+ * Supported: d == 128, hidden == 128.  n >= 1, h_kv >= 1, and each of
+ * k_rope and v below 4 GiB (h_kv * n * d * 2 < 2^32 bytes); larger inputs
+ * return VS_ERR_UNSUPPORTED -- call per group of KV heads instead. */
 vs_status vs_index(const void* k_rope, const void* v, int h_kv, int n, int d, int hidden,
                    const void* w1, const void* w2, float* vlog, float* slog,
                    hipStream_t stream);

@@ -70,6 +70,8 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert L.vs_index(p, p, 8, 100, 128, 64, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED
     assert L.vs_index(p, p, 0, 100, 128, 128, p, p, p, p, None) == vsa.VS_ERR_INVALID
     assert L.vs_index(None, p, 8, 100, 128, 128, p, p, p, p, None) == vsa.VS_ERR_INVALID
+    # one KV-head tensor must fit a 32-bit byte range (8 x 2^21 x 128 x 2 B = 4 GiB)
+    assert L.vs_index(p, p, 8, 1 << 21, 128, 128, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED
 
     def attn(**kw):
         a = dict(q=p, k=p, v=p, dt=0, h_q=32, h_kv=8, n=1024, d=128, scale=0.088, vi=p, vc=p,

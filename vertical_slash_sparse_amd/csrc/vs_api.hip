@@ -41,6 +41,8 @@ vs_status vs_index(const void* k_rope, const void* v, int h_kv, int n, int d, in
   if (h_kv <= 0 || n <= 0 || d <= 0 || hidden <= 0) return VS_ERR_INVALID;
   if ((long long)h_kv * n > (1LL << 40)) return VS_ERR_INVALID;
   if (d != 128 || hidden != 128) return VS_ERR_UNSUPPORTED;
+  // K and V are each read through one buffer resource with a 32-bit range
+  if ((long long)h_kv * n * d * 2 >= (1LL << 32)) return VS_ERR_UNSUPPORTED;
   return from_hip(launch_index(k_rope, v, h_kv, n, w1, w2, vlog, slog, stream));
 }
 

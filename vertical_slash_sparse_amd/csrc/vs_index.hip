@@ -9,16 +9,16 @@
 // Each position reads 2*d*2 = 512 bytes and costs 2*256*128 + 2*2*128 flops,
 // about 128 flop per byte -- under the MI355X ridge (~315 flop/B for bf16
 // MFMA against 8 TB/s), so the kernel is HBM-bound and is built to stream:
-//  * persistent workgroups; W1 (64 KiB of bf16) is staged into LDS once per
-//    workgroup and serves every position it visits;
-//  * H^T = W1 X^T on v_mfma_f32_32x32x16_bf16 with W1 rows as the A operand
-//    (from LDS) and 32 positions per wave as the B operand, loaded straight
-//    from HBM in the operand layout (16 bytes per lane per k-step, the whole
-//    512-byte row consumed by two lanes);
-//  * the second layer in fp32 on the vector ALUs from the fp32 accumulators,
-//    with the two wave halves' partial sums joined by one lane exchange;
-//  * the next 32 positions' rows are loaded before the current ones are
-//    multiplied, so HBM traffic overlaps the matrix work.
+//  * a workgroup of four waves takes 32 consecutive positions at a time; their
+//    K and V rows (16 KiB, contiguous in HBM) arrive by LDS-DMA into a ring of
+//    four stages, so every HBM read is a full 1 KiB line run and three blocks
+//    are in flight while one is multiplied;
+//  * wave w owns hidden units 32w .. 32w+31: its slice of W1 (the A operand of
+//    H^T = W1 X^T on v_mfma_f32_32x32x16_bf16) and of W2 stay in registers for
+//    the whole kernel, and the 32 positions are the B operand, read from LDS;
+//  * the second layer runs in fp32 on the vector ALUs from the fp32
+//    accumulators; the four waves' partial sums meet in LDS and are added
+//    after the next block's barrier, so each block costs one barrier.
 #include "vs_common.h"
 #include "vs_internal.h"
 
@@ -26,100 +26,134 @@ namespace vs {
 
 namespace {
 
-constexpr int kIdxD = 128;          // head dim
-constexpr int kIdxX = 2 * kIdxD;    // indexer input width
-constexpr int kIdxH = 128;          // hidden width
-constexpr int kIdxRow = kIdxX + 8;  // padded LDS row of W1 (bf16)
-constexpr int kIdxKS = kIdxX / 16;  // k-steps
-constexpr int kIdxHT = kIdxH / 32;  // 32-row tiles of H^T
+constexpr int kIdxD = 128;            // head dim
+constexpr int kIdxX = 2 * kIdxD;      // indexer input width
+constexpr int kIdxH = 128;            // hidden width
+constexpr int kIdxKS = kIdxX / 16;    // k-steps of the first layer
+constexpr int kIdxRows = 32;          // positions per block
+constexpr int kIdxRowB = kIdxD * 2;   // bytes of one K (or V) row
+constexpr int kIdxStageB = 2 * kIdxRows * kIdxRowB;  // K rows then V rows
+constexpr int kIdxNst = 4;            // ring stages
+constexpr int kIdxThreads = 256;
+constexpr int kIdxDma = kIdxStageB / 1024 / (kIdxThreads / 64);  // 1 KiB loads per wave per block
 
-__global__ __launch_bounds__(256) void index_kernel(const uint16_t* __restrict__ k,
-                                                    const uint16_t* __restrict__ v,
-                                                    const uint16_t* __restrict__ w1,
-                                                    const uint16_t* __restrict__ w2,
-                                                    float* __restrict__ vlog,
-                                                    float* __restrict__ slog,
-                                                    long long total_rows) {
-  __shared__ __align__(16) uint16_t w1_lds[kIdxH * kIdxRow];
-  __shared__ __align__(16) float w2_lds[kIdxH * 2];  // [hidden][vertical, slash]
+// XOR swizzle of the 16-byte chunks of a 256-byte row, so that 32 lanes
+// reading one chunk of 32 consecutive rows hit distinct banks
+__device__ __forceinline__ int idx_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, ql = lane & 31;
-  for (int id = tid; id < kIdxH * kIdxX / 8; id += 256) {
-    const int r = id / (kIdxX / 8), c8 = id % (kIdxX / 8);
-    *reinterpret_cast<u32x4*>(&w1_lds[r * kIdxRow + 8 * c8]) =
-        *reinterpret_cast<const u32x4*>(&w1[r * kIdxX + 8 * c8]);
-  }
-  for (int id = tid; id < kIdxH * 2; id += 256) {
-    const int hid = id >> 1, o = id & 1;
-    w2_lds[id] = __uint_as_float((uint32_t)w2[o * kIdxH + hid] << 16);
-  }
-  __syncthreads();
+__global__ __launch_bounds__(kIdxThreads, 2) void index_kernel(const uint16_t* __restrict__ k,
+                                                               const uint16_t* __restrict__ v,
+                                                               const uint16_t* __restrict__ w1,
+                                                               const uint16_t* __restrict__ w2,
+                                                               float* __restrict__ vlog,
+                                                               float* __restrict__ slog,
+                                                               long long total_rows) {
+  __shared__ __align__(16) uint8_t xs[kIdxNst * kIdxStageB];
+  __shared__ float2 red[2][4][kIdxRows];  // [block parity][wave][position] partial (vertical, slash)
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  lds_u8* const xbase = (lds_u8*)xs;
 
-  const long long step = (long long)gridDim.x * 4 * 32;
-  long long r0 = ((long long)blockIdx.x * 4 + wave) * 32;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, ql = lane & 31;
+  const int wave = wave_uniform(tid >> 6);
 
-  auto load_rows = [&](long long base, u32x4 (&bx)[kIdxKS]) {
-    const long long row = base + ql;
-    const long long rr = row < total_rows ? row : (total_rows - 1);
+  // W1 rows 32*wave + ql as A operands (k-step s: input dims 16s + 8*half ..)
+  bf16x8 wa[kIdxKS];
 #pragma unroll
-    for (int s = 0; s < kIdxKS; ++s) {
-      const uint16_t* src = s < kIdxKS / 2 ? k + rr * kIdxD + 16 * s + 8 * half
-                                           : v + rr * kIdxD + 16 * (s - kIdxKS / 2) + 8 * half;
-      bx[s] = *reinterpret_cast<const u32x4*>(src);
+  for (int s = 0; s < kIdxKS; ++s)
+    wa[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(w1 + (size_t)(32 * wave + ql) * kIdxX + 16 * s + 8 * half));
+  // W2 for the hidden units this lane's accumulators hold: 32*wave + 8a + 4*half + b
+  float w2v[16], w2s[16];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int h = 32 * wave + 8 * a + 4 * half + b;
+      w2v[4 * a + b] = __uint_as_float((uint32_t)w2[h] << 16);
+      w2s[4 * a + b] = __uint_as_float((uint32_t)w2[kIdxH + h] << 16);
+    }
+
+  // DMA: wave w moves kIdxDma KiB of each block; a KiB holds 4 rows, lane l
+  // row (l / 16) of them, chunk slot l % 16, which holds source chunk
+  // slot ^ swizzle(row)
+  const uint32_t rbytes = (uint32_t)(total_rows * kIdxRowB);
+  const u32x4 wk = buffer_words(k, rbytes);
+  const u32x4 wv = buffer_words(v, rbytes);
+  int dma_lds[kIdxDma], dma_src[kIdxDma], dma_mat[kIdxDma];
+#pragma unroll
+  for (int i = 0; i < kIdxDma; ++i) {
+    const int kib = wave * kIdxDma + i;   // 0..15: K rows 0..31 in KiB 0..7, V rows in 8..15
+    const int mat = kib >= 8 ? 1 : 0;
+    const int r = 4 * (kib & 7) + lane / 16;
+    dma_mat[i] = mat;
+    dma_lds[i] = kib * 1024;
+    dma_src[i] = r * kIdxRowB + 16 * ((lane & 15) ^ idx_swz(r));
+  }
+  unsigned dma_off[kIdxDma];
+  auto stage_block = [&](long long blk, int st) {
+    const unsigned base = (unsigned)(blk * kIdxRows * kIdxRowB);  // past the end: out of range, zeros
+#pragma unroll
+    for (int i = 0; i < kIdxDma; ++i) {
+      const unsigned off = blk * kIdxRows < total_rows ? base + (unsigned)dma_src[i] : rbytes;
+      dma16(dma_mat[i] ? wv : wk, (uint32_t)(uintptr_t)(xbase + st * kIdxStageB + dma_lds[i]), off);
+      dma_off[i] = off;
     }
   };
+  // B operand (k-step s) of block stage st: position ql, chunk 2s' + half
+  int boff[kIdxKS / 2];
+#pragma unroll
+  for (int s = 0; s < kIdxKS / 2; ++s) boff[s] = ql * kIdxRowB + 16 * ((2 * s + half) ^ idx_swz(ql));
 
-  u32x4 cur[kIdxKS];
-  if (r0 < total_rows) load_rows(r0, cur);
-  for (; r0 < total_rows; r0 += step) {
-    u32x4 nxt[kIdxKS];
-    const bool more = r0 + step < total_rows;
-    if (more) load_rows(r0 + step, nxt);
-    f32x16 acc[kIdxHT];
+  const long long nblk = (total_rows + kIdxRows - 1) / kIdxRows;
+  const long long first = blockIdx.x, stride = gridDim.x;
+  if (first >= nblk) return;
+  const long long mine = (nblk - first + stride - 1) / stride;  // blocks of this workgroup
+  for (int j = 0; j < kIdxNst - 1; ++j) stage_block(first + j * stride < nblk ? first + j * stride : nblk, j);
+
+  for (long long it = 0; it <= mine; ++it) {
+    // this wave's loads of block `it` have landed once at most the newer
+    // kIdxNst-2 blocks' are in flight; the barrier completes the block for
+    // all waves and frees the stage the load below refills
+    if (it < mine) __builtin_amdgcn_s_waitcnt(0x0F70 | (kIdxDma * (kIdxNst - 2)));
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    // partial sums of the previous block -> logits
+    if (it > 0 && wave == 0 && half == 0) {
+      const long long row = (first + (it - 1) * stride) * kIdxRows + ql;
+      const int par = (int)((it - 1) & 1);
+      const float2 a0 = red[par][0][ql], a1 = red[par][1][ql], a2 = red[par][2][ql], a3 = red[par][3][ql];
+      if (row < total_rows) {
+        vlog[row] = (a0.x + a1.x) + (a2.x + a3.x);
+        slog[row] = (a0.y + a1.y) + (a2.y + a3.y);
+      }
+    }
+    if (it == mine) break;
+    {
+      const long long nb = first + (it + kIdxNst - 1) * stride;
+      stage_block(nb < nblk ? nb : nblk, (int)((it + kIdxNst - 1) % kIdxNst));
 #pragma unroll
-    for (int t = 0; t < kIdxHT; ++t)
+      for (int i = 0; i < kIdxDma; ++i) asm volatile("" ::"v"(dma_off[i]));
+    }
+    const int st = (int)(it % kIdxNst);
+    const lds_u8* xb = xbase + st * kIdxStageB;
+    f32x16 acc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
     for (int s = 0; s < kIdxKS; ++s) {
-      const bf16x8 b = as_bf16x8(cur[s]);
-#pragma unroll
-      for (int t = 0; t < kIdxHT; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&w1_lds[(32 * t + ql) * kIdxRow + 16 * s + 8 * half]);
-        acc[t] = mfma32(a, b, acc[t]);
-      }
+      const int m = s / (kIdxKS / 2), ss = s % (kIdxKS / 2);
+      const bf16x8 b = *(const __attribute__((address_space(3))) bf16x8*)(xb + m * kIdxRows * kIdxRowB + boff[ss]);
+      acc = mfma32(wa[s], b, acc);
     }
-    // second layer: this lane holds hidden units 32t + 8a + 4*half + 0..3
     float pv = 0.f, ps = 0.f;
 #pragma unroll
-    for (int t = 0; t < kIdxHT; ++t)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int h0 = 32 * t + 8 * a + 4 * half;
-        const float4 wa = *reinterpret_cast<const float4*>(&w2_lds[2 * h0]);
-        const float4 wb = *reinterpret_cast<const float4*>(&w2_lds[2 * h0 + 4]);
-        const float x0 = fmaxf(acc[t][4 * a + 0], 0.f), x1 = fmaxf(acc[t][4 * a + 1], 0.f);
-        const float x2 = fmaxf(acc[t][4 * a + 2], 0.f), x3 = fmaxf(acc[t][4 * a + 3], 0.f);
-        pv = fmaf(x0, wa.x, pv);
-        ps = fmaf(x0, wa.y, ps);
-        pv = fmaf(x1, wa.z, pv);
-        ps = fmaf(x1, wa.w, ps);
-        pv = fmaf(x2, wb.x, pv);
-        ps = fmaf(x2, wb.y, ps);
-        pv = fmaf(x3, wb.z, pv);
-        ps = fmaf(x3, wb.w, ps);
-      }
+    for (int e = 0; e < 16; ++e) {
+      const float x = fmaxf(acc[e], 0.f);
+      pv = fmaf(x, w2v[e], pv);
+      ps = fmaf(x, w2s[e], ps);
+    }
     pv += swap_halves(pv);
     ps += swap_halves(ps);
-    const long long row = r0 + ql;
-    if (half == 0 && row < total_rows) {
-      vlog[row] = pv;
-      slog[row] = ps;
-    }
-    if (more) {
-#pragma unroll
-      for (int s = 0; s < kIdxKS; ++s) cur[s] = nxt[s];
-    }
+    if (half == 0) red[it & 1][wave][ql] = float2{pv, ps};
   }
 }
 
@@ -134,9 +168,9 @@ hipError_t launch_index(const void* k, const void* v, int h_kv, int n, const voi
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
       cus = c;
   }
-  const long long want = (total + 127) / 128;
-  const long long grid = want < 2LL * cus ? want : 2LL * cus;
-  hipLaunchKernelGGL(index_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+  const long long blocks = (total + kIdxRows - 1) / kIdxRows;
+  const long long grid = blocks < 2LL * cus ? blocks : 2LL * cus;
+  hipLaunchKernelGGL(index_kernel, dim3((unsigned)grid), dim3(kIdxThreads), 0, stream,
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w2), vlog,
                      slog, total);
