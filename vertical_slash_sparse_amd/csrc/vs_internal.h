@@ -39,15 +39,23 @@ struct AttnWsLayout {
   }
 };
 
-// Device workspace of vs_select.
+constexpr int kSelChunk = 4096;  // candidates per selection workgroup
+
+// Device workspace of vs_select: per-candidate keys and masses, per-head
+// decision state, two digit histograms per head, and per-chunk counts.
 struct SelectWsLayout {
-  size_t off_key, off_mass, total;
+  int chunks;  // workgroups per head
+  size_t off_key, off_mass, off_state, off_hcnt, off_hmass, off_cc, total;
   SelectWsLayout(int heads, int n) {
+    chunks = (n + kSelChunk - 1) / kSelChunk;
     size_t o = 0;
-    off_key = o;
-    o = align_up(o + sizeof(uint32_t) * (size_t)heads * n, 256);
-    off_mass = o;
-    o = align_up(o + sizeof(uint64_t) * (size_t)heads * n, 256);
+    auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+    off_key = take(sizeof(uint32_t) * (size_t)heads * n);
+    off_mass = take(sizeof(uint64_t) * (size_t)heads * n);
+    off_state = take(sizeof(uint64_t) * 16 * (size_t)heads);
+    off_hcnt = take(sizeof(uint32_t) * 2 * 256 * (size_t)heads);
+    off_hmass = take(sizeof(uint64_t) * 2 * 256 * (size_t)heads);
+    off_cc = take(sizeof(int32_t) * 4 * (size_t)heads * chunks);
     total = o;
   }
 };

@@ -19,7 +19,13 @@
 //      mass reaches T or whose running count reaches cap.
 //   4. Equal scores have equal u, so the number r of tied elements needed is
 //      a division; they are the r lowest indices of the tie.
-//   5. One ordered compaction pass writes the chosen candidates ascending.
+//   5. An ordered compaction writes the chosen candidates ascending.
+// Every pass over the candidates is spread over workgroups of kSelChunk
+// candidates (a few hundred workgroups at n = 128K), joined by integer
+// atomics in the workspace and a one-block decision per head between passes;
+// integer sums are order-free, so the result does not depend on scheduling.
+// The launches form a fixed chain of nine kernels plus two per digit pass
+// (at most four); passes the key range does not need return at once.
 // The mass arithmetic follows a fixed specification so the budget is an
 // exact integer decision: exp is Cody and Waite's range reduction with a
 // two-piece ln 2 (W. J. Cody, W. Waite, 1980) and the degree-7 Taylor
@@ -33,8 +39,26 @@ namespace vs {
 
 namespace {
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kMaxPasses = 4;
+
+// per-head decision state (unsigned 64-bit words in the workspace)
+enum : int {
+  kStMaxKey = 0,   // order key of the maximum score
+  kStKmin,         // smallest candidate key
+  kStU,            // sum of quantised masses
+  kStCand,         // number of candidates
+  kStT,            // mass target
+  kStPasses,       // digit passes needed
+  kStPrefix,       // digits of (key - kmin) fixed so far
+  kStMassAbove,    // mass of candidates strictly above the current bucket
+  kStCntAbove,     // their number
+  kStBucketCnt,    // candidates in the bucket holding the K-th
+  kStBucketMass,   // their mass
+  kStR,            // ties taken
+  kStK             // budget
+};
 
 __device__ __forceinline__ float spec_exp(float x) {
   const float log2e = 0x1.715476p+0f;
@@ -65,6 +89,9 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   const uint32_t b = __float_as_uint(s == 0.0f ? 0.0f : s);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
 
 __device__ __forceinline__ float load_score(const float* row, int n, int kind, int c) {
   return kind == 0 ? row[c] : row[n - 1 - c];
@@ -75,6 +102,19 @@ __device__ T wave_reduce(T x, Op op) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = op(x, __shfl_xor(x, o, 64));
   return x;
+}
+
+// block-wide reduction through `sh` (kSelWaves slots); every thread gets it
+template <typename T, typename Op>
+__device__ T block_reduce(T x, Op op, T* sh) {
+  x = wave_reduce(x, op);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+  __syncthreads();
+  T r = sh[0];
+#pragma unroll
+  for (int w = 1; w < kSelWaves; ++w) r = op(r, sh[w]);
+  __syncthreads();
+  return r;
 }
 
 // exclusive count of `flag` over the block in thread order, plus the total
@@ -96,163 +136,219 @@ __device__ int block_count(bool flag, int* total, int* sh) {
   return before + below;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ logit, int n,
-                                                             int kind, double mass, int cap,
-                                                             int32_t* __restrict__ idx,
-                                                             int32_t* __restrict__ count,
-                                                             uint32_t* __restrict__ key_ws,
-                                                             uint64_t* __restrict__ mass_ws) {
-  __shared__ float shf[kSelWaves];
+struct SelArgs {
+  const float* logit;
+  int n, kind, cap, chunks;
+  double mass;
+  int32_t* idx;
+  int32_t* count;
+  uint32_t* key;
+  uint64_t* um;
+  unsigned long long* state;  // [heads][16]
+  uint32_t* hcnt;             // [heads][2][256]
+  unsigned long long* hmass;  // [heads][2][256]
+  int32_t* cc;                // [heads][chunks][4]: strict, ties, strict before, ties before
+};
+
+__global__ __launch_bounds__(kSelThreads) void sel_init_kernel(SelArgs a) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  unsigned long long* st = a.state + 16 * (size_t)h;
+  if (tid < 16) st[tid] = tid == kStKmin ? 0xffffffffull : 0ull;
+  for (int i = tid; i < 512; i += kSelThreads) {
+    a.hcnt[512 * (size_t)h + i] = 0u;
+    a.hmass[512 * (size_t)h + i] = 0ull;
+  }
+}
+
+// 1a. maximum score, as its order key
+__global__ __launch_bounds__(kSelThreads) void sel_max_kernel(SelArgs a) {
+  __shared__ uint32_t sh[kSelWaves];
+  const int h = blockIdx.y, c0 = blockIdx.x * kSelChunk;
+  const float* row = a.logit + (size_t)h * a.n;
+  uint32_t km = 0u;
+  for (int c = c0 + threadIdx.x; c < min(c0 + kSelChunk, a.n); c += kSelThreads)
+    km = max(km, order_key(load_score(row, a.n, a.kind, c)));
+  km = block_reduce(km, [](uint32_t x, uint32_t y) { return max(x, y); }, sh);
+  if (threadIdx.x == 0) atomicMax(&a.state[16 * (size_t)h + kStMaxKey], (unsigned long long)km);
+}
+
+// 1b. quantised masses, keys, U, candidate count and the smallest candidate key
+__global__ __launch_bounds__(kSelThreads) void sel_mass_kernel(SelArgs a) {
   __shared__ unsigned long long shu[kSelWaves];
   __shared__ uint32_t shk[kSelWaves];
-  __shared__ int shc[kSelWaves + 1];
-  __shared__ uint32_t hcnt[256];
-  __shared__ unsigned long long hmass[256];
-  __shared__ unsigned long long sel_state[4];  // prefix, mass_above, cnt_above, bucket
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int h = blockIdx.x;
-  const float* row = logit + (size_t)h * n;
-  uint32_t* key = key_ws + (size_t)h * n;
-  uint64_t* um = mass_ws + (size_t)h * n;
-
-  // 1a. maximum score
-  float mx = -__builtin_inff();
-  for (int c = tid; c < n; c += kSelThreads) mx = fmaxf(mx, load_score(row, n, kind, c));
-  mx = wave_reduce(mx, [](float a, float b) { return fmaxf(a, b); });
-  if (lane == 0) shf[wv] = mx;
-  __syncthreads();
-  mx = shf[0];
-  for (int w = 1; w < kSelWaves; ++w) mx = fmaxf(mx, shf[w]);
-  if (mx == 0.0f) mx = 0.0f;
-
-  // 1b. quantised masses, keys, U and the smallest candidate key
-  unsigned long long usum = 0;
+  const int h = blockIdx.y, c0 = blockIdx.x * kSelChunk;
+  const float* row = a.logit + (size_t)h * a.n;
+  unsigned long long* st = a.state + 16 * (size_t)h;
+  const float mx = key_score((uint32_t)st[kStMaxKey]);
+  unsigned long long usum = 0, ncand = 0;
   uint32_t kmin = 0xffffffffu;
-  for (int c = tid; c < n; c += kSelThreads) {
-    float s = load_score(row, n, kind, c);
+  for (int c = c0 + threadIdx.x; c < min(c0 + kSelChunk, a.n); c += kSelThreads) {
+    float s = load_score(row, a.n, a.kind, c);
     if (s == 0.0f) s = 0.0f;
     const float x = s - mx;
     const bool cand = x >= -32.0f;
     const uint64_t u = spec_mass(x);
     const uint32_t k = order_key(s);
-    key[c] = cand ? k : 0u;
-    um[c] = u;
+    a.key[(size_t)h * a.n + c] = cand ? k : 0u;
+    a.um[(size_t)h * a.n + c] = u;
     usum += u;
+    ncand += cand ? 1ull : 0ull;
     if (cand) kmin = min(kmin, k);
   }
-  usum = wave_reduce(usum, [](unsigned long long a, unsigned long long b) { return a + b; });
-  kmin = wave_reduce(kmin, [](uint32_t a, uint32_t b) { return min(a, b); });
-  if (lane == 0) {
-    shu[wv] = usum;
-    shk[wv] = kmin;
+  usum = block_reduce(usum, [](unsigned long long x, unsigned long long y) { return x + y; }, shu);
+  ncand = block_reduce(ncand, [](unsigned long long x, unsigned long long y) { return x + y; }, shu);
+  kmin = block_reduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); }, shk);
+  if (threadIdx.x == 0) {
+    atomicAdd(&st[kStU], usum);
+    atomicAdd(&st[kStCand], ncand);
+    atomicMin(&st[kStKmin], (unsigned long long)kmin);
   }
-  __syncthreads();
-  unsigned long long U = 0;
-  kmin = 0xffffffffu;
-  for (int w = 0; w < kSelWaves; ++w) {
-    U += shu[w];
-    kmin = min(kmin, shk[w]);
-  }
-  const uint32_t kmax = order_key(mx);
-  const unsigned long long T = (unsigned long long)__builtin_ceil(mass * (double)U);
+}
 
-  // 2-3. radix select over rel = key - kmin of candidates
+// 1c. the target and the digit passes the candidates' key range needs
+__global__ void sel_prep_kernel(SelArgs a) {
+  const int h = blockIdx.x;
+  unsigned long long* st = a.state + 16 * (size_t)h;
+  if (threadIdx.x != 0) return;
+  const unsigned long long U = st[kStU];
+  st[kStT] = (unsigned long long)__builtin_ceil(a.mass * (double)U);
+  const uint32_t kmin = (uint32_t)st[kStKmin], kmax = (uint32_t)st[kStMaxKey];
   const uint32_t range = kmax - kmin;
   const int nbits = range ? 32 - __builtin_clz(range) : 0;
   const int npass = (nbits + 7) / 8;
-  uint64_t prefix = 0;  // determined bits of rel
-  unsigned long long mass_above = 0, cnt_above = 0;
-  unsigned long long bucket_cnt = 0, bucket_mass = 0;
-  if (npass == 0) {
-    // every candidate has the same score
-    int tot;
-    int dummy = 0;
-    for (int base = 0; base < n; base += kSelThreads) {
-      const int c = base + tid;
-      dummy += (c < n && key[c] >= kmin && key[c] != 0u) ? 1 : 0;
-    }
-    dummy = wave_reduce(dummy, [](int a, int b) { return a + b; });
-    if (lane == 0) shc[wv] = dummy;
-    __syncthreads();
-    tot = 0;
-    for (int w = 0; w < kSelWaves; ++w) tot += shc[w];
-    __syncthreads();
-    bucket_cnt = (unsigned long long)tot;
-    bucket_mass = U;
-  }
-  for (int pass = 0; pass < npass; ++pass) {
-    const int shift = 8 * (npass - 1 - pass);
-    for (int i = tid; i < 256; i += kSelThreads) {
-      hcnt[i] = 0u;
-      hmass[i] = 0ull;
-    }
-    __syncthreads();
-    const uint64_t hi_mask = ~((1ull << (shift + 8)) - 1ull);
-    for (int c = tid; c < n; c += kSelThreads) {
-      const uint32_t k = key[c];
-      if (k < kmin || k == 0u) continue;
-      const uint64_t rel = (uint64_t)(k - kmin);
-      if ((rel & hi_mask) != (prefix & hi_mask)) continue;
-      const int dg = (int)((rel >> shift) & 255u);
-      atomicAdd(&hcnt[dg], 1u);
-      atomicAdd(&hmass[dg], (unsigned long long)um[c]);
-    }
-    __syncthreads();
-    if (wv == 0) {
-      // lane l owns digits 255-4l .. 252-4l (descending)
-      unsigned long long lc = 0, lm = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        lc += hcnt[255 - 4 * lane - q];
-        lm += hmass[255 - 4 * lane - q];
-      }
-      // inclusive scan over lanes
-      unsigned long long sc = lc, sm = lm;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long yc = __shfl_up(sc, o, 64), ym = __shfl_up(sm, o, 64);
-        if (lane >= o) {
-          sc += yc;
-          sm += ym;
-        }
-      }
-      const unsigned long long ec = sc - lc, em = sm - lm;  // exclusive, before this lane
-      const bool hit = (mass_above + sm >= T) || (cnt_above + sc >= (unsigned long long)cap);
-      const uint64_t hb = __builtin_amdgcn_ballot_w64(hit);
-      const int first = hb ? __builtin_ctzll(hb) : 63;
-      if (lane == first) {
-        unsigned long long rc = ec, rm = em;
-        int dsel = 255 - 4 * lane - 3;
-        for (int q = 0; q < 4; ++q) {
-          const int dg = 255 - 4 * lane - q;
-          const unsigned long long bc = hcnt[dg], bm = hmass[dg];
-          if (mass_above + rm + bm >= T || cnt_above + rc + bc >= (unsigned long long)cap) {
-            dsel = dg;
-            break;
-          }
-          rc += bc;
-          rm += bm;
-        }
-        sel_state[0] = prefix | ((uint64_t)dsel << shift);
-        sel_state[1] = mass_above + rm;
-        sel_state[2] = cnt_above + rc;
-        sel_state[3] = (unsigned long long)dsel;
-      }
-    }
-    __syncthreads();
-    prefix = sel_state[0];
-    mass_above = sel_state[1];
-    cnt_above = sel_state[2];
-    const int dsel = (int)sel_state[3];
-    bucket_cnt = hcnt[dsel];
-    bucket_mass = hmass[dsel];
-    __syncthreads();
-  }
-  const uint32_t kstar = kmin + (uint32_t)prefix;
+  st[kStPasses] = (unsigned long long)npass;
+  st[kStPrefix] = 0ull;
+  st[kStMassAbove] = 0ull;
+  st[kStCntAbove] = 0ull;
+  // with one distinct candidate score every candidate is a tie at kmin
+  st[kStBucketCnt] = npass == 0 ? st[kStCand] : 0ull;
+  st[kStBucketMass] = npass == 0 ? U : 0ull;
+}
 
-  // 4. how many of the tied elements are needed
-  unsigned long long r = (unsigned long long)cap - cnt_above;
+// 2-3a. digit histogram (counts and masses) of the candidates that match
+//       the fixed digits
+__global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(SelArgs a, int pass) {
+  __shared__ uint32_t lc[256];
+  __shared__ unsigned long long lm[256];
+  const int h = blockIdx.y, c0 = blockIdx.x * kSelChunk;
+  const unsigned long long* st = a.state + 16 * (size_t)h;
+  const int npass = (int)st[kStPasses];
+  if (pass >= npass) return;
+  const int shift = 8 * (npass - 1 - pass);
+  const uint32_t kmin = (uint32_t)st[kStKmin];
+  const uint64_t prefix = st[kStPrefix];
+  const uint64_t hi_mask = ~((1ull << (shift + 8)) - 1ull);
+  for (int i = threadIdx.x; i < 256; i += kSelThreads) {
+    lc[i] = 0u;
+    lm[i] = 0ull;
+  }
+  __syncthreads();
+  for (int c = c0 + threadIdx.x; c < min(c0 + kSelChunk, a.n); c += kSelThreads) {
+    const uint32_t k = a.key[(size_t)h * a.n + c];
+    if (k < kmin || k == 0u) continue;
+    const uint64_t rel = (uint64_t)(k - kmin);
+    if ((rel & hi_mask) != (prefix & hi_mask)) continue;
+    const int dg = (int)((rel >> shift) & 255u);
+    atomicAdd(&lc[dg], 1u);
+    atomicAdd(&lm[dg], (unsigned long long)a.um[(size_t)h * a.n + c]);
+  }
+  __syncthreads();
+  const int par = pass & 1;
+  for (int i = threadIdx.x; i < 256; i += kSelThreads)
+    if (lc[i]) {
+      atomicAdd(&a.hcnt[(512 * (size_t)h) + 256 * par + i], lc[i]);
+      atomicAdd(&a.hmass[(512 * (size_t)h) + 256 * par + i], lm[i]);
+    }
+}
+
+// 2-3b. the bucket holding the K-th candidate; clears the other histogram
+__global__ __launch_bounds__(64) void sel_decide_kernel(SelArgs a, int pass) {
+  const int h = blockIdx.x, lane = threadIdx.x;
+  unsigned long long* st = a.state + 16 * (size_t)h;
+  const int npass = (int)st[kStPasses];
+  if (pass >= npass) return;
+  const int shift = 8 * (npass - 1 - pass);
+  const int par = pass & 1;
+  const uint32_t* hc = a.hcnt + 512 * (size_t)h + 256 * par;
+  const unsigned long long* hm = a.hmass + 512 * (size_t)h + 256 * par;
+  const unsigned long long T = st[kStT], cap = (unsigned long long)a.cap;
+  const unsigned long long mass_above = st[kStMassAbove], cnt_above = st[kStCntAbove];
+  const uint64_t prefix = st[kStPrefix];
+  // lane l owns digits 255-4l .. 252-4l (descending)
+  unsigned long long lc = 0, lm = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    lc += hc[255 - 4 * lane - q];
+    lm += hm[255 - 4 * lane - q];
+  }
+  unsigned long long sc = lc, sm = lm;  // inclusive scan over lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long yc = __shfl_up(sc, o, 64), ym = __shfl_up(sm, o, 64);
+    if (lane >= o) {
+      sc += yc;
+      sm += ym;
+    }
+  }
+  const unsigned long long ec = sc - lc, em = sm - lm;  // before this lane
+  const bool hit = (mass_above + sm >= T) || (cnt_above + sc >= cap);
+  const uint64_t hb = __builtin_amdgcn_ballot_w64(hit);
+  const int first = hb ? __builtin_ctzll(hb) : 63;
+  if (lane == first) {
+    unsigned long long rc = ec, rm = em;
+    int dsel = 255 - 4 * lane - 3;
+    for (int q = 0; q < 4; ++q) {
+      const int dg = 255 - 4 * lane - q;
+      const unsigned long long bc = hc[dg], bm = hm[dg];
+      if (mass_above + rm + bm >= T || cnt_above + rc + bc >= cap) {
+        dsel = dg;
+        break;
+      }
+      rc += bc;
+      rm += bm;
+    }
+    st[kStPrefix] = prefix | ((uint64_t)dsel << shift);
+    st[kStMassAbove] = mass_above + rm;
+    st[kStCntAbove] = cnt_above + rc;
+    st[kStBucketCnt] = hc[dsel];
+    st[kStBucketMass] = hm[dsel];
+  }
+  // the histogram the next pass fills
+  for (int i = lane; i < 256; i += 64) {
+    a.hcnt[512 * (size_t)h + 256 * (par ^ 1) + i] = 0u;
+    a.hmass[512 * (size_t)h + 256 * (par ^ 1) + i] = 0ull;
+  }
+}
+
+// 4a. per chunk: candidates strictly above the K-th key, and ties with it
+__global__ __launch_bounds__(kSelThreads) void sel_count_kernel(SelArgs a) {
+  __shared__ int sh[kSelWaves];
+  const int h = blockIdx.y, q = blockIdx.x, c0 = q * kSelChunk;
+  const unsigned long long* st = a.state + 16 * (size_t)h;
+  const uint32_t kstar = (uint32_t)st[kStKmin] + (uint32_t)st[kStPrefix];
+  int ns = 0, nt = 0;
+  for (int c = c0 + threadIdx.x; c < min(c0 + kSelChunk, a.n); c += kSelThreads) {
+    const uint32_t k = a.key[(size_t)h * a.n + c];
+    ns += (k != 0u && k > kstar) ? 1 : 0;
+    nt += (k != 0u && k == kstar) ? 1 : 0;
+  }
+  ns = block_reduce(ns, [](int x, int y) { return x + y; }, sh);
+  nt = block_reduce(nt, [](int x, int y) { return x + y; }, sh);
+  if (threadIdx.x == 0) {
+    int32_t* cc = a.cc + 4 * ((size_t)h * a.chunks + q);
+    cc[0] = ns;
+    cc[1] = nt;
+  }
+}
+
+// 4b. ties needed, the budget, and each chunk's place in the output
+__global__ __launch_bounds__(kSelThreads) void sel_scan_kernel(SelArgs a) {
+  __shared__ int sh[kSelWaves + 1];
+  const int h = blockIdx.x;
+  unsigned long long* st = a.state + 16 * (size_t)h;
+  const unsigned long long T = st[kStT], mass_above = st[kStMassAbove], cnt_above = st[kStCntAbove];
+  const unsigned long long bucket_cnt = st[kStBucketCnt], bucket_mass = st[kStBucketMass];
+  unsigned long long r = (unsigned long long)a.cap - cnt_above;
   const unsigned long long ustar = bucket_cnt ? bucket_mass / bucket_cnt : 0ull;
   if (ustar > 0ull) {
     const unsigned long long need = (T - mass_above + ustar - 1ull) / ustar;
@@ -260,26 +356,95 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   }
   r = min(r, bucket_cnt);
   const int K = (int)(cnt_above + r);
+  // running totals over chunks, in chunk order
+  int strict_before = 0, tie_before = 0;
+  for (int q0 = 0; q0 < a.chunks; q0 += kSelThreads) {
+    const int q = q0 + threadIdx.x;
+    int32_t* cc = a.cc + 4 * ((size_t)h * a.chunks + (q < a.chunks ? q : 0));
+    const int ns = q < a.chunks ? cc[0] : 0, nt = q < a.chunks ? cc[1] : 0;
+    int tot_s, tot_t;
+    // exclusive scans via two block counts of unary flags would be wasteful;
+    // a shared-memory scan of the two values
+    int xs = ns, xt = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int ys = __shfl_up(xs, o, 64), yt = __shfl_up(xt, o, 64);
+      if ((threadIdx.x & 63) >= o) {
+        xs += ys;
+        xt += yt;
+      }
+    }
+    __shared__ int ws[kSelWaves], wt[kSelWaves];
+    if ((threadIdx.x & 63) == 63) {
+      ws[threadIdx.x >> 6] = xs;
+      wt[threadIdx.x >> 6] = xt;
+    }
+    __syncthreads();
+    int bs = 0, bt = 0;
+    tot_s = 0;
+    tot_t = 0;
+    for (int w = 0; w < kSelWaves; ++w) {
+      if (w < (threadIdx.x >> 6)) {
+        bs += ws[w];
+        bt += wt[w];
+      }
+      tot_s += ws[w];
+      tot_t += wt[w];
+    }
+    __syncthreads();
+    if (q < a.chunks) {
+      cc[2] = strict_before + bs + xs - ns;
+      cc[3] = tie_before + bt + xt - nt;
+    }
+    strict_before += tot_s;
+    tie_before += tot_t;
+  }
+  (void)sh;
+  if (threadIdx.x == 0) {
+    st[kStR] = r;
+    st[kStK] = (unsigned long long)K;
+    a.count[h] = K;
+  }
+}
 
-  // 5. ordered compaction: strictly better keys, then the r lowest-index ties
-  int32_t* out = idx + (size_t)h * cap;
-  int ties_seen = 0, written = 0;
-  for (int base = 0; base < n; base += kSelThreads) {
-    const int c = base + tid;
-    const uint32_t k = c < n ? key[c] : 0u;
-    const bool strict = c < n && k != 0u && k > kstar;
-    const bool tie = c < n && k != 0u && k == kstar;
+// 5. ordered compaction: strictly better keys, then the r lowest-index ties;
+//    the slots past the budget become -1
+__global__ __launch_bounds__(kSelThreads) void sel_write_kernel(SelArgs a) {
+  __shared__ int sh[kSelWaves];
+  const int h = blockIdx.y, q = blockIdx.x, c0 = q * kSelChunk;
+  const unsigned long long* st = a.state + 16 * (size_t)h;
+  const uint32_t kstar = (uint32_t)st[kStKmin] + (uint32_t)st[kStPrefix];
+  const long long r = (long long)st[kStR];
+  const int K = (int)st[kStK];
+  const int32_t* cc = a.cc + 4 * ((size_t)h * a.chunks + q);
+  const int strict_before = cc[2], tie_before = cc[3];
+  // chosen before this chunk: all strict ones, and the ties among the first r
+  const long long ties_taken_before = min((long long)tie_before, r);
+  int written = strict_before + (int)ties_taken_before;
+  int ties_seen = tie_before;
+  int32_t* out = a.idx + (size_t)h * a.cap;
+  for (int base = c0; base < min(c0 + kSelChunk, a.n); base += kSelThreads) {
+    const int c = base + threadIdx.x;
+    const bool in = c < min(c0 + kSelChunk, a.n);
+    const uint32_t k = in ? a.key[(size_t)h * a.n + c] : 0u;
+    const bool strict = in && k != 0u && k > kstar;
+    const bool tie = in && k != 0u && k == kstar;
     int tie_total;
-    const int tie_rank = ties_seen + block_count(tie, &tie_total, shc);
-    const bool take = strict || (tie && (unsigned long long)tie_rank < r);
+    const int tie_rank = ties_seen + block_count(tie, &tie_total, sh);
+    const bool take = strict || (tie && (long long)tie_rank < r);
     int take_total;
-    const int pos = written + block_count(take, &take_total, shc);
-    if (take && pos < cap) out[pos] = c;
+    const int pos = written + block_count(take, &take_total, sh);
+    if (take && pos < a.cap) out[pos] = c;
     ties_seen += tie_total;
     written += take_total;
   }
-  for (int t = K + tid; t < cap; t += kSelThreads) out[t] = -1;
-  if (tid == 0) count[h] = K;
+  // this chunk's share of the unused slots
+  const int spare = a.cap - K;
+  if (spare > 0) {
+    const int per = (spare + a.chunks - 1) / a.chunks;
+    const int lo = K + q * per, hi = min(K + (q + 1) * per, a.cap);
+    for (int t = lo + threadIdx.x; t < hi; t += kSelThreads) out[t] = -1;
+  }
 }
 
 }  // namespace
@@ -288,9 +453,33 @@ hipError_t launch_select(const float* logit, int heads, int n, int kind, double 
                          int32_t* idx, int32_t* count, void* ws, hipStream_t stream) {
   const SelectWsLayout L(heads, n);
   char* base = static_cast<char*>(ws);
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)heads), dim3(kSelThreads), 0, stream, logit, n,
-                     kind, mass, cap, idx, count, reinterpret_cast<uint32_t*>(base + L.off_key),
-                     reinterpret_cast<uint64_t*>(base + L.off_mass));
+  SelArgs a;
+  a.logit = logit;
+  a.n = n;
+  a.kind = kind;
+  a.cap = cap;
+  a.chunks = L.chunks;
+  a.mass = mass;
+  a.idx = idx;
+  a.count = count;
+  a.key = reinterpret_cast<uint32_t*>(base + L.off_key);
+  a.um = reinterpret_cast<uint64_t*>(base + L.off_mass);
+  a.state = reinterpret_cast<unsigned long long*>(base + L.off_state);
+  a.hcnt = reinterpret_cast<uint32_t*>(base + L.off_hcnt);
+  a.hmass = reinterpret_cast<unsigned long long*>(base + L.off_hmass);
+  a.cc = reinterpret_cast<int32_t*>(base + L.off_cc);
+  const dim3 chunks((unsigned)L.chunks, (unsigned)heads);
+  hipLaunchKernelGGL(sel_init_kernel, dim3((unsigned)heads), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_max_kernel, chunks, dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_mass_kernel, chunks, dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_prep_kernel, dim3((unsigned)heads), dim3(64), 0, stream, a);
+  for (int pass = 0; pass < kMaxPasses; ++pass) {
+    hipLaunchKernelGGL(sel_hist_kernel, chunks, dim3(kSelThreads), 0, stream, a, pass);
+    hipLaunchKernelGGL(sel_decide_kernel, dim3((unsigned)heads), dim3(64), 0, stream, a, pass);
+  }
+  hipLaunchKernelGGL(sel_count_kernel, chunks, dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_scan_kernel, dim3((unsigned)heads), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_write_kernel, chunks, dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }
 
