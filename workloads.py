@@ -53,8 +53,19 @@ def streams(seed: int) -> dict:
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round fp32/fp64 values to bf16 (nearest, ties to even); return uint16 bits."""
-    f = np.ascontiguousarray(x, dtype=np.float32)
+    """Round fp32/fp64 values to bf16 (nearest, ties to even), once; return
+    uint16 bits.  fp64 input passes through fp32 rounded to odd (truncate,
+    then set the last bit when inexact), which keeps the final rounding to
+    bf16 correct because fp32 carries more than two extra bits."""
+    x = np.asarray(x)
+    if x.dtype == np.float64:
+        f = x.astype(np.float32)
+        back = f.astype(np.float64)
+        w = f.view(np.uint32)
+        w = np.where(np.abs(back) > np.abs(x), w - np.uint32(1), w)  # toward zero
+        w = np.where(back != x, w | np.uint32(1), w)
+        f = w.astype(np.uint32).view(np.float32)
+    f = np.ascontiguousarray(f if x.dtype == np.float64 else x, dtype=np.float32)
     u = f.view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return u.astype(np.uint16)
