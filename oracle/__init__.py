@@ -54,6 +54,8 @@ def lib():
         L.vso_index.restype = i32
         L.vso_select.argtypes = [P, i32, i32, i32, f64, i32, P, P, P, P]
         L.vso_select.restype = i32
+        L.vso_select_threshold.argtypes = [P, i32, i32, i32, f64, i32, P, P, P]
+        L.vso_select_threshold.restype = i32
         L.vso_exp_spec.argtypes = [ctypes.c_float]
         L.vso_exp_spec.restype = ctypes.c_float
         L.vso_mass_u.argtypes = [ctypes.c_float]
@@ -151,6 +153,23 @@ def select(logit, kind, mass, cap, return_ut=False):
     if rc:
         raise ValueError("oracle select: invalid arguments")
     return (idx, cnt, U, T) if return_ut else (idx, cnt)
+
+
+def select_threshold(logit, kind, alpha, cap, return_a=False):
+    """Max-based dynamic threshold per head: candidates whose softmax score
+    is at least alpha times the largest, decided on the quantised masses
+    (u >= ceil(alpha * 2^32)), at most cap of them in (score desc, index asc)
+    order.  Returns (idx int32 [heads, cap], count int32 [heads])."""
+    logit = _c(logit, np.float32)
+    heads, n = logit.shape
+    idx = np.empty((heads, cap), dtype=np.int32)
+    cnt = np.empty(heads, dtype=np.int32)
+    A = np.zeros(1, dtype=np.uint64)
+    rc = lib().vso_select_threshold(_ptr(logit), heads, n, int(kind), float(alpha), int(cap),
+                                    _ptr(idx), _ptr(cnt), _ptr(A))
+    if rc:
+        raise ValueError("oracle select_threshold: invalid arguments")
+    return (idx, cnt, int(A[0])) if return_a else (idx, cnt)
 
 
 def exp_spec(x) -> np.ndarray:

@@ -321,6 +321,47 @@ int vso_select(const float* logit, int heads, int n, int kind, double mass, int 
   return 0;
 }
 
+/* Max-based dynamic threshold (FlashPrefill summary, arXiv 2603.06199,
+ * Spanish page, "2. Metodologia, B. Umbralizacion Dinamica Basada en
+ * Maximos"): keep every candidate whose score is at least alpha times the
+ * largest score.  The score is the softmax probability over candidates, so
+ * the test p_c >= alpha * max p is exp(s_c - m) >= alpha; it is decided on
+ * the quantised masses above (the maximum has u = 2^32 exactly): keep when
+ * u_c >= A = ceil(alpha * 2^32).  K = the number kept, then min(K, cap), the
+ * first K in (score descending, candidate ascending) order, written
+ * ascending like vso_select.  Returns 0, or 1 on invalid arguments. */
+int vso_select_threshold(const float* logit, int heads, int n, int kind, double alpha, int cap,
+                         int32_t* idx, int32_t* count, uint64_t* out_A) {
+  if (heads <= 0 || n <= 0 || !(alpha > 0.0 && alpha <= 1.0) || cap < 1 || cap > n) return 1;
+  if (kind != VSO_VERTICAL && kind != VSO_SLASH) return 1;
+  const uint64_t A = (uint64_t)ceil(alpha * 4294967296.0);
+  cand_t* cs = (cand_t*)malloc(sizeof(cand_t) * (size_t)n);
+  int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+  for (int h = 0; h < heads; ++h) {
+    const float* row = logit + (int64_t)h * n;
+    float mx = -INFINITY;
+    for (int c = 0; c < n; ++c) {
+      float s = kind == VSO_VERTICAL ? row[c] : row[n - 1 - c];
+      if (s == 0.0f) s = 0.0f;
+      cs[c].s = s;
+      cs[c].c = c;
+      if (s > mx) mx = s;
+    }
+    int K = 0;
+    for (int c = 0; c < n; ++c) K += vso_mass_u(cs[c].s - mx) >= A ? 1 : 0;
+    if (K > cap) K = cap;
+    qsort(cs, (size_t)n, sizeof(cand_t), cand_cmp);
+    for (int a = 0; a < K; ++a) sel[a] = cs[a].c;
+    qsort(sel, (size_t)K, sizeof(int32_t), int_cmp);
+    for (int a = 0; a < cap; ++a) idx[(int64_t)h * cap + a] = a < K ? sel[a] : -1;
+    count[h] = K;
+  }
+  if (out_A) *out_A = A;
+  free(cs);
+  free(sel);
+  return 0;
+}
+
 int vso_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

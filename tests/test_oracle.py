@@ -389,3 +389,80 @@ def test_slash_reads_score_at_last_row():
     is_, cs = oracle.select(lg, oracle.SLASH, 0.6, n)
     np.testing.assert_array_equal(cv, cs)
     np.testing.assert_array_equal(iv, is_)
+
+
+# ------------------------------------------------- max-based threshold selection
+
+def test_hand_worked_threshold_selection():
+    gold = json.load(open(os.path.join(GOLD, "hand_select_threshold.json")))
+    for case in gold["cases"]:
+        kind = oracle.VERTICAL if case["kind"] == "vertical" else oracle.SLASH
+        logit = np.array([case["logit"]], np.float32)
+        idx, cnt, A = oracle.select_threshold(logit, kind, case["alpha"], case["cap"], return_a=True)
+        assert A == case["A"], case
+        assert int(cnt[0]) == case["count"], case
+        assert list(idx[0, :cnt[0]]) == case["idx"], case
+        assert (idx[0, cnt[0]:] == -1).all()
+
+
+def test_threshold_zipf_closed_form():
+    """Logits -s ln(rank): p_c / max p = rank^-s, so alpha keeps exactly the
+    ranks r <= alpha^(-1/s); alpha sits halfway (in log) between two ranks."""
+    import workloads
+    rng = np.random.default_rng(51)
+    n, s = 20000, 1.1
+    lg = workloads.zipf_logits(rng, 2, n, s)
+    ranks = np.rint(np.exp(-lg.astype(np.float64) / s)).astype(np.int64)
+    for K in (1, 7, 37, 400):
+        alpha = math.sqrt(K * (K + 1.0)) ** -s
+        idx, cnt = oracle.select_threshold(lg, oracle.VERTICAL, alpha, n)
+        assert (cnt == K).all(), (K, cnt)
+        for h in range(2):
+            assert set(idx[h, :K].tolist()) == set(np.nonzero(ranks[h] <= K)[0].tolist())
+        kc = min(K, 5)
+        idx, cnt = oracle.select_threshold(lg, oracle.VERTICAL, alpha, 5)
+        assert (cnt == kc).all()
+        for h in range(2):
+            assert set(idx[h, :kc].tolist()) == set(np.nonzero(ranks[h] <= kc)[0].tolist())
+
+
+def test_threshold_matches_real_arithmetic_bruteforce():
+    """exp(s_c - max) >= alpha in float64, ordered by (score desc, index asc),
+    capped; draws whose margin to the threshold is tiny are skipped."""
+    rng = np.random.default_rng(53)
+    checked = 0
+    for trial in range(400):
+        n = int(rng.integers(1, 30))
+        lg = (rng.standard_normal(n) * 2).astype(np.float32)
+        lg[rng.random(n) < 0.2] = lg[0]          # ties
+        alpha = float(np.exp(rng.uniform(-6, 0)))
+        cap = int(rng.integers(1, n + 1))
+        kind = int(rng.integers(0, 2))
+        score = lg if kind == 0 else lg[::-1]
+        s = [0.0 if float(x) == 0.0 else float(x) for x in score]
+        m = max(s)
+        ratio = [math.exp(x - m) for x in s]
+        if any(abs(r - alpha) <= 1e-5 * alpha for r in ratio):
+            continue
+        kept = sum(r >= alpha for r in ratio)
+        order = sorted(range(n), key=lambda c: (-s[c], c))
+        want = sorted(order[:min(kept, cap)])
+        idx, cnt = oracle.select_threshold(lg[None, :], kind, alpha, cap)
+        assert int(cnt[0]) == len(want) and list(idx[0, :cnt[0]]) == want, (lg, alpha, cap, kind)
+        checked += 1
+    assert checked > 300
+
+
+def test_threshold_special_cases():
+    lg = np.array([[3.0, -2.0, 3.0, 1.0, 3.0]], np.float32)
+    idx, cnt = oracle.select_threshold(lg, oracle.VERTICAL, 1.0, 5)
+    assert list(idx[0, :cnt[0]]) == [0, 2, 4]                  # the tied maxima only
+    idx, cnt = oracle.select_threshold(lg, oracle.VERTICAL, 1e-12, 5)
+    assert int(cnt[0]) == 5                                    # within ln(1e12) = 27.6 of the max
+    far = np.array([[0.0, -40.0, -1.0]], np.float32)
+    idx, cnt = oracle.select_threshold(far, oracle.VERTICAL, 1e-12, 3)
+    assert list(idx[0, :cnt[0]]) == [0, 2]                      # 40 below the max: mass 0
+    with pytest.raises(ValueError):
+        oracle.select_threshold(lg, oracle.VERTICAL, 0.0, 5)
+    with pytest.raises(ValueError):
+        oracle.select_threshold(lg, oracle.VERTICAL, 1.5, 5)
