@@ -144,6 +144,8 @@ def main():
                     choices=["zipf128k", "fixed32k", "indexer128k", "e2e256k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--alpha", type=float, default=0.01,
+                    help="max-based threshold timed by the indexer128k workload")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the timed steps, run a plain fp32 copy-like kernel (out = -in) over "
                          "this many MiB three times, so that hardware byte counters of the same run "
@@ -306,7 +308,23 @@ def bench_indexer(args, w, torch, vsa, workloads):
             ti.append(e[0].elapsed_time(e[1]))
             ts.append(e[1].elapsed_time(e[2]))
     ms_i, ms_s = float(np.mean(ti)), float(np.mean(ts))
+    budgets_v, budgets_s = vc.cpu().numpy(), sc.cpu().numpy()
+    # the max-based threshold mode on the same logits (both kinds)
+    alpha = args.alpha
+    tt = []
+    for it in range(args.warmup + args.steps):
+        e[0].record()
+        vsa.vs_select_threshold(vlog, vsa.VS_VERTICAL, alpha, n, vi, vc, ws)
+        vsa.vs_select_threshold(slog, vsa.VS_SLASH, alpha, n, si, sc, ws)
+        e[1].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            tt.append(e[0].elapsed_time(e[1]))
+    ms_t = float(np.mean(tt))
+    kept_t = {"vertical": vc.cpu().tolist(), "slash": sc.cpu().tolist()}
     bytes_alg = hkv * n * (2 * d * 2) + hkv * n * 8   # read K,V rows; write two fp32 logits
+    # selection, both kinds: read the logits, write the chosen indices and counts
+    sel_bytes = 2 * hkv * n * 4 + 4 * int(budgets_v.sum() + budgets_s.sum()) + 2 * hkv * 4
     flops = hkv * n * (2.0 * 2 * d * w["hidden"] + 2.0 * 2 * w["hidden"])
     gbs = bytes_alg / (ms_i * 1e-3) / 1e9
     res = {
@@ -317,8 +335,10 @@ def bench_indexer(args, w, torch, vsa, workloads):
         "config": {"workload": "indexer128k", "n": n, "h_kv": hkv, "d": d, "hidden": w["hidden"],
                    "mass": w["mass"], "seed": w["seed"]},
         "index_ms": round(ms_i, 4), "select_ms": round(ms_s, 4),
+        "select_gbs": round(sel_bytes / (ms_s * 1e-3) / 1e9, 1),
+        "threshold": {"alpha": alpha, "ms": round(ms_t, 4), "kept": kept_t},
         "index_tflops": round(flops / (ms_i * 1e-3) / 1e12, 3),
-        "budgets": {"vertical": vc.cpu().tolist(), "slash": sc.cpu().tolist()},
+        "budgets": {"vertical": budgets_v.tolist(), "slash": budgets_s.tolist()},
         "roofline": {"bound": "hbm", "kernel": "index_kernel (vs_index)", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": recorded_traffic("indexer128k", INDEX_SOURCES),

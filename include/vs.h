@@ -96,6 +96,19 @@ vs_status vs_select(const float* logit, int heads, int n, vs_kind kind, double m
                     int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
+/* Max-based dynamic threshold (FlashPrefill summary, arXiv 2603.06199, Spanish
+ * page, section 2.B "Umbralizacion Dinamica Basada en Maximos"): per head,
+ * keep every candidate whose softmax score is at least `alpha` times the
+ * largest one, with no sort and no cumulative sum -- at most `cap` of them,
+ * the best first in (score descending, candidate ascending) order.  The test
+ * exp(score - max) >= alpha is decided on the quantised masses defined for
+ * vs_select: keep when u >= ceil(alpha * 2^32) (the maximum has u = 2^32).
+ * Candidates, scores, outputs, workspace and errors as for vs_select;
+ * 0 < alpha <= 1. */
+vs_status vs_select_threshold(const float* logit, int heads, int n, vs_kind kind, double alpha,
+                              int cap, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
 /* -------------------------------------------------------- sparse attention
  * Causal prefill attention restricted to the vertical-slash index set
  * (English page, section 2, "Core Concept: Vertical-Slash Pattern" and

@@ -65,6 +65,12 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert L.vs_select(p, 1, 10, 0, 0.5, 0, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
     assert L.vs_select(p, 1, 10, 7, 0.5, 5, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
     assert L.vs_select(p, 1, 10, 0, 0.5, 5, p, p, p, 8, None) == vsa.VS_ERR_WORKSPACE
+    # vs_select_threshold: alpha in (0, 1], same other checks
+    assert L.vs_select_threshold(p, 1, 10, 0, 0.0, 5, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
+    assert L.vs_select_threshold(p, 1, 10, 0, 1.01, 5, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
+    assert L.vs_select_threshold(None, 1, 10, 0, 0.5, 5, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
+    assert L.vs_select_threshold(p, 1, 10, 0, 0.5, 11, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
+    assert L.vs_select_threshold(p, 1, 10, 0, 0.5, 5, p, p, p, 8, None) == vsa.VS_ERR_WORKSPACE
     # vs_index: shapes
     assert L.vs_index(p, p, 8, 100, 64, 128, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED
     assert L.vs_index(p, p, 8, 100, 128, 64, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED

@@ -149,3 +149,49 @@ def test_zipf128k_layer_sampled():
     rows = sample_rows(np.random.default_rng(11), 32, w["n"], 12)
     ro, rl = oracle.attn(q, k, v, *lists, rows=rows)
     assert_attn_close(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, "zipf128k")
+
+
+THRESH_CASES = [
+    # name, heads, n, alpha, cap
+    ("normal", 8, 131072, 0.01, 131072),
+    ("normal-capped", 8, 131072, 0.001, 1000),
+    ("tight", 4, 50000, 0.5, 50000),
+    ("ties", 3, 10000, 0.3, 10000),
+    ("ties-capped", 3, 10000, 0.05, 77),
+    ("alpha-one", 2, 20000, 1.0, 20000),
+    ("tiny-alpha", 2, 20000, 1e-12, 20000),
+    ("n-one", 5, 1, 0.5, 1),
+]
+
+
+@pytest.mark.parametrize("case", [c + (k,) for c in THRESH_CASES for k in ("vertical", "slash")],
+                         ids=[f"{c[0]}-{k}" for c in THRESH_CASES for k in ("vertical", "slash")])
+def test_select_threshold_bit_exact(case):
+    name, heads, n, alpha, cap, kname = case
+    kind = vsa.VS_VERTICAL if kname == "vertical" else vsa.VS_SLASH
+    _log(f"case: threshold select {case}")
+    rng = np.random.default_rng(zlib.crc32(f"thresh-{name}-{kname}".encode()))
+    if name.startswith("ties"):
+        logit = rng.integers(-3, 1, size=(heads, n)).astype(np.float32) * 0.75
+    else:
+        logit = (rng.standard_normal((heads, n)) * 3).astype(np.float32)
+    gi, gc = vsa.vs_select_threshold(to_dev(logit), kind, alpha, cap)
+    torch.cuda.synchronize()
+    ri, rc = oracle.select_threshold(logit, kind, alpha, cap)
+    _assert_same_selection(gi.cpu().numpy(), gc.cpu().numpy(), ri, rc, f"threshold {case}")
+
+
+def test_select_threshold_zipf_closed_form():
+    """On Zipf(1.1) scores alpha = (K(K+1))^(-s/2) keeps exactly ranks 1..K."""
+    _log("case: threshold zipf")
+    w = workloads.WORKLOADS["zipf128k"]
+    vlog, _ = workloads.zipf_scores("zipf128k")
+    ranks = np.rint(np.exp(-vlog.astype(np.float64) / w["zipf_s"])).astype(np.int64)
+    for K in (3, 50, 3000):
+        alpha = (K * (K + 1.0)) ** (-w["zipf_s"] / 2)
+        gi, gc = vsa.vs_select_threshold(to_dev(vlog), vsa.VS_VERTICAL, alpha, w["n"])
+        torch.cuda.synchronize()
+        gi, gc = gi.cpu().numpy(), gc.cpu().numpy()
+        assert (gc == K).all(), (K, gc)
+        for h in range(vlog.shape[0]):
+            assert set(gi[h, :K].tolist()) == set(np.nonzero(ranks[h] <= K)[0].tolist())

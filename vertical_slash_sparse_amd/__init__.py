@@ -8,6 +8,7 @@ calls raise.
 
     vs_index(k_rope, v, w1, w2)                    -> (vlog, slog)
     vs_select(logit, kind, mass, cap)              -> (idx, count)
+    vs_select_threshold(logit, kind, alpha, cap)   -> (idx, count)
     vs_sparse_attn_prefill(q, k, v, v_idx, v_cnt, s_off, s_cnt, scale=None)
                                                    -> (out, lse)
 """
@@ -26,7 +27,8 @@ VS_OK, VS_ERR_INVALID, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_HIP = range(
 VS_BF16, VS_F32 = 0, 1
 VS_VERTICAL, VS_SLASH = 0, 1
 
-_SYMBOLS = ("vs_index", "vs_select_workspace_bytes", "vs_select", "vs_attn_workspace_bytes",
+_SYMBOLS = ("vs_index", "vs_select_workspace_bytes", "vs_select", "vs_select_threshold",
+            "vs_attn_workspace_bytes",
             "vs_sparse_attn_prefill", "vs_attn_tile_counts", "vs_status_str")
 
 
@@ -53,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.vs_select_workspace_bytes.restype = sz
         L.vs_select.argtypes = [P, i32, i32, i32, f64, i32, P, P, P, sz, P]
         L.vs_select.restype = i32
+        L.vs_select_threshold.argtypes = [P, i32, i32, i32, f64, i32, P, P, P, sz, P]
+        L.vs_select_threshold.restype = i32
         L.vs_attn_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.vs_attn_workspace_bytes.restype = sz
         L.vs_sparse_attn_prefill.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P, i32, P, P,
@@ -128,6 +132,38 @@ def vs_index(k_rope: torch.Tensor, v: torch.Tensor, w1: torch.Tensor, w2: torch.
 
 def vs_select_workspace_bytes(heads: int, n: int) -> int:
     return int(lib().vs_select_workspace_bytes(heads, n))
+
+
+def _select_outputs(fn, logit, cap, idx, count, workspace):
+    _need(logit, "logit", torch.float32, 2)
+    dev = logit.device
+    heads, n = logit.shape
+    idx = torch.empty((heads, cap), dtype=torch.int32, device=dev) if idx is None else idx
+    count = torch.empty((heads,), dtype=torch.int32, device=dev) if count is None else count
+    _need(idx, "idx", torch.int32, 2, dev)
+    _need(count, "count", torch.int32, 1, dev)
+    if idx.shape != (heads, cap) or count.shape != (heads,):
+        raise ValueError(f"{fn}: idx must be [heads, cap] and count [heads]")
+    need = vs_select_workspace_bytes(heads, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    return heads, n, idx, count, workspace
+
+
+def vs_select_threshold(logit: torch.Tensor, kind: int, alpha: float, cap: int,
+                        idx: torch.Tensor | None = None, count: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None):
+    """Max-based dynamic threshold: per head the candidates whose softmax score
+    is at least alpha times the largest, at most cap of them.  logit: fp32
+    [heads, n].  Returns int32 (idx [heads, cap] ascending then -1, count [heads])."""
+    heads, n, idx, count, workspace = _select_outputs("vs_select_threshold", logit, cap, idx, count,
+                                                      workspace)
+    st = lib().vs_select_threshold(_ptr(logit), heads, n, int(kind), float(alpha), int(cap), _ptr(idx),
+                                   _ptr(count), _ptr(workspace), workspace.numel(),
+                                   _stream(logit, stream))
+    _check("vs_select_threshold", st)
+    return idx, count
 
 
 def vs_select(logit: torch.Tensor, kind: int, mass: float, cap: int, idx: torch.Tensor | None = None,

@@ -60,7 +60,20 @@ vs_status vs_select(const float* logit, int heads, int n, vs_kind kind, double m
   if (!(mass > 0.0 && mass <= 1.0)) return VS_ERR_INVALID;
   if (cap < 1 || cap > n) return VS_ERR_INVALID;
   if (ws_bytes < vs_select_workspace_bytes(heads, n)) return VS_ERR_WORKSPACE;
-  return from_hip(launch_select(logit, heads, n, (int)kind, mass, cap, idx, count, ws, stream));
+  return from_hip(launch_select(logit, heads, n, (int)kind, mass, 0ull, cap, idx, count, ws, stream));
+}
+
+vs_status vs_select_threshold(const float* logit, int heads, int n, vs_kind kind, double alpha,
+                              int cap, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (!logit || !idx || !count || !ws) return VS_ERR_INVALID;
+  if (heads <= 0 || n <= 0 || heads > 65535) return VS_ERR_INVALID;
+  if (kind != VS_VERTICAL && kind != VS_SLASH) return VS_ERR_INVALID;
+  if (!(alpha > 0.0 && alpha <= 1.0)) return VS_ERR_INVALID;
+  if (cap < 1 || cap > n) return VS_ERR_INVALID;
+  if (ws_bytes < vs_select_workspace_bytes(heads, n)) return VS_ERR_WORKSPACE;
+  const unsigned long long thresh = (unsigned long long)ceil(alpha * 4294967296.0);
+  return from_hip(launch_select(logit, heads, n, (int)kind, 1.0, thresh, cap, idx, count, ws, stream));
 }
 
 size_t vs_attn_workspace_bytes(int h_kv, int n, int cap_v, int cap_s) {

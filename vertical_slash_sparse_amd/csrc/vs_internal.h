@@ -67,8 +67,11 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
 
 int attn_query_rows_per_block(int group);
 
-hipError_t launch_select(const float* logit, int heads, int n, int kind, double mass, int cap,
-                         int32_t* idx, int32_t* count, void* ws, hipStream_t stream);
+// mass in (0, 1] with thresh == 0: cumulative-mass budget; thresh > 0: keep
+// quantised masses >= thresh (max-based threshold)
+hipError_t launch_select(const float* logit, int heads, int n, int kind, double mass,
+                         unsigned long long thresh, int cap, int32_t* idx, int32_t* count, void* ws,
+                         hipStream_t stream);
 
 hipError_t launch_index(const void* k, const void* v, int h_kv, int n, const void* w1,
                         const void* w2, float* vlog, float* slog, hipStream_t stream);

@@ -24,6 +24,11 @@
 // candidates (a few hundred workgroups at n = 128K), joined by integer
 // atomics in the workspace and a one-block decision per head between passes;
 // integer sums are order-free, so the result does not depend on scheduling.
+// The same chain serves FlashPrefill's max-based dynamic threshold
+// (FlashPrefill summary, Spanish page, section 2.B): keep the candidates whose
+// softmax score is at least alpha times the largest, i.e. u >= ceil(alpha *
+// 2^32) (the maximum has u = 2^32), at most cap of them in the same order;
+// there the budget is that count and no mass target applies.
 // The launches form a fixed chain of nine kernels plus two per digit pass
 // (at most four); passes the key range does not need return at once.
 // The mass arithmetic follows a fixed specification so the budget is an
@@ -57,7 +62,9 @@ enum : int {
   kStBucketCnt,    // candidates in the bucket holding the K-th
   kStBucketMass,   // their mass
   kStR,            // ties taken
-  kStK             // budget
+  kStK,            // budget
+  kStCap,          // candidates the selection may take
+  kStAbove         // candidates at or above the threshold (threshold mode)
 };
 
 __device__ __forceinline__ float spec_exp(float x) {
@@ -140,6 +147,7 @@ struct SelArgs {
   const float* logit;
   int n, kind, cap, chunks;
   double mass;
+  unsigned long long thresh;  // threshold mode: keep u >= thresh; 0 for the mass budget
   int32_t* idx;
   int32_t* count;
   uint32_t* key;
@@ -180,7 +188,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_mass_kernel(SelArgs a) {
   const float* row = a.logit + (size_t)h * a.n;
   unsigned long long* st = a.state + 16 * (size_t)h;
   const float mx = key_score((uint32_t)st[kStMaxKey]);
-  unsigned long long usum = 0, ncand = 0;
+  unsigned long long usum = 0, ncand = 0, nabove = 0;
   uint32_t kmin = 0xffffffffu;
   for (int c = c0 + threadIdx.x; c < min(c0 + kSelChunk, a.n); c += kSelThreads) {
     float s = load_score(row, a.n, a.kind, c);
@@ -193,14 +201,17 @@ __global__ __launch_bounds__(kSelThreads) void sel_mass_kernel(SelArgs a) {
     a.um[(size_t)h * a.n + c] = u;
     usum += u;
     ncand += cand ? 1ull : 0ull;
+    nabove += (a.thresh && u >= a.thresh) ? 1ull : 0ull;
     if (cand) kmin = min(kmin, k);
   }
   usum = block_reduce(usum, [](unsigned long long x, unsigned long long y) { return x + y; }, shu);
   ncand = block_reduce(ncand, [](unsigned long long x, unsigned long long y) { return x + y; }, shu);
+  nabove = block_reduce(nabove, [](unsigned long long x, unsigned long long y) { return x + y; }, shu);
   kmin = block_reduce(kmin, [](uint32_t x, uint32_t y) { return min(x, y); }, shk);
   if (threadIdx.x == 0) {
     atomicAdd(&st[kStU], usum);
     atomicAdd(&st[kStCand], ncand);
+    atomicAdd(&st[kStAbove], nabove);
     atomicMin(&st[kStKmin], (unsigned long long)kmin);
   }
 }
@@ -211,7 +222,15 @@ __global__ void sel_prep_kernel(SelArgs a) {
   unsigned long long* st = a.state + 16 * (size_t)h;
   if (threadIdx.x != 0) return;
   const unsigned long long U = st[kStU];
-  st[kStT] = (unsigned long long)__builtin_ceil(a.mass * (double)U);
+  if (a.thresh) {
+    // threshold mode: the budget is the count at or above the threshold; no
+    // mass target can stop the walk first (T exceeds the total mass)
+    st[kStT] = U + 1ull;
+    st[kStCap] = min((unsigned long long)a.cap, st[kStAbove]);
+  } else {
+    st[kStT] = (unsigned long long)__builtin_ceil(a.mass * (double)U);
+    st[kStCap] = (unsigned long long)a.cap;
+  }
   const uint32_t kmin = (uint32_t)st[kStKmin], kmax = (uint32_t)st[kStMaxKey];
   const uint32_t range = kmax - kmin;
   const int nbits = range ? 32 - __builtin_clz(range) : 0;
@@ -271,7 +290,7 @@ __global__ __launch_bounds__(64) void sel_decide_kernel(SelArgs a, int pass) {
   const int par = pass & 1;
   const uint32_t* hc = a.hcnt + 512 * (size_t)h + 256 * par;
   const unsigned long long* hm = a.hmass + 512 * (size_t)h + 256 * par;
-  const unsigned long long T = st[kStT], cap = (unsigned long long)a.cap;
+  const unsigned long long T = st[kStT], cap = st[kStCap];
   const unsigned long long mass_above = st[kStMassAbove], cnt_above = st[kStCntAbove];
   const uint64_t prefix = st[kStPrefix];
   // lane l owns digits 255-4l .. 252-4l (descending)
@@ -348,7 +367,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_scan_kernel(SelArgs a) {
   unsigned long long* st = a.state + 16 * (size_t)h;
   const unsigned long long T = st[kStT], mass_above = st[kStMassAbove], cnt_above = st[kStCntAbove];
   const unsigned long long bucket_cnt = st[kStBucketCnt], bucket_mass = st[kStBucketMass];
-  unsigned long long r = (unsigned long long)a.cap - cnt_above;
+  unsigned long long r = st[kStCap] - cnt_above;
   const unsigned long long ustar = bucket_cnt ? bucket_mass / bucket_cnt : 0ull;
   if (ustar > 0ull) {
     const unsigned long long need = (T - mass_above + ustar - 1ull) / ustar;
@@ -449,8 +468,9 @@ __global__ __launch_bounds__(kSelThreads) void sel_write_kernel(SelArgs a) {
 
 }  // namespace
 
-hipError_t launch_select(const float* logit, int heads, int n, int kind, double mass, int cap,
-                         int32_t* idx, int32_t* count, void* ws, hipStream_t stream) {
+hipError_t launch_select(const float* logit, int heads, int n, int kind, double mass,
+                         unsigned long long thresh, int cap, int32_t* idx, int32_t* count, void* ws,
+                         hipStream_t stream) {
   const SelectWsLayout L(heads, n);
   char* base = static_cast<char*>(ws);
   SelArgs a;
@@ -460,6 +480,7 @@ hipError_t launch_select(const float* logit, int heads, int n, int kind, double 
   a.cap = cap;
   a.chunks = L.chunks;
   a.mass = mass;
+  a.thresh = thresh;
   a.idx = idx;
   a.count = count;
   a.key = reinterpret_cast<uint32_t*>(base + L.off_key);
