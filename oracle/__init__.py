@@ -56,6 +56,8 @@ def lib():
         L.vso_select.restype = i32
         L.vso_select_threshold.argtypes = [P, i32, i32, i32, f64, i32, P, P, P]
         L.vso_select_threshold.restype = i32
+        L.vso_aggregate.argtypes = [P, P, i32, i32, i32, i32, i32, f64, P, P, i32]
+        L.vso_aggregate.restype = i32
         L.vso_exp_spec.argtypes = [ctypes.c_float]
         L.vso_exp_spec.restype = ctypes.c_float
         L.vso_mass_u.argtypes = [ctypes.c_float]
@@ -153,6 +155,24 @@ def select(logit, kind, mass, cap, return_ut=False):
     if rc:
         raise ValueError("oracle select: invalid arguments")
     return (idx, cnt, U, T) if return_ut else (idx, cnt)
+
+
+def aggregate(q, k, scale=None, nthreads=0):
+    """Full causal attention weights of every query head summed per KV head
+    along key columns (a_v [hkv, n]) and along diagonals i-j (a_s [hkv, n]),
+    fp64, unnormalised."""
+    q, k = _c(q), _c(k)
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    assert k.shape == (hkv, n, d) and q.dtype == k.dtype
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    a_v = np.empty((hkv, n), dtype=np.float64)
+    a_s = np.empty((hkv, n), dtype=np.float64)
+    rc = lib().vso_aggregate(_ptr(q), _ptr(k), _dtype_code(q), hq, hkv, n, d, scale, _ptr(a_v),
+                             _ptr(a_s), int(nthreads))
+    if rc:
+        raise ValueError("oracle aggregate: invalid arguments")
+    return a_v, a_s
 
 
 def select_threshold(logit, kind, alpha, cap, return_a=False):

@@ -175,6 +175,71 @@ int vso_attn_rows(const void* q, const void* k, const void* v, int dtype, int hq
   return err;
 }
 
+/* ------------------------------------------------- vertical/slash aggregation */
+
+/* Ground truth for the indexer's distillation (VSPrefill summaries: English
+ * page, section 2, "Key Components, 2. Distillation Training, Ground Truth
+ * Generation"; German page, 2.B.2): full causal attention weights summed
+ * along key columns and along diagonals.  For every query head h of KV head
+ * g and every row i, P_ij = softmax_j(scale q_i . k_j) over j <= i (fp64, two
+ * passes); a_v[g][j] += P_ij and a_s[g][i-j] += P_ij.  Sums over the group's
+ * query heads and all rows, unnormalised (each of a_v[g], a_s[g] totals
+ * G * n).  Rows are spread over threads, each with private sums that are
+ * added at the end.  Returns 0, or 1 on invalid arguments. */
+int vso_aggregate(const void* q, const void* k, int dtype, int hq, int hkv, int n, int d,
+                  double scale, double* a_v, double* a_s, int nthreads) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || n <= 0 || d <= 0) return 1;
+  const int group = hq / hkv;
+  const size_t cells = (size_t)hkv * (size_t)n;
+  for (size_t t = 0; t < cells; ++t) a_v[t] = a_s[t] = 0.0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double* pv = (double*)calloc(cells, sizeof(double));
+    double* ps = (double*)calloc(cells, sizeof(double));
+    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    double* qi = (double*)malloc(sizeof(double) * (size_t)d);
+    double* kj = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < (int64_t)hq * n; ++r) {
+      const int h = (int)(r / n), i = (int)(r % n), g = h / group;
+      load_row(q, dtype, ((int64_t)h * n + i) * d, d, qi);
+      double mx = -INFINITY;
+      for (int j = 0; j <= i; ++j) {
+        load_row(k, dtype, ((int64_t)g * n + j) * d, d, kj);
+        double dot = 0.0;
+        for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];
+        s[j] = scale * dot;
+        if (s[j] > mx) mx = s[j];
+      }
+      double l = 0.0;
+      for (int j = 0; j <= i; ++j) l += exp(s[j] - mx);
+      for (int j = 0; j <= i; ++j) {
+        const double pij = exp(s[j] - mx) / l;
+        pv[(size_t)g * n + j] += pij;
+        ps[(size_t)g * n + (i - j)] += pij;
+      }
+    }
+#pragma omp critical
+    {
+      for (size_t t = 0; t < cells; ++t) {
+        a_v[t] += pv[t];
+        a_s[t] += ps[t];
+      }
+    }
+    free(pv);
+    free(ps);
+    free(s);
+    free(qi);
+    free(kj);
+  }
+  return 0;
+}
+
 /* ---------------------------------------------------------------- the indexer */
 
 /* Per KV head g and position j: x = [k_j | v_j] (2d values), h = max(0, W1 x)

@@ -466,3 +466,67 @@ def test_threshold_special_cases():
         oracle.select_threshold(lg, oracle.VERTICAL, 0.0, 5)
     with pytest.raises(ValueError):
         oracle.select_threshold(lg, oracle.VERTICAL, 1.5, 5)
+
+
+# -------------------------------------------- vertical/slash ground-truth sums
+
+def _explicit_aggregate(q, k, scale):
+    """Whole P matrices in numpy (float64), then column and diagonal sums."""
+    hq, n, _ = q.shape
+    hkv = k.shape[0]
+    G = hq // hkv
+    a_v = np.zeros((hkv, n))
+    a_s = np.zeros((hkv, n))
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    for h in range(hq):
+        g = h // G
+        s = scale * (q[h] @ k[g].T)
+        s = np.where(causal, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        a_v[g] += p.sum(axis=0)
+        for o in range(n):
+            a_s[g, o] += np.diagonal(p, offset=-o).sum()
+    return a_v, a_s
+
+
+@pytest.mark.parametrize("hq,hkv,n,d", [(1, 1, 1, 8), (2, 1, 17, 16), (4, 2, 64, 32), (8, 2, 50, 64)])
+def test_aggregate_matches_explicit_matrices(hq, hkv, n, d):
+    rng = np.random.default_rng(hq * 100 + n)
+    q = rng.standard_normal((hq, n, d))
+    k = rng.standard_normal((hkv, n, d))
+    scale = 1.0 / math.sqrt(d)
+    a_v, a_s = oracle.aggregate(q, k, scale)
+    e_v, e_s = _explicit_aggregate(q, k, scale)
+    np.testing.assert_allclose(a_v, e_v, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a_s, e_s, rtol=1e-12, atol=1e-12)
+
+
+def test_aggregate_row_sums_and_uniform_closed_form():
+    """Rows of P sum to 1, so each sum totals G*n; with Q = 0 every row is
+    uniform over j <= i, so a_v[j] = a_s[j] = G * (H_n - H_j)."""
+    rng = np.random.default_rng(61)
+    hq, hkv, n, d = 8, 2, 300, 32
+    q = rng.standard_normal((hq, n, d))
+    k = rng.standard_normal((hkv, n, d))
+    a_v, a_s = oracle.aggregate(q, k)
+    np.testing.assert_allclose(a_v.sum(axis=1), 4 * n, rtol=1e-12)
+    np.testing.assert_allclose(a_s.sum(axis=1), 4 * n, rtol=1e-12)
+    a_v, a_s = oracle.aggregate(np.zeros_like(q), k)
+    H = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+    want = 4 * (H[n] - H[:n])
+    for g in range(hkv):
+        np.testing.assert_allclose(a_v[g], want, rtol=1e-12)
+        np.testing.assert_allclose(a_s[g], want, rtol=1e-12)
+
+
+def test_aggregate_diagonal_attention():
+    """Keys equal to their queries times a large factor: each row attends to
+    itself, so all mass sits on offset 0 and on the row's own column."""
+    rng = np.random.default_rng(62)
+    hq, hkv, n, d = 1, 1, 40, 64
+    x = rng.standard_normal((1, n, d))
+    x /= np.linalg.norm(x, axis=2, keepdims=True)
+    a_v, a_s = oracle.aggregate(x * 30.0, x * 30.0, scale=1.0)
+    assert a_s[0, 0] > n - 1e-3
+    np.testing.assert_allclose(a_v[0], 1.0, atol=2e-3)
