@@ -141,7 +141,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="zipf128k",
-                    choices=["zipf128k", "fixed32k", "indexer128k", "e2e256k"])
+                    choices=["zipf128k", "fixed32k", "indexer128k", "e2e256k", "aggregate32k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--alpha", type=float, default=0.01,
@@ -160,12 +160,14 @@ def main():
     import vertical_slash_sparse_amd as vsa
     import workloads
 
-    w = workloads.WORKLOADS[args.workload]
+    w = workloads.WORKLOADS.get(args.workload, workloads.WORKLOADS["fixed32k"])
     t_gen = time.perf_counter()
     print(f"[bench] generating {args.workload} inputs", file=sys.stderr, flush=True)
 
     if args.workload == "indexer128k":
         return bench_indexer(args, w, torch, vsa, workloads)
+    if args.workload == "aggregate32k":
+        return bench_aggregate(args, torch, vsa, workloads)
 
     n, hq, hkv, d = w["n"], w["hq"], w["hkv"], w["d"]
     group = hq // hkv
@@ -345,6 +347,59 @@ def bench_indexer(args, w, torch, vsa, workloads):
                      "src_digest": source_digest(INDEX_SOURCES)},
     }
     copy_calibration(args, torch)
+    print(json.dumps(res), flush=True)
+
+
+def bench_aggregate(args, torch, vsa, workloads):
+    """vs_attn_aggregate on the 32K layer's Q/K/V (32/8 heads, d=128): dense
+    causal attention, then its weights summed along columns and diagonals."""
+    w = workloads.WORKLOADS["fixed32k"]
+    n, hq, hkv, d = w["n"], w["hq"], w["hkv"], w["d"]
+    q, k, v = workloads.attention_inputs("fixed32k")
+    qd, kd, vd = _dev(q, torch), _dev(k, torch), _dev(v, torch)
+    out = torch.empty_like(qd)
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    a_v = torch.empty((hkv, n), dtype=torch.float32, device="cuda")
+    a_s = torch.empty((hkv, n), dtype=torch.float32, device="cuda")
+    ws = torch.empty(vsa.vs_aggregate_workspace_bytes(hkv, n), dtype=torch.uint8, device="cuda")
+    # pass 1 alone: the same dense attention through the prefill entry point
+    soff = torch.arange(n, dtype=torch.int32, device="cuda").repeat(hkv, 1).contiguous()
+    scnt = torch.full((hkv,), n, dtype=torch.int32, device="cuda")
+    vidx = torch.full((hkv, 1), -1, dtype=torch.int32, device="cuda")
+    vcnt = torch.zeros((hkv,), dtype=torch.int32, device="cuda")
+    aws = torch.empty(vsa.vs_attn_workspace_bytes(hkv, n, 1, n), dtype=torch.uint8, device="cuda")
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    tt, t1 = [], []
+    for it in range(args.warmup + args.steps):
+        e[0].record()
+        vsa.vs_attn_aggregate(qd, kd, vd, out=out, lse=lse, a_v=a_v, a_s=a_s, workspace=ws)
+        e[1].record()
+        vsa.vs_sparse_attn_prefill(qd, kd, vd, vidx, vcnt, soff, scnt, out=out, lse=lse, workspace=aws)
+        e[2].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            tt.append(e[0].elapsed_time(e[1]))
+            t1.append(e[1].elapsed_time(e[2]))
+    ms, ms1 = float(np.mean(tt)), float(np.mean(t1))
+    ms2 = ms - ms1
+    group = hq // hkv
+    bp = 512 // group
+    tiles = hkv * sum((min((b + 1) * bp, n) - 1) // 64 + 1 for b in range((n + bp - 1) // bp))
+    f2 = 2.0 * d * 512 * 64 * tiles               # Q K^T over every computed tile, pass 2
+    tot = a_v.double().sum().item() / (hkv * group * n)
+    res = {
+        "metric": "vertical/slash ground-truth aggregation ms @32K (dense attention + sums)",
+        "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "aggregate32k", "n": n, "h_q": hq, "h_kv": hkv, "d": d, "seed": w["seed"]},
+        "pass1_attention_ms": round(ms1, 4), "pass2_sums_ms": round(ms2, 4),
+        "row_sum_check": round(tot, 6),
+        "roofline": {"bound": "mfma", "kernel": "agg_kernel (vs_attn_aggregate, pass 2)",
+                     "achieved": round(f2 / (ms2 * 1e-3) / 1e12, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(f2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
     print(json.dumps(res), flush=True)
 
 

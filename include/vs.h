@@ -152,6 +152,30 @@ vs_status vs_attn_tile_counts(const void* ws, int h_kv, int n, int cap_v, int ca
                               int h_q, int64_t tiles[4], hipStream_t stream);
 
 /* Static text for a status code. */
+/* ------------------------------------------ vertical/slash ground truth
+ * VSPrefill (English page, section 2, "Key Components, 2. Distillation
+ * Training, Ground Truth Generation"; German page, 2.B.2): the indexer is
+ * distilled from full attention weights aggregated along vertical columns
+ * and slash diagonals, computed without materialising the n x n matrix.
+ * This call runs dense causal attention (out, lse as vs_sparse_attn_prefill
+ * would with every offset selected) and then, per KV head g,
+ *     a_v[g][j] = sum over the group's query heads h and rows i >= j of P^h_ij
+ *     a_s[g][o] = sum over h and rows i >= o of P^h_{i,i-o}
+ * with P the attention weights (softmax of scale * q_i . k_j over j <= i).
+ * The sums are not normalised: each of a_v[g], a_s[g] totals G * n.
+ *   q, k, v   : bf16 as for vs_sparse_attn_prefill
+ *   out, lse  : bf16 [h_q][n][d], fp32 [h_q][n] (lse is required)
+ *   a_v, a_s  : fp32 [h_kv][n]
+ * P is formed in fp32 from the bf16 products and the fp32 lse of the first
+ * pass; sums use fp32 atomics, so their last bits may vary run to run.
+ * Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8, 16}; K per head under
+ * 2 GiB.  The workspace holds the list of all offsets and the attention
+ * workspace. */
+size_t vs_aggregate_workspace_bytes(int h_kv, int n);
+vs_status vs_attn_aggregate(const void* q, const void* k, const void* v, int h_q, int h_kv, int n,
+                            int d, float scale, void* out, float* lse, float* a_v, float* a_s,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
 const char* vs_status_str(vs_status s);
 
 #ifdef __cplusplus

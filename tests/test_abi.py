@@ -71,6 +71,17 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert L.vs_select_threshold(None, 1, 10, 0, 0.5, 5, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
     assert L.vs_select_threshold(p, 1, 10, 0, 0.5, 11, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
     assert L.vs_select_threshold(p, 1, 10, 0, 0.5, 5, p, p, p, 8, None) == vsa.VS_ERR_WORKSPACE
+    # vs_attn_aggregate: pointers, shapes, workspace
+    agg = lambda **kw: L.vs_attn_aggregate(*[kw.get(k, dv) for k, dv in (
+        ("q", p), ("k", p), ("v", p), ("h_q", 8), ("h_kv", 2), ("n", 256), ("d", 128),
+        ("scale", ctypes.c_float(0.088)), ("out", p), ("lse", p), ("a_v", p), ("a_s", p), ("ws", p),
+        ("ws_bytes", 1 << 30), ("stream", None))])
+    assert agg(lse=None) == vsa.VS_ERR_INVALID
+    assert agg(a_s=None) == vsa.VS_ERR_INVALID
+    assert agg(h_q=6) == vsa.VS_ERR_UNSUPPORTED
+    assert agg(d=96) == vsa.VS_ERR_UNSUPPORTED
+    assert agg(ws_bytes=16) == vsa.VS_ERR_WORKSPACE
+    assert L.vs_aggregate_workspace_bytes(2, 256) > L.vs_attn_workspace_bytes(2, 256, 1, 256)
     # vs_index: shapes
     assert L.vs_index(p, p, 8, 100, 64, 128, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED
     assert L.vs_index(p, p, 8, 100, 128, 64, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED

@@ -9,6 +9,7 @@ calls raise.
     vs_index(k_rope, v, w1, w2)                    -> (vlog, slog)
     vs_select(logit, kind, mass, cap)              -> (idx, count)
     vs_select_threshold(logit, kind, alpha, cap)   -> (idx, count)
+    vs_attn_aggregate(q, k, v)                     -> (out, lse, a_v, a_s)
     vs_sparse_attn_prefill(q, k, v, v_idx, v_cnt, s_off, s_cnt, scale=None)
                                                    -> (out, lse)
 """
@@ -28,7 +29,7 @@ VS_BF16, VS_F32 = 0, 1
 VS_VERTICAL, VS_SLASH = 0, 1
 
 _SYMBOLS = ("vs_index", "vs_select_workspace_bytes", "vs_select", "vs_select_threshold",
-            "vs_attn_workspace_bytes",
+            "vs_attn_workspace_bytes", "vs_aggregate_workspace_bytes", "vs_attn_aggregate",
             "vs_sparse_attn_prefill", "vs_attn_tile_counts", "vs_status_str")
 
 
@@ -57,6 +58,10 @@ def lib() -> ctypes.CDLL:
         L.vs_select.restype = i32
         L.vs_select_threshold.argtypes = [P, i32, i32, i32, f64, i32, P, P, P, sz, P]
         L.vs_select_threshold.restype = i32
+        L.vs_aggregate_workspace_bytes.argtypes = [i32, i32]
+        L.vs_aggregate_workspace_bytes.restype = sz
+        L.vs_attn_aggregate.argtypes = [P, P, P, i32, i32, i32, i32, f32, P, P, P, P, P, sz, P]
+        L.vs_attn_aggregate.restype = i32
         L.vs_attn_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.vs_attn_workspace_bytes.restype = sz
         L.vs_sparse_attn_prefill.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P, i32, P, P,
@@ -241,6 +246,45 @@ def vs_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                       workspace.numel(), _stream(q, stream))
     _check("vs_sparse_attn_prefill", st)
     return out, lse
+
+
+def vs_aggregate_workspace_bytes(h_kv: int, n: int) -> int:
+    return int(lib().vs_aggregate_workspace_bytes(h_kv, n))
+
+
+def vs_attn_aggregate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                      a_v: torch.Tensor | None = None, a_s: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None):
+    """Dense causal attention plus its weights summed per KV head along key
+    columns (a_v) and diagonals (a_s).  q [h_q, n, d], k/v [h_kv, n, d] bf16.
+    Returns (out, lse, a_v [h_kv, n], a_s [h_kv, n])."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, 3, dev)
+    _need(v, "v", torch.bfloat16, 3, dev)
+    h_q, n, d = q.shape
+    h_kv = k.shape[0]
+    if k.shape != (h_kv, n, d) or v.shape != (h_kv, n, d):
+        raise ValueError("vs_attn_aggregate: k and v must be [h_kv, n, d] like q")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((h_q, n), dtype=torch.float32, device=dev) if lse is None else lse
+    a_v = torch.empty((h_kv, n), dtype=torch.float32, device=dev) if a_v is None else a_v
+    a_s = torch.empty((h_kv, n), dtype=torch.float32, device=dev) if a_s is None else a_s
+    _need(out, "out", torch.bfloat16, 3, dev)
+    _need(lse, "lse", torch.float32, 2, dev)
+    _need(a_v, "a_v", torch.float32, 2, dev)
+    _need(a_s, "a_s", torch.float32, 2, dev)
+    need = vs_aggregate_workspace_bytes(h_kv, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = lib().vs_attn_aggregate(_ptr(q), _ptr(k), _ptr(v), h_q, h_kv, n, d, scale, _ptr(out), _ptr(lse),
+                                 _ptr(a_v), _ptr(a_s), _ptr(workspace), workspace.numel(),
+                                 _stream(q, stream))
+    _check("vs_attn_aggregate", st)
+    return out, lse, a_v, a_s
 
 
 def vs_attn_tile_counts(workspace: torch.Tensor, h_kv: int, n: int, cap_v: int, cap_s: int,

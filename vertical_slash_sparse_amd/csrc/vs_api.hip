@@ -103,6 +103,25 @@ vs_status vs_sparse_attn_prefill(const void* q, const void* k, const void* v, vs
                               s_off, s_cnt, cap_s, out, lse, ws, stream));
 }
 
+size_t vs_aggregate_workspace_bytes(int h_kv, int n) {
+  if (h_kv <= 0 || n <= 0) return 0;
+  return aggregate_workspace_bytes(h_kv, n);
+}
+
+vs_status vs_attn_aggregate(const void* q, const void* k, const void* v, int h_q, int h_kv, int n,
+                            int d, float scale, void* out, float* lse, float* a_v, float* a_s,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out || !lse || !a_v || !a_s || !ws) return VS_ERR_INVALID;
+  if (h_q <= 0 || h_kv <= 0 || n <= 0 || d <= 0 || h_q % h_kv) return VS_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return VS_ERR_INVALID;
+  if ((long long)n > (1LL << 30) || (long long)h_kv * n * d > (1LL << 40)) return VS_ERR_INVALID;
+  if (!group_ok(h_q, h_kv)) return VS_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return VS_ERR_UNSUPPORTED;
+  if ((long long)n * d * 2 >= (1LL << 31)) return VS_ERR_UNSUPPORTED;
+  if (ws_bytes < vs_aggregate_workspace_bytes(h_kv, n)) return VS_ERR_WORKSPACE;
+  return from_hip(launch_aggregate(q, k, v, h_q, h_kv, n, d, scale, out, lse, a_v, a_s, ws, stream));
+}
+
 vs_status vs_attn_tile_counts(const void* ws, int h_kv, int n, int cap_v, int cap_s, int h_q,
                               int64_t tiles[4], hipStream_t stream) {
   if (!ws || !tiles) return VS_ERR_INVALID;

@@ -67,6 +67,11 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
 
 int attn_query_rows_per_block(int group);
 
+size_t aggregate_workspace_bytes(int h_kv, int n);
+hipError_t launch_aggregate(const void* q, const void* k, const void* v, int h_q, int h_kv, int n,
+                            int d, float scale, void* out, float* lse, float* a_v, float* a_s,
+                            void* ws, hipStream_t stream);
+
 // mass in (0, 1] with thresh == 0: cumulative-mass budget; thresh > 0: keep
 // quantised masses >= thresh (max-based threshold)
 hipError_t launch_select(const float* logit, int heads, int n, int kind, double mass,
