@@ -17,7 +17,14 @@
 //     per-lane add; diagonals go through LDS atomics into a ring indexed by
 //     the offset.  After each tile the 64 column sums and the 64 diagonals no
 //     later tile reaches leave through global atomics.
+// The ring holds unsigned fixed point with 22 fraction bits: integer LDS
+// atomics run at the rate of plain LDS stores on gfx950, while ds_add_f32 is
+// several times slower.  A workgroup has 512 rows, so a ring slot (one
+// diagonal) gathers at most 512 weights of at most 1 and stays below 2^32;
+// each weight is rounded to nearest (error at most 2^-23), and the scale
+// 2^22 is folded into the exponent.
 #include <climits>
+#include <type_traits>
 
 #include "vs_common.h"
 #include "vs_internal.h"
@@ -30,6 +37,9 @@ constexpr int kAggWaves = 8;
 constexpr int kAggThreads = kAggWaves * 64;
 constexpr int kAggRows = 512;    // query rows (heads x positions) per workgroup
 constexpr int kAggRing = 1024;   // diagonal ring entries (> positions + 127)
+constexpr int kAggRingPad = 64;  // slots past the ring that alias its first 64
+constexpr int kAggFrac = 22;     // fraction bits of the ring's fixed point
+constexpr int kAggDmaWaves = 4;  // waves that load K tiles
 
 struct AggParams {
   const void* q;
@@ -40,6 +50,10 @@ struct AggParams {
   int n, hkv, group, bp, nblocks;
   float c;  // scale * log2(e)
 };
+
+// nearest integer of 0 <= x < 2^31 (halves round up); x + 0.5 is exact
+// below 2^22, the range of the ring's terms
+__device__ __forceinline__ uint32_t round_u32(float x) { return (uint32_t)(x + 0.5f); }
 
 template <int D>
 __device__ __forceinline__ int agg_swz(int r) {
@@ -69,11 +83,11 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggParams p) {
   constexpr int CH = D / 8;
   constexpr int ROWB = D * 2;
   constexpr int TILEB = kBN * ROWB;
-  constexpr int RPD = 1024 / ROWB;
-  constexpr int NDMA = kBN / kAggWaves / RPD;
+  constexpr int RPD = 1024 / ROWB;                 // key rows per 1 KiB DMA
+  constexpr int NDMA = kBN / kAggDmaWaves / RPD;   // DMAs per loading wave per tile
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ __align__(16) uint8_t kt[2 * TILEB];
-  __shared__ float ring[kAggRing];
+  __shared__ uint32_t ring[kAggRing + kAggRingPad];
   __shared__ float colp[kAggWaves][kBN];
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   lds_u8* const kbase = (lds_u8*)kt;
@@ -87,11 +101,12 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggParams p) {
   const int i1 = min(i0 + p.bp, n) - 1;
   const int groups_per_head = p.bp / 32;
 
-  for (int t = tid; t < kAggRing; t += kAggThreads) ring[t] = 0.f;
+  for (int t = tid; t < kAggRing + kAggRingPad; t += kAggThreads) ring[t] = 0u;
 
-  // two row groups of 32 per wave: Q rows as the A operand, lse per element
+  // two row groups of 32 per wave: Q rows as the A operand, and per element
+  // the bias that turns a logit into its weight times 2^kAggFrac
   bf16x8 qa[2][KS];
-  float ls[2][16];
+  float nls[2][16];
   int rbase[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -107,20 +122,25 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggParams p) {
       if (row >= n) raw = u32x4{0u, 0u, 0u, 0u};
       qa[r][s] = as_bf16x8(raw);
     }
-    // element 4a + bb holds row 8a + 4*half + bb of the group
+    // element 4a + bb holds row 8a + 4*half + bb of the group; rows past the
+    // end get -inf, so their weights come out as exactly zero
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int ri = i0w + 8 * (e >> 2) + 4 * half + (e & 3);
-      ls[r][e] = ri < n ? p.lse[(size_t)head * n + ri] * kLog2e : __builtin_inff();
+      const float l = p.lse[(size_t)head * n + min(ri, n - 1)];
+      nls[r][e] = ri < n ? (float)kAggFrac - l * kLog2e : -__builtin_inff();
     }
   }
 
-  // LDS-DMA of one 64-key K tile (chunk-swizzled rows)
+  // LDS-DMA of one 64-key K tile (chunk-swizzled rows) by the first
+  // kAggDmaWaves waves; the others never wait on vector memory, so the global
+  // atomics they issue stay off the critical path
+  const bool loader = wave < kAggDmaWaves;
   const u32x4 wk = buffer_words(static_cast<const char*>(p.k) + (size_t)g * n * ROWB, (uint32_t)(n * ROWB));
   int dma_row[NDMA], dma_col[NDMA];
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
-    const int r = wave * (kBN / kAggWaves) + i * RPD + lane / CH;
+    const int r = (wave % kAggDmaWaves) * (kBN / kAggDmaWaves) + i * RPD + lane / CH;
     dma_row[i] = r;
     dma_col[i] = ((lane % CH) ^ agg_swz<D>(r)) * 16;
   }
@@ -129,72 +149,105 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggParams p) {
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const unsigned off = (unsigned)(tile * kBN + dma_row[i]) * ROWB + dma_col[i];
-      dma16(wk, (uint32_t)(uintptr_t)(kbase + st * TILEB + (wave * (kBN / kAggWaves) + i * RPD) * ROWB), off);
+      dma16(wk, (uint32_t)(uintptr_t)(kbase + st * TILEB +
+                                      ((wave % kAggDmaWaves) * (kBN / kAggDmaWaves) + i * RPD) * ROWB),
+            off);
       dma_off[i] = off;
     }
   };
+  // Ring slot of element e of a 32x32 block: its offset row - key is
+  // (rbase - key0 - 31) + lane_slot + erow(e), with erow(e) = 8(e/4) + e%4
+  // and lane_slot = 4*half - ql + 31 in [0, 35]; the uniform part is taken
+  // mod kAggRing, so a block's 63 slots are contiguous and may run up to
+  // kAggRingPad slots past the ring, into the copies of its first slots
+  const int lane_slot = 4 * half - ql + 31;
   int boff[KS];  // B operand: key row ql of a 32-key block, chunk 2s + half
 #pragma unroll
   for (int s = 0; s < KS; ++s) boff[s] = ql * ROWB + 16 * ((2 * s + half) ^ agg_swz<D>(ql));
 
+  // Key tiles are visited from a start tile that differs between workgroups,
+  // wrapping round: workgroups that run at the same time then add into
+  // different columns.  Diagonal offsets fall by kBN per tile within a run,
+  // so after a tile the kBN largest offsets it touched are complete; at the
+  // end of each run (the diagonal tile, and the last tile visited) every
+  // offset still in the ring is.
   const int T = i1 / kBN + 1;
-  stage(0, 0);
+  const int t_first = (int)(((unsigned)b * 0x9E3779B1u + (unsigned)g * 0x7F4A7C15u) % (unsigned)T);
+  const int diag_tile = i0 / kBN;  // first tile that needs the causal mask
+  if (loader) stage(t_first, 0);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   __syncthreads();
-  for (int t = 0; t < T; ++t) {
-    const int st = t & 1;
-    if (t + 1 < T) stage(t + 1, st ^ 1);
+  for (int it = 0; it < T; ++it) {
+    const int t = t_first + it < T ? t_first + it : t_first + it - T;
+    const int st = it & 1;
+    if (loader && it + 1 < T) {
+      stage(t + 1 < T ? t + 1 : 0, st ^ 1);
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) asm volatile("" ::"v"(dma_off[i]));
+      for (int i = 0; i < NDMA; ++i) asm volatile("" ::"v"(dma_off[i]));
+    }
     const int j0 = t * kBN;
     const lds_u8* kb = kbase + st * TILEB;
     float cs[2] = {0.f, 0.f};
+    auto body = [&](auto masked) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      const int key = j0 + 32 * jb + ql;
+      for (int jb = 0; jb < 2; ++jb) {
+        const int key = j0 + 32 * jb + ql;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        f32x16 s;
+        for (int r = 0; r < 2; ++r) {
+          f32x16 s;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = 0.f;
+          for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const bf16x8 bo = *(const __attribute__((address_space(3))) bf16x8*)(kb + 32 * jb * ROWB + boff[kk]);
-          s = mfma32(qa[r][kk], bo, s);
-        }
+          for (int kk = 0; kk < KS; ++kk) {
+            const bf16x8 bo = *(const __attribute__((address_space(3))) bf16x8*)(kb + 32 * jb * ROWB + boff[kk]);
+            s = mfma32(qa[r][kk], bo, s);
+          }
+          uint32_t* const slot = ring + ((rbase[r] - j0 - 32 * jb - 31) & (kAggRing - 1)) + lane_slot;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = rbase[r] + 8 * (e >> 2) + 4 * half + (e & 3);
-          const float pv = key <= row ? __builtin_amdgcn_exp2f(fmaf(s[e], p.c, -ls[r][e])) : 0.f;
-          cs[jb] += pv;
-          atomicAdd(&ring[(row - key) & (kAggRing - 1)], pv);
+          for (int e = 0; e < 16; ++e) {
+            const int erow = 8 * (e >> 2) + (e & 3);
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[e], p.c, nls[r][e]));
+            if constexpr (decltype(masked)::value) pv = key <= rbase[r] + 4 * half + erow ? pv : 0.f;
+            cs[jb] += pv;
+            atomicAdd(slot + erow, round_u32(pv));
+          }
         }
       }
-    }
+    };
+    if (t >= diag_tile) body(std::true_type{});
+    else body(std::false_type{});
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
-      const float tot = cs[jb] + swap_halves(cs[jb]);
+      const float tot = half_sum(cs[jb]);
       if (half == 0) colp[wave][32 * jb + ql] = tot;
     }
     __syncthreads();
     const int top = i0 + p.bp - 1 - j0;  // largest offset this tile reaches
-    if (tid < kBN) {
+    if (wave == kAggDmaWaves) {
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < kAggWaves; ++w) v += colp[w][tid];
-      const int key = j0 + tid;
+      for (int w = 0; w < kAggWaves; ++w) v += colp[w][lane];
+      v *= 1.f / (float)(1 << kAggFrac);
+      const int key = j0 + lane;
       if (key < n && v != 0.f) atomicAdd(&p.a_v[(size_t)g * n + key], v);
-    } else if (tid < 2 * kBN) {
-      // offsets later tiles no longer reach; after the last tile, all of them
-      const int lo = t + 1 < T ? top - kBN + 1 : max(0, i0 - j0 - (kBN - 1));
-      for (int o = top - (tid - kBN); o >= lo; o -= kBN) {
+    } else if (wave == kAggDmaWaves + 1) {
+      const bool run_end = t == T - 1 || it == T - 1;
+      const int lo = run_end ? max(0, i0 - j0 - (kBN - 1)) : top - kBN + 1;
+      for (int o = top - lane; o >= lo; o -= kBN) {
         if (o < 0 || o >= n) continue;
-        const float v = ring[o & (kAggRing - 1)];
-        ring[o & (kAggRing - 1)] = 0.f;
-        if (v != 0.f) atomicAdd(&p.a_s[(size_t)g * n + o], v);
+        const int sl = o & (kAggRing - 1);
+        uint32_t u = ring[sl];
+        ring[sl] = 0u;
+        if (sl < kAggRingPad) {
+          u += ring[kAggRing + sl];
+          ring[kAggRing + sl] = 0u;
+        }
+        if (u != 0u) atomicAdd(&p.a_s[(size_t)g * n + o], (float)u * (1.f / (float)(1 << kAggFrac)));
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the next tile has landed
+    // the loaders' next tile has landed; the others only need their LDS work done
+    if (loader) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0)
     __syncthreads();
   }
 }
