@@ -7,7 +7,9 @@ shares no kernels, headers, helpers or constants with
 lives in ``vs_oracle.c`` (plain C, fp64, OpenMP over rows); this module only
 builds that file with gcc and marshals numpy arrays to it.
 
-Every function here is pinned by ``tests/test_oracle.py`` against brute
+Every function here is pinned by ``tests/test_oracle.py`` (vertical-slash
+path, selection, indexer, aggregation) and ``tests/test_oracle_blocks.py``
+(FlashPrefill block discovery and block-sparse attention) against brute
 force, closed forms, library routines or hand-derived values.
 """
 from __future__ import annotations
@@ -66,6 +68,15 @@ def lib():
         L.vso_row_set.restype = i32
         L.vso_pair_count.argtypes = [P, P, i32, P, P, i32, i32, i32]
         L.vso_pair_count.restype = i64
+        L.vso_block_means.argtypes = [P, i32, i32, i32, i32, i32, P]
+        L.vso_block_means.restype = i32
+        L.vso_block_scores.argtypes = [P, i32, i32, i32, i32, i32, f64, i32, i32, P, P, i32]
+        L.vso_block_scores.restype = i32
+        L.vso_block_select.argtypes = [P, i32, i32, ctypes.c_float, P, i32]
+        L.vso_block_select.restype = i32
+        L.vso_block_attn_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, i32, P, i32, P,
+                                          P, i64, P, P, i32]
+        L.vso_block_attn_rows.restype = i32
         L.vso_num_threads.restype = i32
         _lib = L
     return _lib
@@ -216,3 +227,92 @@ def pair_count(vidx, vcnt, soff, scnt, g, n) -> int:
     vidx, vcnt, soff, scnt = (_c(x, np.int32) for x in (vidx, vcnt, soff, scnt))
     return int(lib().vso_pair_count(_ptr(vidx), _ptr(vcnt), vidx.shape[1], _ptr(soff),
                                     _ptr(scnt), soff.shape[1], int(g), int(n)))
+
+
+# ---------------------------------------------------------------- FlashPrefill blocks
+
+BLOCK = 64  # query and key block size of the block-sparse mode
+
+
+def block_means(k, bs=BLOCK):
+    """Mean key of every block of bs positions, fp64 [hkv, nb, d] (the last
+    block averages the keys it has)."""
+    k = _c(k)
+    hkv, n, d = k.shape
+    nb = (n + bs - 1) // bs
+    kbar = np.empty((hkv, nb, d), dtype=np.float64)
+    if lib().vso_block_means(_ptr(k), _dtype_code(k), hkv, n, d, bs, _ptr(kbar)):
+        raise ValueError("oracle block_means: invalid arguments")
+    return kbar
+
+
+def block_scores(q, k, skel, scale=None, bs=BLOCK, nthreads=0):
+    """Block scores [hkv, nb, nb] fp64: for query block I and candidate J < I,
+    the softmax probability of J under scale * q . kbar_J averaged over the
+    skeleton probes (rows bs*I + m*(bs/skel) < n of every query head of the
+    group); zero for J >= I."""
+    q = _c(q)
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    assert k.shape == (hkv, n, d) and q.dtype == _c(k).dtype
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    kbar = block_means(k, bs)
+    nb = kbar.shape[1]
+    score = np.empty((hkv, nb, nb), dtype=np.float64)
+    if lib().vso_block_scores(_ptr(q), _dtype_code(q), hq, hkv, n, d, scale, bs, int(skel),
+                              _ptr(kbar), _ptr(score), int(nthreads)):
+        raise ValueError("oracle block_scores: invalid arguments")
+    return score
+
+
+def words_per_row(nb):
+    return (nb + 31) // 32
+
+
+def block_select(score, alpha):
+    """Max-based threshold on fp32 scores [hkv, nb, nb], decided in fp32:
+    keep J < I when score >= alpha * max (one fp32 product), and J = I.
+    Returns the mask uint32 [hkv, nb, words_per_row(nb)]."""
+    score = _c(score, np.float32)
+    hkv, nb, nb2 = score.shape
+    assert nb == nb2
+    wpr = words_per_row(nb)
+    mask = np.empty((hkv, nb, wpr), dtype=np.uint32)
+    if lib().vso_block_select(_ptr(score), hkv, nb, float(np.float32(alpha)), _ptr(mask), wpr):
+        raise ValueError("oracle block_select: invalid arguments")
+    return mask
+
+
+def mask_to_dense(mask, nb):
+    """Block mask words -> bool [hkv, nb, nb]."""
+    bits = np.unpackbits(mask.view(np.uint8), axis=-1, bitorder="little")
+    return bits[..., :nb].astype(bool)
+
+
+def block_attn(q, k, v, mask, scale=None, bs=BLOCK, rows=None, nthreads=0):
+    """Causal attention of every query head over S_i = {j <= i : block j/bs
+    kept for query block i/bs of its KV head}.  Same conventions as attn()."""
+    q, k, v = _c(q), _c(k), _c(v)
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    assert k.shape == v.shape == (hkv, n, d) and q.dtype == k.dtype == v.dtype
+    mask = _c(mask, np.uint32)
+    nb = (n + bs - 1) // bs
+    assert mask.shape[:2] == (hkv, nb)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    full = rows is None
+    if full:
+        hh, ii = np.meshgrid(np.arange(hq), np.arange(n), indexing="ij")
+        rows = np.stack([hh.ravel(), ii.ravel()], axis=1)
+    rows = _c(rows, np.int32).reshape(-1, 2)
+    rh, ri = _c(rows[:, 0]), _c(rows[:, 1])
+    m = rows.shape[0]
+    out = np.empty((m, d), dtype=np.float64)
+    lse = np.empty(m, dtype=np.float64)
+    if lib().vso_block_attn_rows(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), hq, hkv, n, d, scale,
+                                 bs, _ptr(mask), mask.shape[2], _ptr(rh), _ptr(ri), m, _ptr(out),
+                                 _ptr(lse), int(nthreads)):
+        raise ValueError("oracle block_attn: invalid arguments")
+    if full:
+        return out.reshape(hq, n, d), lse.reshape(hq, n)
+    return out, lse

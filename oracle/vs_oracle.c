@@ -427,6 +427,189 @@ int vso_select_threshold(const float* logit, int heads, int n, int kind, double 
   return 0;
 }
 
+/* ------------------------------------------- FlashPrefill block discovery */
+
+/* FlashPrefill (gist.science summary of arXiv 2603.06199, Spanish page,
+ * "2. Metodologia", part A "Descubrimiento Instantaneo de Patrones",
+ * "Estrategia de Aproximacion de Bloques", and part B "Umbralizacion Dinamica
+ * Basada en Maximos"): key blocks are scored for a query block by a sparse,
+ * evenly spaced set of probe ("skeleton") queries against the mean key of
+ * each block, whose exponential is the geometric mean of the block's
+ * exponentials (the AM-GM proxy); a query block keeps the key blocks whose
+ * score is at least alpha times its largest score.
+ *
+ * Readings where the page is silent: query and key blocks are bs consecutive
+ * positions (the last block may be short); the skeleton of query block I for
+ * KV head g is, for every query head h of g, the rows bs*I + m*(bs/skel),
+ * m = 0..skel-1, that are below n (row bs*I always is); the candidates of
+ * query block I are the full causal blocks J < I; one probe's block
+ * distribution is the softmax over the candidates of scale * q . kbar_J; a
+ * block's score is that probability averaged over the probes; the diagonal
+ * block J = I is always kept, and block 0 keeps only itself. */
+
+/* kbar[g][J][t] = mean over the keys j of block J of k[g][j][t], fp64. */
+int vso_block_means(const void* k, int dtype, int hkv, int n, int d, int bs, double* kbar) {
+  if (hkv <= 0 || n <= 0 || d <= 0 || bs <= 0) return 1;
+  const int nb = (n + bs - 1) / bs;
+  double* row = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int g = 0; g < hkv; ++g)
+    for (int J = 0; J < nb; ++J) {
+      double* out = kbar + ((int64_t)g * nb + J) * d;
+      const int j0 = J * bs, j1 = (j0 + bs < n ? j0 + bs : n);
+      for (int t = 0; t < d; ++t) out[t] = 0.0;
+      for (int j = j0; j < j1; ++j) {
+        load_row(k, dtype, ((int64_t)g * n + j) * d, d, row);
+        for (int t = 0; t < d; ++t) out[t] += row[t];
+      }
+      for (int t = 0; t < d; ++t) out[t] /= (double)(j1 - j0);
+    }
+  free(row);
+  return 0;
+}
+
+/* score[g][I][J] for J < I (zero elsewhere), from the block means kbar
+ * [hkv][nb][d]: the mean over the skeleton probes of block I of
+ * exp(z_J - max z) / sum_{J' < I} exp(z_J' - max z), z_J = scale q . kbar_J. */
+int vso_block_scores(const void* q, int dtype, int hq, int hkv, int n, int d, double scale, int bs,
+                     int skel, const double* kbar, double* score, int nthreads) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || n <= 0 || d <= 0 || bs <= 0) return 1;
+  if (skel <= 0 || skel > bs || bs % skel != 0) return 1;
+  const int group = hq / hkv, nb = (n + bs - 1) / bs, step = bs / skel;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double* qi = (double*)malloc(sizeof(double) * (size_t)d);
+    double* z = (double*)malloc(sizeof(double) * (size_t)nb);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < (int64_t)hkv * nb; ++r) {
+      const int g = (int)(r / nb), I = (int)(r % nb);
+      double* out = score + ((int64_t)g * nb + I) * nb;
+      for (int J = 0; J < nb; ++J) out[J] = 0.0;
+      if (I == 0) continue;
+      int probes = 0;
+      for (int h = g * group; h < (g + 1) * group; ++h)
+        for (int m = 0; m < skel; ++m) {
+          const int i = I * bs + m * step;
+          if (i >= n) continue;
+          load_row(q, dtype, ((int64_t)h * n + i) * d, d, qi);
+          double mx = -INFINITY;
+          for (int J = 0; J < I; ++J) {
+            const double* kb = kbar + ((int64_t)g * nb + J) * d;
+            double dot = 0.0;
+            for (int t = 0; t < d; ++t) dot += qi[t] * kb[t];
+            z[J] = scale * dot;
+            if (z[J] > mx) mx = z[J];
+          }
+          double l = 0.0;
+          for (int J = 0; J < I; ++J) l += exp(z[J] - mx);
+          for (int J = 0; J < I; ++J) out[J] += exp(z[J] - mx) / l;
+          ++probes;
+        }
+      for (int J = 0; J < I; ++J) out[J] /= (double)probes;
+    }
+    free(qi);
+    free(z);
+  }
+  return 0;
+}
+
+/* The max-based threshold on given fp32 scores [hkv][nb][nb], decided in
+ * fp32: thr = alpha * max_{J<I} score (one IEEE fp32 product); block J < I is
+ * kept when score >= thr, and J = I always.  mask[g][I][w] bit b <-> block
+ * 32 w + b; words_per_row >= ceil(nb / 32). */
+int vso_block_select(const float* score, int hkv, int nb, float alpha, uint32_t* mask,
+                     int words_per_row) {
+  if (hkv <= 0 || nb <= 0 || !(alpha > 0.0f && alpha <= 1.0f) || words_per_row * 32 < nb) return 1;
+  for (int g = 0; g < hkv; ++g)
+    for (int I = 0; I < nb; ++I) {
+      const float* row = score + ((int64_t)g * nb + I) * nb;
+      uint32_t* mrow = mask + ((int64_t)g * nb + I) * words_per_row;
+      for (int w = 0; w < words_per_row; ++w) mrow[w] = 0u;
+      float mx = -INFINITY;
+      for (int J = 0; J < I; ++J)
+        if (row[J] > mx) mx = row[J];
+      volatile float thr = alpha * mx;
+      for (int J = 0; J < I; ++J)
+        if (row[J] >= thr) mrow[J / 32] |= 1u << (J % 32);
+      mrow[I / 32] |= 1u << (I % 32);
+    }
+  return 0;
+}
+
+/* Attention under a block mask: for each requested (head, row i) of KV head
+ * g, S_i = { j <= i : bit (j / bs) of mask[g][i / bs] }, then the same fp64
+ * two-pass softmax as vso_attn_rows (empty S_i: out = 0, lse = -inf). */
+int vso_block_attn_rows(const void* q, const void* k, const void* v, int dtype, int hq, int hkv,
+                        int n, int d, double scale, int bs, const uint32_t* mask,
+                        int words_per_row, const int32_t* row_h, const int32_t* row_i,
+                        int64_t nrows, double* out, double* lse, int nthreads) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || n <= 0 || d <= 0 || bs <= 0) return 1;
+  const int group = hq / hkv, nb = (n + bs - 1) / bs;
+  if (words_per_row * 32 < nb) return 1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int err = 0;
+#pragma omp parallel
+  {
+    int32_t* set = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    double* qi = (double*)malloc(sizeof(double) * (size_t)d);
+    double* kj = (double*)malloc(sizeof(double) * (size_t)d);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; ++r) {
+      const int h = row_h[r], i = row_i[r];
+      if (h < 0 || h >= hq || i < 0 || i >= n) {
+        err = 1;
+        continue;
+      }
+      const int g = h / group;
+      const uint32_t* mrow = mask + ((int64_t)g * nb + i / bs) * words_per_row;
+      int m = 0;
+      for (int j = 0; j <= i; ++j)
+        if ((mrow[(j / bs) / 32] >> ((j / bs) % 32)) & 1u) set[m++] = j;
+      double* o = out + r * d;
+      if (m == 0) {
+        for (int t = 0; t < d; ++t) o[t] = 0.0;
+        lse[r] = -INFINITY;
+        continue;
+      }
+      load_row(q, dtype, ((int64_t)h * n + i) * d, d, qi);
+      double mx = -INFINITY;
+      for (int a = 0; a < m; ++a) {
+        load_row(k, dtype, ((int64_t)g * n + set[a]) * d, d, kj);
+        double dot = 0.0;
+        for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];
+        s[a] = scale * dot;
+        if (s[a] > mx) mx = s[a];
+      }
+      double l = 0.0;
+      for (int t = 0; t < d; ++t) acc[t] = 0.0;
+      for (int a = 0; a < m; ++a) {
+        const double p = exp(s[a] - mx);
+        l += p;
+        load_row(v, dtype, ((int64_t)g * n + set[a]) * d, d, kj);
+        for (int t = 0; t < d; ++t) acc[t] += p * kj[t];
+      }
+      for (int t = 0; t < d; ++t) o[t] = acc[t] / l;
+      lse[r] = mx + log(l);
+    }
+    free(set);
+    free(s);
+    free(qi);
+    free(kj);
+    free(acc);
+  }
+  return err;
+}
+
 int vso_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
