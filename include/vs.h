@@ -151,7 +151,6 @@ vs_status vs_sparse_attn_prefill(const void* q, const void* k, const void* v, vs
 vs_status vs_attn_tile_counts(const void* ws, int h_kv, int n, int cap_v, int cap_s,
                               int h_q, int64_t tiles[4], hipStream_t stream);
 
-/* Static text for a status code. */
 /* ------------------------------------------ vertical/slash ground truth
  * VSPrefill (English page, section 2, "Key Components, 2. Distillation
  * Training, Ground Truth Generation"; German page, 2.B.2): the indexer is
@@ -167,7 +166,10 @@ vs_status vs_attn_tile_counts(const void* ws, int h_kv, int n, int cap_v, int ca
  *   out, lse  : bf16 [h_q][n][d], fp32 [h_q][n] (lse is required)
  *   a_v, a_s  : fp32 [h_kv][n]
  * P is formed in fp32 from the bf16 products and the fp32 lse of the first
- * pass; sums use fp32 atomics, so their last bits may vary run to run.
+ * pass.  Column sums add fp32 partials; a diagonal's partial within a
+ * workgroup (at most 512 rows) is kept in fixed point with 22 fraction bits,
+ * each weight rounded to nearest (at most 2^-23 off), and the partials meet
+ * through fp32 atomics, so the last bits of both may vary run to run.
  * Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8, 16}; K per head under
  * 2 GiB.  The workspace holds the list of all offsets and the attention
  * workspace. */
@@ -176,6 +178,52 @@ vs_status vs_attn_aggregate(const void* q, const void* k, const void* v, int h_q
                             int d, float scale, void* out, float* lse, float* a_v, float* a_s,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------ FlashPrefill block discovery
+ * FlashPrefill (gist.science summary of arXiv 2603.06199, Spanish page,
+ * section 2.A "Estrategia de Aproximacion de Bloques", 2.B "Umbralizacion
+ * Dinamica Basada en Maximos"): query and key blocks are 64 positions (the
+ * last may be short), nb = ceil(n / 64).  For KV head g and query block I the
+ * probes are rows 64 I + m (64 / skel), m < skel, below n, of every query
+ * head of the group; each probe's distribution over the candidate blocks
+ * J < I is the softmax of scale * q . kbar_J, kbar_J the mean key of block J
+ * (its exponential is the geometric mean of the block's exponentials); the
+ * block score is that probability averaged over the probes.  Kept: the J < I
+ * with score >= alpha * max_J score (one fp32 product), and J = I always.
+ *   q, k   : bf16, [h_q][n][d] and [h_kv][n][d], row-major, device memory
+ *   skel   : probes per query head and block; divides 64; G * skel <= 32
+ *   alpha  : (0, 1]
+ *   mask   : out, uint32 [h_kv][nb][words_per_row], bit b of word w set when
+ *            key block 32 w + b is kept for that query block (words past I
+ *            are zero); words_per_row >= ceil(nb / 32)
+ *   score  : optional out (NULL to skip), fp32 [h_kv][nb][nb], the block
+ *            scores the mask was decided on (zero for J >= I)
+ * Block means are summed in fp32 and held as a bf16 pair (about 16
+ * significant bits); the scores run on the matrix cores with fp32
+ * accumulation.  Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8, 16};
+ * nb <= 8192 (the scores of four query blocks stay in LDS).  The workspace
+ * holds the block means.  Nothing is allocated; the calls only enqueue. */
+size_t vs_block_workspace_bytes(int h_kv, int n, int d);
+vs_status vs_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,
+                            float scale, int skel, float alpha, uint32_t* mask, int words_per_row,
+                            float* score, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Block-sparse causal prefill (FlashPrefill, same page, section 3 item 3:
+ * a block-sparse kernel that walks an index list of kept blocks instead of
+ * branching past masked ones).  Row i of a query head of KV head g attends
+ * to the keys j <= i whose block j / 64 is set in mask[g][i / 64]; bits above
+ * a query block's diagonal are ignored.  A row with no key gets out = 0 and
+ * lse = -inf.  Arguments as vs_sparse_attn_prefill, with the mask of
+ * vs_block_discover (or any caller-made mask of that layout) in place of the
+ * index lists.  The workspace (vs_block_attn_workspace_bytes() bytes) holds
+ * work counters.  Supported: as vs_sparse_attn_prefill, with
+ * n <= 2^30 - 64. */
+size_t vs_block_attn_workspace_bytes(void);
+vs_status vs_block_attn_prefill(const void* q, const void* k, const void* v, vs_dtype dt, int h_q,
+                                int h_kv, int n, int d, float scale, const uint32_t* mask,
+                                int words_per_row, void* out, float* lse, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
 const char* vs_status_str(vs_status s);
 
 #ifdef __cplusplus

@@ -70,7 +70,8 @@ def lib():
         L.vso_pair_count.restype = i64
         L.vso_block_means.argtypes = [P, i32, i32, i32, i32, i32, P]
         L.vso_block_means.restype = i32
-        L.vso_block_scores.argtypes = [P, i32, i32, i32, i32, i32, f64, i32, i32, P, P, i32]
+        L.vso_block_scores.argtypes = [P, i32, i32, i32, i32, i32, f64, i32, i32, P, P, P, i64, P,
+                                       i32]
         L.vso_block_scores.restype = i32
         L.vso_block_select.argtypes = [P, i32, i32, ctypes.c_float, P, i32]
         L.vso_block_select.restype = i32
@@ -246,11 +247,12 @@ def block_means(k, bs=BLOCK):
     return kbar
 
 
-def block_scores(q, k, skel, scale=None, bs=BLOCK, nthreads=0):
+def block_scores(q, k, skel, scale=None, bs=BLOCK, rows=None, nthreads=0):
     """Block scores [hkv, nb, nb] fp64: for query block I and candidate J < I,
     the softmax probability of J under scale * q . kbar_J averaged over the
     skeleton probes (rows bs*I + m*(bs/skel) < n of every query head of the
-    group); zero for J >= I."""
+    group); zero for J >= I.  With ``rows`` (int [m, 2] of (g, I)) only those
+    query blocks, as [m, nb]."""
     q = _c(q)
     hq, n, d = q.shape
     hkv = k.shape[0]
@@ -258,9 +260,18 @@ def block_scores(q, k, skel, scale=None, bs=BLOCK, nthreads=0):
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     kbar = block_means(k, bs)
     nb = kbar.shape[1]
-    score = np.empty((hkv, nb, nb), dtype=np.float64)
+    if rows is None:
+        score = np.empty((hkv, nb, nb), dtype=np.float64)
+        rg = ri = None
+        m = 0
+    else:
+        rows = _c(rows, np.int32).reshape(-1, 2)
+        rg, ri = _c(rows[:, 0]), _c(rows[:, 1])
+        m = rows.shape[0]
+        score = np.empty((m, nb), dtype=np.float64)
     if lib().vso_block_scores(_ptr(q), _dtype_code(q), hq, hkv, n, d, scale, bs, int(skel),
-                              _ptr(kbar), _ptr(score), int(nthreads)):
+                              _ptr(kbar), None if rg is None else _ptr(rg),
+                              None if ri is None else _ptr(ri), m, _ptr(score), int(nthreads)):
         raise ValueError("oracle block_scores: invalid arguments")
     return score
 

@@ -469,9 +469,12 @@ int vso_block_means(const void* k, int dtype, int hkv, int n, int d, int bs, dou
 
 /* score[g][I][J] for J < I (zero elsewhere), from the block means kbar
  * [hkv][nb][d]: the mean over the skeleton probes of block I of
- * exp(z_J - max z) / sum_{J' < I} exp(z_J' - max z), z_J = scale q . kbar_J. */
+ * exp(z_J - max z) / sum_{J' < I} exp(z_J' - max z), z_J = scale q . kbar_J.
+ * With rows_g == NULL every (g, I) is computed into score [hkv][nb][nb];
+ * otherwise only the nrows pairs (rows_g[r], rows_I[r]) into score [nrows][nb]. */
 int vso_block_scores(const void* q, int dtype, int hq, int hkv, int n, int d, double scale, int bs,
-                     int skel, const double* kbar, double* score, int nthreads) {
+                     int skel, const double* kbar, const int32_t* rows_g, const int32_t* rows_I,
+                     int64_t nrows, double* score, int nthreads) {
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || n <= 0 || d <= 0 || bs <= 0) return 1;
   if (skel <= 0 || skel > bs || bs % skel != 0) return 1;
   const int group = hq / hkv, nb = (n + bs - 1) / bs, step = bs / skel;
@@ -484,10 +487,12 @@ int vso_block_scores(const void* q, int dtype, int hq, int hkv, int n, int d, do
   {
     double* qi = (double*)malloc(sizeof(double) * (size_t)d);
     double* z = (double*)malloc(sizeof(double) * (size_t)nb);
+    const int64_t total = rows_g ? nrows : (int64_t)hkv * nb;
 #pragma omp for schedule(dynamic, 4)
-    for (int64_t r = 0; r < (int64_t)hkv * nb; ++r) {
-      const int g = (int)(r / nb), I = (int)(r % nb);
-      double* out = score + ((int64_t)g * nb + I) * nb;
+    for (int64_t r = 0; r < total; ++r) {
+      const int g = rows_g ? rows_g[r] : (int)(r / nb), I = rows_g ? rows_I[r] : (int)(r % nb);
+      if (g < 0 || g >= hkv || I < 0 || I >= nb) continue;
+      double* out = score + r * nb;
       for (int J = 0; J < nb; ++J) out[J] = 0.0;
       if (I == 0) continue;
       int probes = 0;

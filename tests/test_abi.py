@@ -109,6 +109,43 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert attn(cap_v=0) == vsa.VS_ERR_INVALID
     assert attn(n=0) == vsa.VS_ERR_INVALID
     assert attn(ws_bytes=16) == vsa.VS_ERR_WORKSPACE
+    # vs_block_discover: pointers, alpha, skel, group x skel, words, workspace
+    def disc(**kw):
+        a = dict(q=p, k=p, h_q=8, h_kv=2, n=1000, d=128, scale=ctypes.c_float(0.088), skel=8,
+                 alpha=ctypes.c_float(0.5), mask=p, wpr=1, score=None, ws=p, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.vs_block_discover(a["q"], a["k"], a["h_q"], a["h_kv"], a["n"], a["d"], a["scale"],
+                                   a["skel"], a["alpha"], a["mask"], a["wpr"], a["score"], a["ws"],
+                                   a["ws_bytes"], None)
+
+    assert disc(mask=None) == vsa.VS_ERR_INVALID
+    assert disc(alpha=ctypes.c_float(0.0)) == vsa.VS_ERR_INVALID
+    assert disc(alpha=ctypes.c_float(1.5)) == vsa.VS_ERR_INVALID
+    assert disc(skel=3) == vsa.VS_ERR_INVALID            # must divide 64
+    assert disc(skel=16) == vsa.VS_ERR_UNSUPPORTED       # G * skel = 64 > 32
+    assert disc(wpr=0) == vsa.VS_ERR_INVALID             # 16 blocks need one word
+    assert disc(d=96) == vsa.VS_ERR_UNSUPPORTED
+    assert disc(h_q=6) == vsa.VS_ERR_UNSUPPORTED
+    assert disc(n=8192 * 64 + 1, wpr=257) == vsa.VS_ERR_UNSUPPORTED   # more than 8192 blocks
+    assert disc(ws_bytes=16) == vsa.VS_ERR_WORKSPACE
+    assert L.vs_block_workspace_bytes(2, 1000, 128) == 2 * 2 * 16 * 128 * 2
+    # vs_block_attn_prefill
+    def battn(**kw):
+        a = dict(q=p, k=p, v=p, dt=0, h_q=8, h_kv=2, n=1000, d=128, scale=ctypes.c_float(0.088),
+                 mask=p, wpr=1, out=p, lse=None, ws=p, ws_bytes=256)
+        a.update(kw)
+        return L.vs_block_attn_prefill(a["q"], a["k"], a["v"], a["dt"], a["h_q"], a["h_kv"], a["n"],
+                                       a["d"], a["scale"], a["mask"], a["wpr"], a["out"], a["lse"],
+                                       a["ws"], a["ws_bytes"], None)
+
+    assert battn(mask=None) == vsa.VS_ERR_INVALID
+    assert battn(wpr=0) == vsa.VS_ERR_INVALID
+    assert battn(dt=3) == vsa.VS_ERR_INVALID
+    assert battn(h_q=24) == vsa.VS_ERR_UNSUPPORTED
+    assert battn(d=80) == vsa.VS_ERR_UNSUPPORTED
+    assert battn(scale=ctypes.c_float(float("inf"))) == vsa.VS_ERR_INVALID
+    assert battn(ws_bytes=8) == vsa.VS_ERR_WORKSPACE
+    assert L.vs_block_attn_workspace_bytes() >= 32
     t = (ctypes.c_int64 * 4)()
     assert L.vs_attn_tile_counts(None, 8, 1024, 16, 16, 32, ctypes.cast(t, ctypes.c_void_p), None) == vsa.VS_ERR_INVALID
     assert L.vs_attn_tile_counts(p, 8, 1024, 16, 16, 24, ctypes.cast(t, ctypes.c_void_p), None) == vsa.VS_ERR_UNSUPPORTED

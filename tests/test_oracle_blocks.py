@@ -112,6 +112,18 @@ def test_scores_rows_sum_to_one_and_shift_invariance():
     np.testing.assert_allclose(oracle.block_scores(q, k + c, skel=4), sc, rtol=0, atol=1e-12)
 
 
+def test_scores_selected_rows_match_full():
+    rng = np.random.default_rng(11)
+    hkv, group, n, d = 2, 2, 6 * BS, 8
+    q = rng.standard_normal((hkv * group, n, d))
+    k = rng.standard_normal((hkv, n, d))
+    full = oracle.block_scores(q, k, skel=2)
+    rows = np.array([[0, 5], [1, 0], [1, 3]])
+    part = oracle.block_scores(q, k, skel=2, rows=rows)
+    for r, (g, I) in enumerate(rows):
+        np.testing.assert_array_equal(part[r], full[g, I])
+
+
 def _planted(n, d, group, skel, row_of, hot_block, amp=60.0):
     """Keys: block hot_block along e_0, the rest 0; Q: zero except one row of
     head 0 (row_of), along e_0.  Returns (q, k)."""

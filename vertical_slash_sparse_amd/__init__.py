@@ -10,6 +10,8 @@ calls raise.
     vs_select(logit, kind, mass, cap)              -> (idx, count)
     vs_select_threshold(logit, kind, alpha, cap)   -> (idx, count)
     vs_attn_aggregate(q, k, v)                     -> (out, lse, a_v, a_s)
+    vs_block_discover(q, k, skel, alpha)           -> mask (, score)
+    vs_block_attn_prefill(q, k, v, mask)           -> (out, lse)
     vs_sparse_attn_prefill(q, k, v, v_idx, v_cnt, s_off, s_cnt, scale=None)
                                                    -> (out, lse)
 """
@@ -30,7 +32,9 @@ VS_VERTICAL, VS_SLASH = 0, 1
 
 _SYMBOLS = ("vs_index", "vs_select_workspace_bytes", "vs_select", "vs_select_threshold",
             "vs_attn_workspace_bytes", "vs_aggregate_workspace_bytes", "vs_attn_aggregate",
-            "vs_sparse_attn_prefill", "vs_attn_tile_counts", "vs_status_str")
+            "vs_sparse_attn_prefill", "vs_attn_tile_counts", "vs_block_workspace_bytes",
+            "vs_block_discover", "vs_block_attn_workspace_bytes", "vs_block_attn_prefill",
+            "vs_status_str")
 
 
 class VSError(RuntimeError):
@@ -69,6 +73,15 @@ def lib() -> ctypes.CDLL:
         L.vs_sparse_attn_prefill.restype = i32
         L.vs_attn_tile_counts.argtypes = [P, i32, i32, i32, i32, i32, P, P]
         L.vs_attn_tile_counts.restype = i32
+        L.vs_block_workspace_bytes.argtypes = [i32, i32, i32]
+        L.vs_block_workspace_bytes.restype = sz
+        L.vs_block_discover.argtypes = [P, P, i32, i32, i32, i32, f32, i32, f32, P, i32, P, P, sz, P]
+        L.vs_block_discover.restype = i32
+        L.vs_block_attn_workspace_bytes.argtypes = []
+        L.vs_block_attn_workspace_bytes.restype = sz
+        L.vs_block_attn_prefill.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, i32, P, P, P,
+                                            sz, P]
+        L.vs_block_attn_prefill.restype = i32
         L.vs_status_str.argtypes = [i32]
         L.vs_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -296,6 +309,96 @@ def vs_attn_tile_counts(workspace: torch.Tensor, h_kv: int, n: int, cap_v: int, 
                                    ctypes.cast(tiles, ctypes.c_void_p), _stream(workspace, stream))
     _check("vs_attn_tile_counts", st)
     return tuple(int(x) for x in tiles)
+
+
+BLOCK = 64  # query and key block size of the block-sparse mode
+
+
+def vs_block_workspace_bytes(h_kv: int, n: int, d: int) -> int:
+    return int(lib().vs_block_workspace_bytes(h_kv, n, d))
+
+
+def block_words_per_row(n: int) -> int:
+    return ((n + BLOCK - 1) // BLOCK + 31) // 32
+
+
+def vs_block_discover(q: torch.Tensor, k: torch.Tensor, skel: int, alpha: float,
+                      scale: float | None = None, mask: torch.Tensor | None = None,
+                      want_score: bool = False, workspace: torch.Tensor | None = None,
+                      stream=None):
+    """FlashPrefill block discovery: per (KV head, query block of 64) the key
+    blocks whose skeleton-probe score is at least alpha times the best, and
+    the diagonal block.  q [h_q, n, d], k [h_kv, n, d] bf16.  Returns mask
+    int32 [h_kv, nb, words] (bit b of word w <-> key block 32 w + b; the words
+    are unsigned), plus score fp32 [h_kv, nb, nb] when want_score."""
+    _need(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, 3, dev)
+    h_q, n, d = q.shape
+    h_kv = k.shape[0]
+    if k.shape != (h_kv, n, d):
+        raise ValueError("vs_block_discover: k must be [h_kv, n, d] like q")
+    nb = (n + BLOCK - 1) // BLOCK
+    wpr = block_words_per_row(n)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    mask = torch.empty((h_kv, nb, wpr), dtype=torch.int32, device=dev) if mask is None else mask
+    _need(mask, "mask", torch.int32, 3, dev)
+    if mask.shape[:2] != (h_kv, nb):
+        raise ValueError("vs_block_discover: mask must be [h_kv, nb, words]")
+    score = torch.empty((h_kv, nb, nb), dtype=torch.float32, device=dev) if want_score else None
+    need = vs_block_workspace_bytes(h_kv, n, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = lib().vs_block_discover(_ptr(q), _ptr(k), h_q, h_kv, n, d, scale, int(skel), float(alpha),
+                                 _ptr(mask), mask.shape[2], _ptr(score), _ptr(workspace),
+                                 workspace.numel(), _stream(q, stream))
+    _check("vs_block_discover", st)
+    return (mask, score) if want_score else mask
+
+
+def vs_block_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor,
+                          scale: float | None = None, out: torch.Tensor | None = None,
+                          lse: torch.Tensor | None = None, want_lse: bool = True,
+                          workspace: torch.Tensor | None = None, stream=None):
+    """Block-sparse causal prefill: row i of a query head of KV head g attends
+    to keys j <= i whose block j // 64 is set in mask[g, i // 64].  q [h_q, n,
+    d], k/v [h_kv, n, d] (bf16 or fp32); mask int32 [h_kv, nb, words].
+    Returns (out, lse fp32 [h_q, n])."""
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bf16 or fp32")
+    dt = VS_BF16 if q.dtype == torch.bfloat16 else VS_F32
+    _need(q, "q", q.dtype, 3)
+    dev = q.device
+    _need(k, "k", q.dtype, 3, dev)
+    _need(v, "v", q.dtype, 3, dev)
+    _need(mask, "mask", torch.int32, 3, dev)
+    h_q, n, d = q.shape
+    h_kv = k.shape[0]
+    if k.shape != (h_kv, n, d) or v.shape != k.shape:
+        raise ValueError("vs_block_attn_prefill: k and v must be [h_kv, n, d]")
+    if mask.shape[:2] != (h_kv, (n + BLOCK - 1) // BLOCK):
+        raise ValueError("vs_block_attn_prefill: mask must be [h_kv, nb, words]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", q.dtype, 3, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    if want_lse and lse is None:
+        lse = torch.empty((h_q, n), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+        if lse.shape != (h_q, n):
+            raise ValueError("lse must be [h_q, n]")
+    if workspace is None:
+        workspace = torch.empty(int(lib().vs_block_attn_workspace_bytes()), dtype=torch.uint8,
+                                device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = lib().vs_block_attn_prefill(_ptr(q), _ptr(k), _ptr(v), dt, h_q, h_kv, n, d, scale,
+                                     _ptr(mask), mask.shape[2], _ptr(out), _ptr(lse),
+                                     _ptr(workspace), workspace.numel(), _stream(q, stream))
+    _check("vs_block_attn_prefill", st)
+    return out, lse
 
 
 def exported_symbols():

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libvs.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["vs_api.hip", "vs_attn.hip", "vs_index.hip", "vs_select.hip", "vs_aggregate.hip"]
+SOURCES = ["vs_api.hip", "vs_attn.hip", "vs_index.hip", "vs_select.hip", "vs_aggregate.hip", "vs_blocks.hip"]
 ARCH = os.environ.get("VS_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -122,6 +122,58 @@ vs_status vs_attn_aggregate(const void* q, const void* k, const void* v, int h_q
   return from_hip(launch_aggregate(q, k, v, h_q, h_kv, n, d, scale, out, lse, a_v, a_s, ws, stream));
 }
 
+size_t vs_block_workspace_bytes(int h_kv, int n, int d) {
+  if (h_kv <= 0 || n <= 0 || d <= 0) return 0;
+  return block_workspace_bytes(h_kv, n, d);
+}
+
+vs_status vs_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,
+                            float scale, int skel, float alpha, uint32_t* mask, int words_per_row,
+                            float* score, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !mask || !ws) return VS_ERR_INVALID;
+  if (h_q <= 0 || h_kv <= 0 || n <= 0 || d <= 0 || h_q % h_kv) return VS_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return VS_ERR_INVALID;
+  if (!(alpha > 0.f && alpha <= 1.f)) return VS_ERR_INVALID;
+  if (skel < 1 || skel > kBN || kBN % skel) return VS_ERR_INVALID;
+  if ((long long)n > (1LL << 30) || (long long)h_q * n * d > (1LL << 40)) return VS_ERR_INVALID;
+  const long long nb = ((long long)n + kBN - 1) / kBN;
+  if ((long long)words_per_row * 32 < nb) return VS_ERR_INVALID;
+  if (!group_ok(h_q, h_kv)) return VS_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return VS_ERR_UNSUPPORTED;
+  if ((h_q / h_kv) * skel > 32) return VS_ERR_UNSUPPORTED;
+  if (nb > kBlkMaxBlocks) return VS_ERR_UNSUPPORTED;
+  if (ws_bytes < vs_block_workspace_bytes(h_kv, n, d)) return VS_ERR_WORKSPACE;
+  int dev = 0, lds = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return VS_ERR_HIP;
+  if (block_score_lds_bytes(n) + 1024 > (size_t)lds) return VS_ERR_UNSUPPORTED;
+  return from_hip(launch_block_discover(q, k, h_q, h_kv, n, d, scale, skel, alpha, mask,
+                                        words_per_row, score, ws, stream));
+}
+
+size_t vs_block_attn_workspace_bytes(void) { return 256; }
+
+vs_status vs_block_attn_prefill(const void* q, const void* k, const void* v, vs_dtype dt, int h_q,
+                                int h_kv, int n, int d, float scale, const uint32_t* mask,
+                                int words_per_row, void* out, float* lse, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !mask || !out || !ws) return VS_ERR_INVALID;
+  if (dt != VS_BF16 && dt != VS_F32) return VS_ERR_INVALID;
+  if (h_q <= 0 || h_kv <= 0 || n <= 0 || d <= 0 || h_q % h_kv) return VS_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return VS_ERR_INVALID;
+  // block indices travel in 24 bits beside per-query-block flags
+  if ((long long)n > (1LL << 30) - kBN || (long long)h_kv * n * d > (1LL << 40)) return VS_ERR_INVALID;
+  const long long nb = ((long long)n + kBN - 1) / kBN;
+  if ((long long)words_per_row * 32 < nb) return VS_ERR_INVALID;
+  if (!group_ok(h_q, h_kv)) return VS_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return VS_ERR_UNSUPPORTED;
+  if ((long long)n * d * (dt == VS_F32 ? 4 : 2) >= (1LL << 31)) return VS_ERR_UNSUPPORTED;
+  if (ws_bytes < vs_block_attn_workspace_bytes()) return VS_ERR_WORKSPACE;
+  return from_hip(launch_attn_blocks(q, k, v, dt == VS_F32, h_q, h_kv, n, d, scale, mask,
+                                     words_per_row, out, lse, ws, stream));
+}
+
 vs_status vs_attn_tile_counts(const void* ws, int h_kv, int n, int cap_v, int cap_s, int h_q,
                               int64_t tiles[4], hipStream_t stream) {
   if (!ws || !tiles) return VS_ERR_INVALID;

@@ -205,6 +205,8 @@ struct AttnParams {
   int cap_s;
   const int32_t* counts;
   unsigned long long* stats;
+  const uint32_t* blk;  // block mode: key-block bitmap per (KV head, query block of 64)
+  int blk_wpr;          // its words per row
 };
 
 template <bool F32>
@@ -256,7 +258,7 @@ struct MhalfOrder {
   }
 };
 
-template <int D, bool F32>
+template <int D, bool F32, bool BLK>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   constexpr int KS = D / 16;            // k-steps of Q K^T
   constexpr int DT = D / 32;            // 32-row tiles of O^T
@@ -641,202 +643,305 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     __syncthreads();
   };
 
-  // ---- contiguous tiles: the key ranges the slash clusters reach, in
-  // ascending key order.  Cluster ranges are disjoint (clusters are split
-  // wherever neighbouring offsets differ by more than bmp + 63), so the list
-  // is their concatenation; it is built in LDS windows of kListCap tiles.
-  const int32_t* clo = p.clLo + (size_t)g * p.cap_s;
-  const int32_t* chi = p.clHi + (size_t)g * p.cap_s;
-  int ncb;  // clusters whose smallest offset is at most i1
-  {
-    const int ncl = ldc(p.counts, 4 * g + 2);
-    int lo = 0, hi = ncl;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (ldc(clo, mid) <= i1) lo = mid + 1;
-      else hi = mid;
+  if constexpr (BLK) {
+    // ---- block mode: whole 64-key tiles.  The workgroup's rows fall in
+    // query blocks qb0 .. qb1 (at most four); its tile list is the union of
+    // their kept key blocks at or below each one's diagonal, in ascending
+    // order, each entry carrying in bits 24.. which of the query blocks keep
+    // it.  A wave's rows lie in one query block, so a tile is either in its
+    // set or not, and inside it only the causal mask applies.
+    const int qb0 = i0 / kBN, qb1 = i1 / kBN;
+    const int nbk = (n + kBN - 1) / kBN;
+    const uint32_t* mrow = p.blk + ((size_t)g * nbk + qb0) * p.blk_wpr;
+    const int nwords = qb1 / 32 + 1;
+    // kept blocks of word w for the query blocks of this workgroup, and the
+    // per-query-block words (masked to blocks at or below that query block)
+    auto word_of = [&](int r, int w) -> uint32_t {
+      const int I = qb0 + r;
+      const int lo = 32 * w;
+      const uint32_t causal = I >= lo + 31 ? ~0u : (I < lo ? 0u : ((2u << (I - lo)) - 1u));
+      return mrow[(size_t)r * p.blk_wpr + w] & causal;
+    };
+    auto union_word = [&](int w) -> uint32_t {
+      uint32_t u = 0u;
+      for (int r = 0; r <= qb1 - qb0; ++r) u |= word_of(r, w);
+      return u;
+    };
+    int T_total = 0;
+    for (int w0 = 0; w0 < nwords; w0 += kThreads) {
+      const int cnt = w0 + tid < nwords ? __popc(union_word(w0 + tid)) : 0;
+      int tot;
+      block_excl_scan<kThreads>(cnt, &tot, wcnt);
+      T_total += tot;
     }
-    ncb = lo;
-  }
-  const int tend = (n + kBN - 1) / kBN;  // a tile index past the keys
-  // the j-th cluster in key order covers tiles [tlo, thi]; in a full block
-  // every one of them is active, in the short last block they are tested
-  auto cluster_tiles = [&](int j, int& tlo, int& thi) {
-    const int c = ncb - 1 - j;
-    tlo = max(0, i0 - p.clHi[(size_t)g * p.cap_s + c]) / kBN;
-    thi = (i1 - p.clLo[(size_t)g * p.cap_s + c]) / kBN;
-    if (j > 0) tlo = max(tlo, (i1 - p.clLo[(size_t)g * p.cap_s + c + 1]) / kBN + 1);
-  };
-  auto active_count = [&](int tlo, int thi) -> int {
-    if (!partial) return max(0, thi - tlo + 1);
-    int k = 0;
-    for (int t = tlo; t <= thi; ++t) k += tile_active(t) ? 1 : 0;
-    return k;
-  };
-  int T_total = 0;
-  for (int j0 = 0; j0 < ncb; j0 += kThreads) {
-    int cnt = 0;
-    if (j0 + tid < ncb) {
-      int tlo, thi;
-      cluster_tiles(j0 + tid, tlo, thi);
-      cnt = active_count(tlo, thi);
+    const int tend = nbk;  // a tile index past the keys, in no query block's set
+    const int msh = 24 + (i0w / kBN - qb0);
+    auto key_word_block = [&](int code, uint32_t& kh0, uint32_t& kh1) {
+      const int dq = qrow - (code & 0xFFFFFF) * kBN;  // largest causal key index of this row
+      uint32_t k0 = dq >= 31 ? ~0u : (dq < 0 ? 0u : ((2u << dq) - 1u));
+      uint32_t k1 = dq >= 63 ? ~0u : (dq < 32 ? 0u : ((2u << (dq - 32)) - 1u));
+      if (!((code >> msh) & 1)) k0 = k1 = 0u;
+      kh0 = __builtin_amdgcn_alignbit(k1, k0, 4 * half);
+      kh1 = k1 >> (4 * half);
+    };
+    struct BlockSrc {
+      decltype(stage_tile)& stage_fn;
+      decltype(key_word_block)& key_fn;
+      const int* list;
+      int T, tend;
+      int t, c1, c2, c3, pref;
+      __device__ int code(int i) const {
+        const int x = __builtin_amdgcn_readfirstlane(list[min(i, T - 1)]);
+        return i < T ? x : tend;
+      }
+      __device__ void stage_first() {
+        const int c0 = code(0);
+        c1 = code(1);
+        c2 = code(2);
+        c3 = code(3);
+        t = 0;
+        stage_fn(0, c0 & 0xFFFFFF, KREG);
+        stage_fn(0, c1 & 0xFFFFFF, KREG + TILEB);
+        stage_fn(0, c2 & 0xFFFFFF, KREG + 2 * TILEB);
+        stage_fn(1, c0 & 0xFFFFFF, VREG);
+        stage_fn(1, c1 & 0xFFFFFF, VREG + TILEB);
+      }
+      __device__ void key_word_first(uint32_t& k0, uint32_t& k1) { key_fn(code(0), k0, k1); }
+      __device__ void begin() { pref = list[min(t + 4, T - 1)]; }
+      __device__ void key_word(uint32_t& k0, uint32_t& k1) { key_fn(c1, k0, k1); }
+      __device__ void stage_k(int dst) { stage_fn(0, c3 & 0xFFFFFF, dst); }
+      __device__ void stage_v(int dst) { stage_fn(1, c2 & 0xFFFFFF, dst); }
+      __device__ void rotate() {
+        c1 = c2;
+        c2 = c3;
+        const int x = __builtin_amdgcn_readfirstlane(pref);
+        c3 = t + 4 < T ? x : tend;
+        ++t;
+      }
+    };
+    for (int wst = 0; wst < T_total; wst += kListCap) {
+      int base = 0;
+      for (int w0 = 0; w0 < nwords; w0 += kThreads) {
+        const int w = w0 + tid;
+        const uint32_t u = w < nwords ? union_word(w) : 0u;
+        int tot;
+        int pos = base + block_excl_scan<kThreads>(__popc(u), &tot, wcnt) - wst;
+        for (uint32_t rest = u; rest && pos < kListCap; rest &= rest - 1u) {
+          const int bit = __builtin_ctz(rest);
+          if (pos >= 0) {
+            int memb = 0;
+            for (int r = 0; r <= qb1 - qb0; ++r) memb |= (int)((word_of(r, w) >> bit) & 1u) << r;
+            glist[pos] = (32 * w + bit) | (memb << 24);
+          }
+          ++pos;
+        }
+        base += tot;
+      }
+      __syncthreads();
+      const int T = min(T_total - wst, kListCap);
+      BlockSrc src{stage_tile, key_word_block, glist, T, tend, 0, 0, 0, 0, 0};
+      pipeline(src, T);
+      n_dense += T;
     }
-    int tot;
-    block_excl_scan<kThreads>(cnt, &tot, wcnt);
-    T_total += tot;
-  }
-  // Tile codes for steps t+1, t+2, t+3 live in scalar registers; the code
-  // of t+4 is read from the LDS list one step ahead (unconditionally, from a
-  // clamped index) and the bitmap words of tile t+1 are requested at the
-  // start of the V half, so neither wait sits on the critical path.
-  struct TileSrc {
-    decltype(stage_tile)& stage_fn;
-    decltype(load_words)& load_fn;
-    decltype(key_word_tile)& key_fn;
-    const int* list;
-    int T, tend;
-    int t, c1, c2, c3, pref;
-    BitWords w;
-    __device__ int code(int i) const {
-      const int x = __builtin_amdgcn_readfirstlane(list[min(i, T - 1)]);
-      return i < T ? x : tend;
+  } else {
+    // ---- contiguous tiles: the key ranges the slash clusters reach, in
+    // ascending key order.  Cluster ranges are disjoint (clusters are split
+    // wherever neighbouring offsets differ by more than bmp + 63), so the list
+    // is their concatenation; it is built in LDS windows of kListCap tiles.
+    const int32_t* clo = p.clLo + (size_t)g * p.cap_s;
+    const int32_t* chi = p.clHi + (size_t)g * p.cap_s;
+    int ncb;  // clusters whose smallest offset is at most i1
+    {
+      const int ncl = ldc(p.counts, 4 * g + 2);
+      int lo = 0, hi = ncl;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (ldc(clo, mid) <= i1) lo = mid + 1;
+        else hi = mid;
+      }
+      ncb = lo;
     }
-    __device__ void stage_first() {
-      const int c0 = code(0);
-      c1 = code(1);
-      c2 = code(2);
-      c3 = code(3);
-      t = 0;
-      stage_fn(0, c0, KREG);
-      stage_fn(0, c1, KREG + TILEB);
-      stage_fn(0, c2, KREG + 2 * TILEB);
-      stage_fn(1, c0, VREG);
-      stage_fn(1, c1, VREG + TILEB);
-      load_fn(c0, w);
-    }
-    __device__ void key_word_first(uint32_t& k0, uint32_t& k1) { key_fn(code(0), w, k0, k1); }
-    __device__ void begin() {
-      load_fn(c1, w);
-      pref = list[min(t + 4, T - 1)];
-    }
-    __device__ void key_word(uint32_t& k0, uint32_t& k1) { key_fn(c1, w, k0, k1); }
-    __device__ void stage_k(int dst) { stage_fn(0, c3, dst); }
-    __device__ void stage_v(int dst) { stage_fn(1, c2, dst); }
-    __device__ void rotate() {
-      c1 = c2;
-      c2 = c3;
-      const int x = __builtin_amdgcn_readfirstlane(pref);
-      c3 = t + 4 < T ? x : tend;
-      ++t;
-    }
-  };
-  for (int wst = 0; wst < T_total; wst += kListCap) {
-    int base = 0;
+    const int tend = (n + kBN - 1) / kBN;  // a tile index past the keys
+    // the j-th cluster in key order covers tiles [tlo, thi]; in a full block
+    // every one of them is active, in the short last block they are tested
+    auto cluster_tiles = [&](int j, int& tlo, int& thi) {
+      const int c = ncb - 1 - j;
+      tlo = max(0, i0 - p.clHi[(size_t)g * p.cap_s + c]) / kBN;
+      thi = (i1 - p.clLo[(size_t)g * p.cap_s + c]) / kBN;
+      if (j > 0) tlo = max(tlo, (i1 - p.clLo[(size_t)g * p.cap_s + c + 1]) / kBN + 1);
+    };
+    auto active_count = [&](int tlo, int thi) -> int {
+      if (!partial) return max(0, thi - tlo + 1);
+      int k = 0;
+      for (int t = tlo; t <= thi; ++t) k += tile_active(t) ? 1 : 0;
+      return k;
+    };
+    int T_total = 0;
     for (int j0 = 0; j0 < ncb; j0 += kThreads) {
-      int cnt = 0, tlo = 0, thi = -1;
+      int cnt = 0;
       if (j0 + tid < ncb) {
+        int tlo, thi;
         cluster_tiles(j0 + tid, tlo, thi);
         cnt = active_count(tlo, thi);
       }
       int tot;
-      int pos = base + block_excl_scan<kThreads>(cnt, &tot, wcnt) - wst;
-      for (int t = tlo; t <= thi && pos < kListCap; ++t) {
-        if (partial && !tile_active(t)) continue;
-        if (pos >= 0) glist[pos] = t;
-        ++pos;
-      }
-      base += tot;
+      block_excl_scan<kThreads>(cnt, &tot, wcnt);
+      T_total += tot;
     }
-    __syncthreads();
-    const int T = min(T_total - wst, kListCap);
-    TileSrc src{stage_tile, load_words, key_word_tile, glist, T, tend, 0, 0, 0, 0, 0, {}};
-    pipeline(src, T);
-    n_dense += T;
-  }
+    // Tile codes for steps t+1, t+2, t+3 live in scalar registers; the code
+    // of t+4 is read from the LDS list one step ahead (unconditionally, from a
+    // clamped index) and the bitmap words of tile t+1 are requested at the
+    // start of the V half, so neither wait sits on the critical path.
+    struct TileSrc {
+      decltype(stage_tile)& stage_fn;
+      decltype(load_words)& load_fn;
+      decltype(key_word_tile)& key_fn;
+      const int* list;
+      int T, tend;
+      int t, c1, c2, c3, pref;
+      BitWords w;
+      __device__ int code(int i) const {
+        const int x = __builtin_amdgcn_readfirstlane(list[min(i, T - 1)]);
+        return i < T ? x : tend;
+      }
+      __device__ void stage_first() {
+        const int c0 = code(0);
+        c1 = code(1);
+        c2 = code(2);
+        c3 = code(3);
+        t = 0;
+        stage_fn(0, c0, KREG);
+        stage_fn(0, c1, KREG + TILEB);
+        stage_fn(0, c2, KREG + 2 * TILEB);
+        stage_fn(1, c0, VREG);
+        stage_fn(1, c1, VREG + TILEB);
+        load_fn(c0, w);
+      }
+      __device__ void key_word_first(uint32_t& k0, uint32_t& k1) { key_fn(code(0), w, k0, k1); }
+      __device__ void begin() {
+        load_fn(c1, w);
+        pref = list[min(t + 4, T - 1)];
+      }
+      __device__ void key_word(uint32_t& k0, uint32_t& k1) { key_fn(c1, w, k0, k1); }
+      __device__ void stage_k(int dst) { stage_fn(0, c3, dst); }
+      __device__ void stage_v(int dst) { stage_fn(1, c2, dst); }
+      __device__ void rotate() {
+        c1 = c2;
+        c2 = c3;
+        const int x = __builtin_amdgcn_readfirstlane(pref);
+        c3 = t + 4 < T ? x : tend;
+        ++t;
+      }
+    };
+    for (int wst = 0; wst < T_total; wst += kListCap) {
+      int base = 0;
+      for (int j0 = 0; j0 < ncb; j0 += kThreads) {
+        int cnt = 0, tlo = 0, thi = -1;
+        if (j0 + tid < ncb) {
+          cluster_tiles(j0 + tid, tlo, thi);
+          cnt = active_count(tlo, thi);
+        }
+        int tot;
+        int pos = base + block_excl_scan<kThreads>(cnt, &tot, wcnt) - wst;
+        for (int t = tlo; t <= thi && pos < kListCap; ++t) {
+          if (partial && !tile_active(t)) continue;
+          if (pos >= 0) glist[pos] = t;
+          ++pos;
+        }
+        base += tot;
+      }
+      __syncthreads();
+      const int T = min(T_total - wst, kListCap);
+      TileSrc src{stage_tile, load_words, key_word_tile, glist, T, tend, 0, 0, 0, 0, 0, {}};
+      pipeline(src, T);
+      n_dense += T;
+    }
 
-  // ---- gathered tiles: selected columns in no active tile, 64 per tile
-  const int32_t* cv = p.cleanV + (size_t)g * p.cap_v;
-  int total_v;
-  {
-    const int nv = ldc(p.counts, 4 * g + 1);
-    int lo = 0, hi = nv;  // columns <= i1
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (ldc(cv, mid) <= i1) lo = mid + 1;
-      else hi = mid;
-    }
-    total_v = lo;
-  }
-  auto stage_chunk = [&](int which, int t, int nch, int dst) {
-    int key[NDMA];
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) key[i] = t < nch ? glist[t * kBN + dma_row[i]] : n;
-    stage_keys(which, key, dst);
-  };
-  struct ChunkSrc {
-    decltype(stage_chunk)& stage_fn;
-    decltype(key_word_chunk)& key_fn;
-    const int* list;
-    int T, t;
-    __device__ void kw(int i, uint32_t& k0, uint32_t& k1) {
-      if (i < T) {
-        key_fn(list + i * kBN, k0, k1);
-      } else {
-        k0 = 0u;
-        k1 = 0u;
+    // ---- gathered tiles: selected columns in no active tile, 64 per tile
+    const int32_t* cv = p.cleanV + (size_t)g * p.cap_v;
+    int total_v;
+    {
+      const int nv = ldc(p.counts, 4 * g + 1);
+      int lo = 0, hi = nv;  // columns <= i1
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (ldc(cv, mid) <= i1) lo = mid + 1;
+        else hi = mid;
       }
+      total_v = lo;
     }
-    __device__ void stage_first() {
-      t = 0;
-      stage_fn(0, 0, T, KREG);
-      stage_fn(0, 1, T, KREG + TILEB);
-      stage_fn(0, 2, T, KREG + 2 * TILEB);
-      stage_fn(1, 0, T, VREG);
-      stage_fn(1, 1, T, VREG + TILEB);
-    }
-    __device__ void key_word_first(uint32_t& k0, uint32_t& k1) { kw(0, k0, k1); }
-    __device__ void begin() {}
-    __device__ void key_word(uint32_t& k0, uint32_t& k1) { kw(t + 1, k0, k1); }
-    __device__ void stage_k(int dst) { stage_fn(0, t + 3, T, dst); }
-    __device__ void stage_v(int dst) { stage_fn(1, t + 2, T, dst); }
-    __device__ void rotate() { ++t; }
-  };
-  int cursor = 0;
-  while (cursor < total_v) {
-    // gather the next batch of columns whose tile no offset reaches
-    int fill = 0;
-    while (cursor < total_v && fill + kThreads <= kListCap) {
-      const int idx = cursor + tid;
-      bool keep = false;
-      int col = 0;
-      if (idx < total_v) {
-        col = cv[idx];
-        keep = !tile_active(col / kBN);
+    auto stage_chunk = [&](int which, int t, int nch, int dst) {
+      int key[NDMA];
+  #pragma unroll
+      for (int i = 0; i < NDMA; ++i) key[i] = t < nch ? glist[t * kBN + dma_row[i]] : n;
+      stage_keys(which, key, dst);
+    };
+    struct ChunkSrc {
+      decltype(stage_chunk)& stage_fn;
+      decltype(key_word_chunk)& key_fn;
+      const int* list;
+      int T, t;
+      __device__ void kw(int i, uint32_t& k0, uint32_t& k1) {
+        if (i < T) {
+          key_fn(list + i * kBN, k0, k1);
+        } else {
+          k0 = 0u;
+          k1 = 0u;
+        }
       }
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
-      const int below_l = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-      if (lane == 0) wcnt[wave] = __popcll(bal);
+      __device__ void stage_first() {
+        t = 0;
+        stage_fn(0, 0, T, KREG);
+        stage_fn(0, 1, T, KREG + TILEB);
+        stage_fn(0, 2, T, KREG + 2 * TILEB);
+        stage_fn(1, 0, T, VREG);
+        stage_fn(1, 1, T, VREG + TILEB);
+      }
+      __device__ void key_word_first(uint32_t& k0, uint32_t& k1) { kw(0, k0, k1); }
+      __device__ void begin() {}
+      __device__ void key_word(uint32_t& k0, uint32_t& k1) { kw(t + 1, k0, k1); }
+      __device__ void stage_k(int dst) { stage_fn(0, t + 3, T, dst); }
+      __device__ void stage_v(int dst) { stage_fn(1, t + 2, T, dst); }
+      __device__ void rotate() { ++t; }
+    };
+    int cursor = 0;
+    while (cursor < total_v) {
+      // gather the next batch of columns whose tile no offset reaches
+      int fill = 0;
+      while (cursor < total_v && fill + kThreads <= kListCap) {
+        const int idx = cursor + tid;
+        bool keep = false;
+        int col = 0;
+        if (idx < total_v) {
+          col = cv[idx];
+          keep = !tile_active(col / kBN);
+        }
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+        const int below_l = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (lane == 0) wcnt[wave] = __popcll(bal);
+        __syncthreads();
+        int before = 0, all = 0;
+  #pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const int cw = wcnt[w];
+          before += w < wave ? cw : 0;
+          all += cw;
+        }
+        if (keep) glist[fill + before + below_l] = col;
+        fill += all;
+        cursor += kThreads;
+        __syncthreads();
+      }
+      if (fill == 0) continue;
+      // pad the last chunk with n: sorts after every key, reads as zeros
+      for (int r = fill + tid; r < ((fill + kBN - 1) / kBN) * kBN; r += kThreads) glist[r] = n;
       __syncthreads();
-      int before = 0, all = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const int cw = wcnt[w];
-        before += w < wave ? cw : 0;
-        all += cw;
-      }
-      if (keep) glist[fill + before + below_l] = col;
-      fill += all;
-      cursor += kThreads;
-      __syncthreads();
+      const int nch = (fill + kBN - 1) / kBN;
+      ChunkSrc src{stage_chunk, key_word_chunk, glist, nch, 0};
+      pipeline(src, nch);
+      n_gath += nch;
     }
-    if (fill == 0) continue;
-    // pad the last chunk with n: sorts after every key, reads as zeros
-    for (int r = fill + tid; r < ((fill + kBN - 1) / kBN) * kBN; r += kThreads) glist[r] = n;
-    __syncthreads();
-    const int nch = (fill + kBN - 1) / kBN;
-    ChunkSrc src{stage_chunk, key_word_chunk, glist, nch, 0};
-    pipeline(src, nch);
-    n_gath += nch;
+
   }
 
   // ---------------- finish: normalise, write O and lse
@@ -861,7 +966,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     if (half == 0 && p.lse)
       p.lse[(size_t)head * n + qrow] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -__builtin_inff();
   }
-  if (tid == 0) {
+  if (tid == 0 && p.stats) {
     atomicAdd(&p.stats[0], (unsigned long long)n_dense);
     atomicAdd(&p.stats[1], (unsigned long long)n_gath);
   }
@@ -938,13 +1043,52 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
   prm.cap_s = cap_s;
   prm.counts = counts;
   prm.stats = stats;
+  prm.blk = nullptr;
+  prm.blk_wpr = 0;
   const dim3 grid((unsigned)((long long)prm.nblocks * h_kv * nsplit));
   if (d == 128) {
-    if (f32) hipLaunchKernelGGL((attn_kernel<128, true>), grid, dim3(kThreads), 0, stream, prm);
-    else hipLaunchKernelGGL((attn_kernel<128, false>), grid, dim3(kThreads), 0, stream, prm);
+    if (f32) hipLaunchKernelGGL((attn_kernel<128, true, false>), grid, dim3(kThreads), 0, stream, prm);
+    else hipLaunchKernelGGL((attn_kernel<128, false, false>), grid, dim3(kThreads), 0, stream, prm);
   } else {
-    if (f32) hipLaunchKernelGGL((attn_kernel<64, true>), grid, dim3(kThreads), 0, stream, prm);
-    else hipLaunchKernelGGL((attn_kernel<64, false>), grid, dim3(kThreads), 0, stream, prm);
+    if (f32) hipLaunchKernelGGL((attn_kernel<64, true, false>), grid, dim3(kThreads), 0, stream, prm);
+    else hipLaunchKernelGGL((attn_kernel<64, false, false>), grid, dim3(kThreads), 0, stream, prm);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_blocks(const void* q, const void* k, const void* v, bool f32, int h_q,
+                              int h_kv, int n, int d, float scale, const uint32_t* blk, int wpr,
+                              void* out, float* lse, void* ws, hipStream_t stream) {
+  unsigned long long* stats = static_cast<unsigned long long*>(ws);
+  hipLaunchKernelGGL(ws_clear_kernel, dim3(1), dim3(64), 0, stream, nullptr, nullptr, (size_t)0, stats);
+  const int group = h_q / h_kv;
+  const int hpw = heads_per_block(group);
+  const int nsplit = group / hpw;
+  const int bmp = 32 * (kWaves / hpw);
+  AttnParams prm = {};
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.out = out;
+  prm.lse = lse;
+  prm.n = n;
+  prm.hkv = h_kv;
+  prm.group = group;
+  prm.hpw = hpw;
+  prm.nsplit = nsplit;
+  prm.bmp = bmp;
+  prm.nblocks = (n + bmp - 1) / bmp;
+  prm.c = scale * kLog2e;
+  prm.stats = stats;
+  prm.blk = blk;
+  prm.blk_wpr = wpr;
+  const dim3 grid((unsigned)((long long)prm.nblocks * h_kv * nsplit));
+  if (d == 128) {
+    if (f32) hipLaunchKernelGGL((attn_kernel<128, true, true>), grid, dim3(kThreads), 0, stream, prm);
+    else hipLaunchKernelGGL((attn_kernel<128, false, true>), grid, dim3(kThreads), 0, stream, prm);
+  } else {
+    if (f32) hipLaunchKernelGGL((attn_kernel<64, true, true>), grid, dim3(kThreads), 0, stream, prm);
+    else hipLaunchKernelGGL((attn_kernel<64, false, true>), grid, dim3(kThreads), 0, stream, prm);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,264 @@
+// vs_blocks.hip -- FlashPrefill block discovery for gfx950: block-mean keys,
+// skeleton-probe block scores and the max-based threshold, written out as a
+// per-query-block bitmap of key blocks.
+//
+// What is computed (FlashPrefill, gist.science summary of arXiv 2603.06199,
+// Spanish page, section 2.A "Estrategia de Aproximacion de Bloques" and 2.B
+// "Umbralizacion Dinamica Basada en Maximos"): a sparse set of evenly spaced
+// probe queries of each query block is scored against the mean key of every
+// earlier key block (exp of that score is the geometric mean of the block's
+// exponentials, the AM-GM proxy); a block's score is the probes' softmax
+// probability of it, averaged over the probes; a query block keeps the key
+// blocks scoring at least alpha times its best, and always its own diagonal
+// block.  Blocks are 64 positions, the attention kernel's key tile.
+//
+// Layout on the chip
+//  * blk_mean_kernel: one workgroup per (KV head, key block) sums the block's
+//    rows in fp32 (each thread one 16-byte column chunk over a strided set of
+//    rows, then the row groups meet in LDS) and stores the mean as a bf16
+//    pair hi + lo (hi = bf16(mean), lo = bf16(mean - hi)), about 16
+//    significant bits, so the matrix cores can take it.
+//  * blk_score_kernel: one wave per query block, four per workgroup.  The
+//    wave's 32 probe rows (G heads x skel rows, zero-padded) are one MFMA
+//    operand held in registers; the block means stream through in chunks of
+//    32 blocks straight from L2 (every probe row needs every earlier block
+//    once, so there is nothing to reuse from LDS).  Pass 1 runs
+//    S^T = Kbar Q^T, so each lane owns one probe and keeps its running max
+//    and sum over blocks; pass 2 runs S = Q Kbar^T, so each lane owns one
+//    block and adds the probes' normalised probabilities over its elements.
+//    Scores stay in LDS until the row maximum is known; the threshold is one
+//    fp32 product and the kept flags become mask words through ballots.
+#include "vs_common.h"
+#include "vs_internal.h"
+
+namespace vs {
+
+namespace {
+
+constexpr int kBlkWaves = 4;  // query blocks per workgroup
+constexpr int kBlkThreads = kBlkWaves * 64;
+constexpr float kNegBig = -1.0e30f;
+
+struct BlkParams {
+  const uint16_t* q;    // bf16 [hq][n][d]
+  const uint16_t* khi;  // bf16 [hkv][nb][d]: mean keys, high part
+  const uint16_t* klo;  // low part
+  uint32_t* mask;       // [hkv][nb][wpr]
+  float* score;         // optional [hkv][nb][nb]
+  int n, nb, hkv, group, skel, wpr;
+  float c;              // scale * log2(e)
+  float alpha;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void blk_mean_kernel(const uint16_t* __restrict__ k,
+                                                       uint16_t* __restrict__ khi,
+                                                       uint16_t* __restrict__ klo, int n, int nb) {
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int RG = 256 / CH;         // row groups
+  __shared__ float part[RG][D];
+  const int J = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, ch = tid % CH, rg = tid / CH;
+  const int j0 = J * kBN;
+  const int cnt = min(kBN, n - j0);
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = rg; r < cnt; r += RG) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(k + ((size_t)g * n + j0 + r) * D + 8 * ch);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[2 * e] += bf16_lo(w[e]);
+      s[2 * e + 1] += bf16_hi(w[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rg][8 * ch + e] = s[e];
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.f;
+    for (int r = 0; r < RG; ++r) t += part[r][tid];
+    const float mean = t / (float)cnt;
+    const __bf16 hi = (__bf16)mean;
+    const __bf16 lo = (__bf16)(mean - (float)hi);
+    const size_t o = ((size_t)g * nb + J) * D + tid;
+    khi[o] = __builtin_bit_cast(uint16_t, hi);
+    klo[o] = __builtin_bit_cast(uint16_t, lo);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
+  constexpr int KS = D / 16;
+  extern __shared__ float sc_all[];                 // [kBlkWaves][nb] block scores
+  __shared__ float st_m[kBlkWaves][32], st_w[kBlkWaves][32];  // per probe: max, weight / sum
+
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, ql = lane & 31;
+  const int wave = wave_uniform(tid >> 6);
+  const int g = blockIdx.x % p.hkv;
+  const int nbw = (p.nb + kBlkWaves - 1) / kBlkWaves;
+  const int I = (nbw - 1 - (int)(blockIdx.x / p.hkv)) * kBlkWaves + wave;  // longest rows first
+  const bool active = I < p.nb;
+  float* sc = sc_all + wave * p.nb;
+  const int n = p.n, nb = p.nb;
+
+  // probe slot ql: head ql / skel of the group, row 64 I + (ql % skel) * (64 / skel)
+  const int step = kBN / p.skel;
+  const int slot_head = ql / p.skel, slot_m = ql % p.skel;
+  const int prow = I * kBN + slot_m * step;
+  const bool probe = active && slot_head < p.group && prow < n;
+  // number of probes of this query block: G x (rows below n)
+  const int rows_in = active ? min(p.skel, (n - I * kBN + step - 1) / step) : 1;
+  const float weight = 1.f / (float)(p.group * rows_in);
+  bf16x8 qf[KS];
+  {
+    const int h = g * p.group + min(slot_head, p.group - 1);
+    const size_t ro = ((size_t)h * n + min(prow, n - 1)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(p.q + ro + 16 * s + 8 * half);
+      if (!probe) raw = u32x4{0u, 0u, 0u, 0u};
+      qf[s] = as_bf16x8(raw);
+    }
+  }
+  // mean-key fragment of block J (this lane's row): dims 16 s + 8 half ..
+  auto kfrag = [&](const uint16_t* base, int J, int s) -> bf16x8 {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(base + ((size_t)g * nb + J) * D + 16 * s + 8 * half));
+  };
+  const int nchunk = active ? (I + 31) / 32 : 0;  // candidates are blocks 0 .. I-1
+
+  // ---- pass 1: S^T = Kbar Q^T; lane (ql, half) holds probe ql against
+  // blocks 32 c + 8 (e / 4) + 4 half + e % 4
+  float m2 = kNegBig, l = 0.f;
+  for (int c = 0; c < nchunk; ++c) {
+    const int Jr = min(c * 32 + ql, nb - 1);
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = mfma32(kfrag(p.khi, Jr, s), qf[s], acc);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = mfma32(kfrag(p.klo, Jr, s), qf[s], acc);
+    float z[16];
+    float mloc = kNegBig;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int J = c * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+      z[e] = J < I ? acc[e] * p.c : kNegBig;
+      mloc = fmaxf(mloc, z[e]);
+    }
+    const float mn = fmaxf(m2, mloc);
+    float add = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) add += z[e] > kNegBig ? __builtin_amdgcn_exp2f(z[e] - mn) : 0.f;
+    l = l * __builtin_amdgcn_exp2f(m2 - mn) + add;
+    m2 = mn;
+  }
+  {
+    // the two halves of the wave saw different blocks of the same probe
+    const auto sm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m2), __float_as_uint(m2), false, false);
+    const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+    const float ma = __uint_as_float(sm[0]), mb = __uint_as_float(sm[1]);
+    const float M = fmaxf(ma, mb);
+    const float L = __uint_as_float(sl[0]) * __builtin_amdgcn_exp2f(ma - M) +
+                    __uint_as_float(sl[1]) * __builtin_amdgcn_exp2f(mb - M);
+    if (half == 0) {
+      st_m[wave][ql] = M;
+      st_w[wave][ql] = probe && L > 0.f ? weight / L : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- pass 2: S = Q Kbar^T; lane (ql, half) holds block 32 c + ql against
+  // probes 8 (e / 4) + 4 half + e % 4
+  float nm[16], wl[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int pr = 8 * (e >> 2) + 4 * half + (e & 3);
+    nm[e] = -st_m[wave][pr];
+    wl[e] = st_w[wave][pr];
+  }
+  for (int c = 0; c < nchunk; ++c) {
+    const int J = c * 32 + ql;
+    const int Jr = min(J, nb - 1);
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = mfma32(qf[s], kfrag(p.khi, Jr, s), acc);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = mfma32(qf[s], kfrag(p.klo, Jr, s), acc);
+    float t = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t += __builtin_amdgcn_exp2f(fmaf(acc[e], p.c, nm[e])) * wl[e];
+    t = half_sum(t);
+    if (half == 0 && J < nb) sc[J] = J < I ? t : 0.f;
+  }
+  __syncthreads();
+  if (!active) return;
+
+  // ---- threshold: alpha times the row's largest score, one fp32 product
+  float mx = 0.f;
+  for (int J = lane; J < I; J += 64) mx = fmaxf(mx, sc[J]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  const float thr = __fmul_rn(p.alpha, mx);
+  uint32_t* mrow = p.mask + ((size_t)g * nb + I) * p.wpr;
+  for (int w0 = 0; w0 < p.wpr; w0 += 2) {
+    const int J = 32 * w0 + lane;
+    const bool keep = J == I || (J < I && sc[J] >= thr);
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+    if (lane == 0) mrow[w0] = (uint32_t)bal;
+    if (lane == 32 && w0 + 1 < p.wpr) mrow[w0 + 1] = (uint32_t)(bal >> 32);
+  }
+  if (p.score) {
+    float* srow = p.score + ((size_t)g * nb + I) * nb;
+    for (int J = lane; J < nb; J += 64) srow[J] = J < I ? sc[J] : 0.f;
+  }
+}
+
+}  // namespace
+
+size_t block_workspace_bytes(int h_kv, int n, int d) {
+  const size_t nb = (size_t)(n + kBN - 1) / kBN;
+  return 2 * align_up(sizeof(uint16_t) * (size_t)h_kv * nb * d, 256);
+}
+
+size_t block_score_lds_bytes(int n) {
+  return sizeof(float) * (size_t)kBlkWaves * (size_t)((n + kBN - 1) / kBN);
+}
+
+hipError_t launch_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,
+                                 float scale, int skel, float alpha, uint32_t* mask, int wpr,
+                                 float* score, void* ws, hipStream_t stream) {
+  const int nb = (n + kBN - 1) / kBN;
+  uint16_t* khi = static_cast<uint16_t*>(ws);
+  uint16_t* klo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
+                                              align_up(sizeof(uint16_t) * (size_t)h_kv * nb * d, 256));
+  const dim3 mg((unsigned)nb, (unsigned)h_kv);
+  if (d == 128)
+    hipLaunchKernelGGL(blk_mean_kernel<128>, mg, dim3(256), 0, stream, static_cast<const uint16_t*>(k), khi, klo, n, nb);
+  else
+    hipLaunchKernelGGL(blk_mean_kernel<64>, mg, dim3(256), 0, stream, static_cast<const uint16_t*>(k), khi, klo, n, nb);
+  BlkParams prm;
+  prm.q = static_cast<const uint16_t*>(q);
+  prm.khi = khi;
+  prm.klo = klo;
+  prm.mask = mask;
+  prm.score = score;
+  prm.n = n;
+  prm.nb = nb;
+  prm.hkv = h_kv;
+  prm.group = h_q / h_kv;
+  prm.skel = skel;
+  prm.wpr = wpr;
+  prm.c = scale * 1.4426950408889634f;
+  prm.alpha = alpha;
+  const dim3 sg((unsigned)(((nb + kBlkWaves - 1) / kBlkWaves) * h_kv));
+  const size_t lds = block_score_lds_bytes(n);
+  if (d == 128)
+    hipLaunchKernelGGL(blk_score_kernel<128>, sg, dim3(kBlkThreads), lds, stream, prm);
+  else
+    hipLaunchKernelGGL(blk_score_kernel<64>, sg, dim3(kBlkThreads), lds, stream, prm);
+  return hipGetLastError();
+}
+
+}  // namespace vs

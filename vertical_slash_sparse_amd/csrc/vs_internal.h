@@ -68,6 +68,19 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
 int attn_query_rows_per_block(int group);
 
 size_t aggregate_workspace_bytes(int h_kv, int n);
+// block-sparse mode of the attention kernel: ws holds 32 bytes of counters
+hipError_t launch_attn_blocks(const void* q, const void* k, const void* v, bool f32, int h_q,
+                              int h_kv, int n, int d, float scale, const uint32_t* blk, int wpr,
+                              void* out, float* lse, void* ws, hipStream_t stream);
+
+// FlashPrefill block discovery
+constexpr int kBlkMaxBlocks = 8192;  // key blocks a discovery call may have
+size_t block_workspace_bytes(int h_kv, int n, int d);
+size_t block_score_lds_bytes(int n);
+hipError_t launch_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,
+                                 float scale, int skel, float alpha, uint32_t* mask, int wpr,
+                                 float* score, void* ws, hipStream_t stream);
+
 hipError_t launch_aggregate(const void* q, const void* k, const void* v, int h_q, int h_kv, int n,
                             int d, float scale, void* out, float* lse, float* a_v, float* a_s,
                             void* ws, hipStream_t stream);
