@@ -141,7 +141,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="zipf128k",
-                    choices=["zipf128k", "fixed32k", "indexer128k", "e2e256k", "aggregate32k"])
+                    choices=["zipf128k", "fixed32k", "indexer128k", "e2e256k", "aggregate32k",
+                             "blocks128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--alpha", type=float, default=0.01,
@@ -168,6 +169,8 @@ def main():
         return bench_indexer(args, w, torch, vsa, workloads)
     if args.workload == "aggregate32k":
         return bench_aggregate(args, torch, vsa, workloads)
+    if args.workload == "blocks128k":
+        return bench_blocks(args, torch, vsa, workloads)
 
     n, hq, hkv, d = w["n"], w["hq"], w["hkv"], w["d"]
     group = hq // hkv
@@ -399,6 +402,80 @@ def bench_aggregate(args, torch, vsa, workloads):
                      "achieved": round(f2 / (ms2 * 1e-3) / 1e12, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(f2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_blocks(args, torch, vsa, workloads):
+    """FlashPrefill block path on the planted-structure 128K layer (32/8
+    heads, d=128): one step = vs_block_discover (block means, probe scores,
+    alpha*max threshold) + vs_block_attn_prefill on inputs resident in HBM."""
+    w = workloads.WORKLOADS["blocks128k"]
+    n, hq, hkv, d, bs = w["n"], w["hq"], w["hkv"], w["d"], w["block"]
+    group = hq // hkv
+    assert group == 4, "tile accounting below assumes one 64-row query block per workgroup"
+    t_gen = time.perf_counter()
+    q, k, v = workloads.block_structured_inputs("blocks128k")
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    qd, kd, vd = _dev(q, torch), _dev(k, torch), _dev(v, torch)
+    nb = (n + bs - 1) // bs
+    wpr = vsa.block_words_per_row(n)
+    mask = torch.empty((hkv, nb, wpr), dtype=torch.int32, device="cuda")
+    dws = torch.empty(vsa.vs_block_workspace_bytes(hkv, n, d), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(qd)
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    td, ta = [], []
+    for it in range(args.warmup + args.steps):
+        e[0].record()
+        vsa.vs_block_discover(qd, kd, w["skel"], w["alpha"], mask=mask, workspace=dws)
+        e[1].record()
+        vsa.vs_block_attn_prefill(qd, kd, vd, mask, out=out, lse=lse, workspace=aws)
+        e[2].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            td.append(e[0].elapsed_time(e[1]))
+            ta.append(e[1].elapsed_time(e[2]))
+    ms_d, ms_a = float(np.mean(td)), float(np.mean(ta))
+    ms = ms_d + ms_a
+    m = mask.cpu().numpy().view(np.uint32)
+    bits = np.unpackbits(m.view(np.uint8), axis=-1, bitorder="little")[..., :nb].astype(bool)
+    bits &= np.tril(np.ones((nb, nb), bool))[None]          # the kernel ignores blocks past the diagonal
+    tiles = int(bits.sum())                                  # one workgroup per (KV head, query block)
+    rows_in = np.minimum(bs, n - bs * np.arange(nb))         # rows of each query block
+    # pairs: full kept blocks below the diagonal, triangle of the diagonal block
+    off = bits.copy()
+    off[:, np.arange(nb), np.arange(nb)] = False
+    pairs = float((off.sum(-1) * bs * rows_in[None]).sum())
+    diag = bits[:, np.arange(nb), np.arange(nb)]
+    pairs += float((diag * (rows_in * (rows_in + 1) / 2)[None]).sum())
+    f_alg = 4.0 * d * group * pairs
+    f_tile = 4.0 * d * (group * bs) * bs * tiles
+    causal_tiles = hkv * nb * (nb + 1) / 2
+    probe_flops = 0.0
+    for I in range(1, nb):                                   # 2 passes x (hi, lo) x 32 probes
+        probe_flops += 2 * 2 * 2.0 * d * 32 * 32 * ((I + 31) // 32)
+    probe_flops *= hkv
+    eff = f_alg / (ms * 1e-3) / 1e12
+    achieved = f_alg / (ms_a * 1e-3) / 1e12
+    res = {
+        "metric": "FlashPrefill block-sparse layer, effective TFLOP/s @128K (discovery + attention)",
+        "value": round(eff, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "blocks128k", "n": n, "h_q": hq, "h_kv": hkv, "d": d,
+                   "alpha": w["alpha"], "skel": w["skel"], "seed": w["seed"]},
+        "discover_ms": round(ms_d, 4), "attn_ms": round(ms_a, 4),
+        "discover_frac": round(ms_d / ms, 4),
+        "discover_mfma_tflops": round(probe_flops / (ms_d * 1e-3) / 1e12, 3),
+        "tile_density": round(tiles / causal_tiles, 5),
+        "pair_density": round(pairs / (hkv * n * (n + 1) / 2), 5),
+        "tile_tflops": round(f_tile / (ms_a * 1e-3) / 1e12, 3),
+        "pct_peak_tile": round(100.0 * f_tile / (ms_a * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 3),
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel block mode (vs_block_attn_prefill)",
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 5), "traffic": None},
     }
     print(json.dumps(res), flush=True)
 

@@ -22,6 +22,11 @@ head dim 128, one of the backbones the VSPrefill pages evaluate on):
   random indexer weights W1 ~ N(0, 1/256), W2 ~ N(0, 1/128)
 * ``e2e256k`` 32/8 heads, n=262144, bf16, RoPE, keys of the first 4 positions
   scaled by 4 (attention sinks), indexer -> selection at 0.95 uncapped
+* ``blocks128k`` 32/8 heads, n=131072, bf16, no RoPE, planted block structure
+  for the FlashPrefill block path: every 64-key block carries one of 32 unit
+  topic directions (amplitude 8), every query block looks for the topic of a
+  uniformly drawn earlier block (amplitude 8), and block 0 carries a sink
+  direction shared by all queries (amplitude 8 on both sides)
 """
 from __future__ import annotations
 
@@ -41,6 +46,8 @@ WORKLOADS = {
                         rope=True, mass=0.95),
     "e2e256k": dict(seed=1005, hq=32, hkv=8, n=262144, d=128, hidden=128, dtype="bf16",
                     rope=True, sink=4, sink_scale=4.0, mass=0.95),
+    "blocks128k": dict(seed=1006, hq=32, hkv=8, n=131072, d=128, dtype="bf16", rope=False,
+                       block=64, topics=32, topic_amp=8.0, sink_amp=8.0, alpha=0.1, skel=8),
 }
 
 _STREAMS = ("q", "k", "v", "idx", "w", "score")
@@ -238,3 +245,39 @@ def clustered_offsets(rng, hkv: int, n: int, n_runs: int, run_len: int, local: i
         soff[g, :len(x)] = x
         scnt[g] = len(x)
     return vidx, vcnt, soff, scnt
+
+
+def block_structured_inputs(name: str = "blocks128k", n: int | None = None,
+                            seed: int | None = None):
+    """Q [hq,n,d], K, V [hkv,n,d] with a planted block pattern (see the module
+    docstring): per KV head, unit topic directions u_t; key block J adds
+    topic_amp * u_{t(J)} to its keys, query block I adds topic_amp * u_{t(J')}
+    for a uniformly drawn J' < I; block 0's keys and every query add
+    sink_amp * w.  Gaussian N(0,1) elsewhere; bf16 bits."""
+    w = WORKLOADS[name]
+    n = n or w["n"]
+    rs = streams(w["seed"] if seed is None else seed)
+    hq, hkv, d, bs = w["hq"], w["hkv"], w["d"], w["block"]
+    group = hq // hkv
+    nb = (n + bs - 1) // bs
+    q = np.empty((hq, n, d), np.uint16)
+    k = np.empty((hkv, n, d), np.uint16)
+    v = gaussian_heads(rs["v"], hkv, n, d, "bf16", None)
+    for g in range(hkv):
+        dirs = rs["idx"].standard_normal((w["topics"] + 1, d))
+        dirs /= np.linalg.norm(dirs, axis=1, keepdims=True)
+        topic_k = rs["idx"].integers(0, w["topics"], nb)
+        look = np.zeros(nb, np.int64)
+        for I in range(1, nb):
+            look[I] = topic_k[rs["idx"].integers(0, I)]
+        blk = np.arange(n) // bs
+        kk = rs["k"].standard_normal((n, d), dtype=np.float32).astype(np.float64)
+        kk += w["topic_amp"] * dirs[topic_k[blk]]
+        kk[:min(bs, n)] += w["sink_amp"] * dirs[-1]
+        k[g] = to_bf16_bits(kk)
+        for hh in range(group):
+            qq = rs["q"].standard_normal((n, d), dtype=np.float32).astype(np.float64)
+            qq += w["topic_amp"] * dirs[look[blk]]
+            qq += w["sink_amp"] * dirs[-1]
+            q[g * group + hh] = to_bf16_bits(qq)
+    return q, k, v
