@@ -140,6 +140,42 @@ vs_status vs_sparse_attn_prefill(const void* q, const void* k, const void* v, vs
                                  void* out, float* lse, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* Per-query-head index sets (the other reading of "per head": every query
+ * head h has its own columns and offsets, S_i^h = { j <= i : j in V_h or
+ * i - j in O_h }).  Arguments as vs_sparse_attn_prefill except that the
+ * lists have h_q rows: v_idx [h_q][cap_v], v_cnt [h_q], s_off [h_q][cap_s],
+ * s_cnt [h_q]; query head h still reads K/V head h / (h_q / h_kv).  Each
+ * query head then has its own tile list, so K/V tiles are not shared
+ * between the heads of a group.  Workspace: vs_attn_workspace_bytes(h_q, n,
+ * cap_v, cap_s). */
+vs_status vs_sparse_attn_prefill_qh(const void* q, const void* k, const void* v, vs_dtype dt,
+                                    int h_q, int h_kv, int n, int d, float scale,
+                                    const int32_t* v_idx, const int32_t* v_cnt, int cap_v,
+                                    const int32_t* s_off, const int32_t* s_cnt, int cap_s,
+                                    void* out, float* lse, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/* Packed batch of independent causal sequences.  Sequence s holds rows
+ * cu_seqlens[s] .. cu_seqlens[s+1]-1 of q [h_q][total_n][d], k/v
+ * [h_kv][total_n][d], out and lse [h_q][total_n]; it attends only within
+ * itself, with positions (and so columns and offsets) counted from its
+ * first row.  cu_seqlens is a HOST array of nseq + 1 ascending entries from
+ * 0 to total_n (empty sequences allowed).  Lists are per sequence:
+ * v_idx [nseq][S][cap_v], v_cnt [nseq][S], s_off [nseq][S][cap_s], s_cnt
+ * [nseq][S], with S = h_kv, or h_q when sets_per_query_head is nonzero.
+ * The sequences run one after another on `stream` through one workspace of
+ * vs_attn_workspace_bytes(S, longest sequence, cap_v, cap_s) bytes (the
+ * tile counters then describe the last non-empty sequence).  Supported:
+ * as vs_sparse_attn_prefill, with each sequence's K/V of one head under
+ * 2 GiB. */
+vs_status vs_sparse_attn_prefill_varlen(const void* q, const void* k, const void* v, vs_dtype dt,
+                                        int h_q, int h_kv, int total_n, int d, float scale,
+                                        const int32_t* cu_seqlens, int nseq,
+                                        int sets_per_query_head, const int32_t* v_idx,
+                                        const int32_t* v_cnt, int cap_v, const int32_t* s_off,
+                                        const int32_t* s_cnt, int cap_s, void* out, float* lse,
+                                        void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Work counters of the most recent vs_sparse_attn_prefill that used `ws`
  * (read synchronously after `stream` finishes):
  *   tiles[0] = contiguous key tiles computed, summed over KV heads and query

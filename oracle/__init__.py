@@ -138,6 +138,39 @@ def attn(q, k, v, vidx, vcnt, soff, scnt, scale=None, rows=None, nthreads=0):
     return out, lse
 
 
+def attn_qh(q, k, v, vidx, vcnt, soff, scnt, scale=None, rows=None, nthreads=0):
+    """Like attn() with one index set per QUERY head (lists [hq, cap]): the
+    same definition with every query head's K/V head repeated, so that the
+    set of head h is the set of "KV head" h."""
+    q = _c(q)
+    hq = q.shape[0]
+    group = hq // k.shape[0]
+    k = np.repeat(_c(k), group, axis=0)
+    v = np.repeat(_c(v), group, axis=0)
+    return attn(q, k, v, vidx, vcnt, soff, scnt, scale=scale, rows=rows, nthreads=nthreads)
+
+
+def attn_varlen(q, k, v, cu_seqlens, vidx, vcnt, soff, scnt, per_query_head=False, scale=None,
+                nthreads=0):
+    """Packed batch: sequence s is rows cu[s]..cu[s+1]-1 of every head and
+    attends only within itself, with its own lists vidx[s] ... (positions
+    relative to its first row).  Returns (out [hq, total, d], lse [hq, total])."""
+    q, k, v = _c(q), _c(k), _c(v)
+    hq, total, d = q.shape
+    out = np.zeros((hq, total, d), dtype=np.float64)
+    lse = np.zeros((hq, total), dtype=np.float64)
+    fn = attn_qh if per_query_head else attn
+    for s in range(len(cu_seqlens) - 1):
+        a, b = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        if b == a:
+            continue
+        o, l = fn(q[:, a:b], k[:, a:b], v[:, a:b], vidx[s], vcnt[s], soff[s], scnt[s],
+                  scale=scale, nthreads=nthreads)
+        out[:, a:b] = o
+        lse[:, a:b] = l
+    return out, lse
+
+
 def index(k, v, w1, w2, nthreads=0):
     """VSIndexer logits (vlog, slog) [hkv, n] fp64 from k/v [hkv,n,d]."""
     k, v, w1, w2 = _c(k), _c(v), _c(w1), _c(w2)

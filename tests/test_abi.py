@@ -146,6 +146,26 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert battn(scale=ctypes.c_float(float("inf"))) == vsa.VS_ERR_INVALID
     assert battn(ws_bytes=8) == vsa.VS_ERR_WORKSPACE
     assert L.vs_block_attn_workspace_bytes() >= 32
+    # per-query-head sets and packed batches
+    assert L.vs_sparse_attn_prefill_qh(p, p, p, 0, 8, 2, 100, 128, ctypes.c_float(0.1), None, p, 4,
+                                       p, p, 4, p, None, p, 1 << 30, None) == vsa.VS_ERR_INVALID
+    assert L.vs_sparse_attn_prefill_qh(p, p, p, 0, 8, 2, 100, 128, ctypes.c_float(0.1), p, p, 4,
+                                       p, p, 4, p, None, p, 16, None) == vsa.VS_ERR_WORKSPACE
+    cu = (ctypes.c_int32 * 3)(0, 50, 120)
+    bad = (ctypes.c_int32 * 3)(0, 60, 50)
+    cup = ctypes.cast(cu, ctypes.c_void_p)
+
+    def varlen(cu_p=cup, total=120, nseq=2, ws_bytes=1 << 30, h_q=8):
+        return L.vs_sparse_attn_prefill_varlen(p, p, p, 0, h_q, 2, total, 128, ctypes.c_float(0.1),
+                                               cu_p, nseq, 0, p, p, 4, p, p, 4, p, None, p,
+                                               ws_bytes, None)
+
+    assert varlen(cu_p=None) == vsa.VS_ERR_INVALID
+    assert varlen(total=121) == vsa.VS_ERR_INVALID          # cu[nseq] must equal total
+    assert varlen(cu_p=ctypes.cast(bad, ctypes.c_void_p), total=50) == vsa.VS_ERR_INVALID
+    assert varlen(nseq=0) == vsa.VS_ERR_INVALID
+    assert varlen(h_q=24) == vsa.VS_ERR_UNSUPPORTED
+    assert varlen(ws_bytes=16) == vsa.VS_ERR_WORKSPACE
     t = (ctypes.c_int64 * 4)()
     assert L.vs_attn_tile_counts(None, 8, 1024, 16, 16, 32, ctypes.cast(t, ctypes.c_void_p), None) == vsa.VS_ERR_INVALID
     assert L.vs_attn_tile_counts(p, 8, 1024, 16, 16, 24, ctypes.cast(t, ctypes.c_void_p), None) == vsa.VS_ERR_UNSUPPORTED

@@ -530,3 +530,66 @@ def test_aggregate_diagonal_attention():
     a_v, a_s = oracle.aggregate(x * 30.0, x * 30.0, scale=1.0)
     assert a_s[0, 0] > n - 1e-3
     np.testing.assert_allclose(a_v[0], 1.0, atol=2e-3)
+
+
+# ------------------------------------------- per-query-head sets, packed batches
+
+def test_qh_sets_equal_shared_sets_when_identical_within_group():
+    """Per-query-head sets that repeat the group's set give the shared result."""
+    rng = np.random.default_rng(31)
+    hkv, group, n, d = 2, 3, 120, 16
+    q = rng.standard_normal((hkv * group, n, d))
+    k = rng.standard_normal((hkv, n, d))
+    v = rng.standard_normal((hkv, n, d))
+    lv = [[0, 5, 77], [3, 9]]
+    lo = [[0, 1, 30], [0, 2, 4, 100]]
+    shared = _lists(hkv, lv, lo)
+    per_q = _lists(hkv * group, [lv[h // group] for h in range(hkv * group)],
+                   [lo[h // group] for h in range(hkv * group)])
+    o1, l1 = oracle.attn(q, k, v, *shared)
+    o2, l2 = oracle.attn_qh(q, k, v, *per_q)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_qh_all_offsets_is_dense_causal_sdpa():
+    """Head 0 gets every offset, head 1 only the diagonal: SDPA per head."""
+    rng = np.random.default_rng(32)
+    n, d = 64, 8
+    q = rng.standard_normal((2, n, d))
+    k = rng.standard_normal((1, n, d))
+    v = rng.standard_normal((1, n, d))
+    sets = _lists(2, [[], []], [list(range(n)), [0]])
+    out, _ = oracle.attn_qh(q, k, v, *sets)
+    np.testing.assert_allclose(out[0], _sdpa(q[:1], k, v, 1, causal=True)[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out[1], np.repeat(v, 1, 0)[0], rtol=0, atol=1e-12)
+
+
+def test_varlen_sequences_are_independent_and_match_single_calls():
+    rng = np.random.default_rng(33)
+    hkv, group, d = 2, 2, 16
+    cu = [0, 70, 70, 200, 201]
+    total = cu[-1]
+    q = rng.standard_normal((hkv * group, total, d))
+    k = rng.standard_normal((hkv, total, d))
+    v = rng.standard_normal((hkv, total, d))
+    per_seq = [_lists(hkv, [[0, 3], [1]], [[0, 1, 2], [0, 5]]) for _ in range(4)]
+    stack = [np.stack([ps[i] for ps in per_seq]) for i in range(4)]
+    out, lse = oracle.attn_varlen(q, k, v, cu, *stack)
+    for s in range(4):
+        a, b = cu[s], cu[s + 1]
+        if a == b:
+            continue
+        o, l = oracle.attn(q[:, a:b], k[:, a:b], v[:, a:b], *per_seq[s])
+        np.testing.assert_array_equal(out[:, a:b], o)
+        np.testing.assert_array_equal(lse[:, a:b], l)
+    # changing the last sequence's keys leaves the others untouched
+    k2 = k.copy()
+    k2[:, 200:] += 1.0
+    out2, _ = oracle.attn_varlen(q, k2, v, cu, *stack)
+    np.testing.assert_array_equal(out2[:, :200], out[:, :200])
+    # a single sequence with every offset is dense causal attention (SDPA)
+    one = [np.stack([x]) for x in _lists(hkv, [[], []], [list(range(70))] * 2)]
+    out3, _ = oracle.attn_varlen(q[:, :70], k[:, :70], v[:, :70], [0, 70], *one)
+    np.testing.assert_allclose(out3, _sdpa(q[:, :70], k[:, :70], v[:, :70], group, causal=True),
+                               rtol=0, atol=1e-12)

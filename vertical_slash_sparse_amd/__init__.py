@@ -14,6 +14,9 @@ calls raise.
     vs_block_attn_prefill(q, k, v, mask)           -> (out, lse)
     vs_sparse_attn_prefill(q, k, v, v_idx, v_cnt, s_off, s_cnt, scale=None)
                                                    -> (out, lse)
+    vs_sparse_attn_prefill_qh(...)                 per-query-head lists [h_q, cap]
+    vs_sparse_attn_prefill_varlen(q, k, v, cu_seqlens, v_idx, v_cnt, s_off, s_cnt)
+                                                   packed batch of sequences
 """
 from __future__ import annotations
 
@@ -32,7 +35,8 @@ VS_VERTICAL, VS_SLASH = 0, 1
 
 _SYMBOLS = ("vs_index", "vs_select_workspace_bytes", "vs_select", "vs_select_threshold",
             "vs_attn_workspace_bytes", "vs_aggregate_workspace_bytes", "vs_attn_aggregate",
-            "vs_sparse_attn_prefill", "vs_attn_tile_counts", "vs_block_workspace_bytes",
+            "vs_sparse_attn_prefill", "vs_sparse_attn_prefill_qh", "vs_sparse_attn_prefill_varlen",
+            "vs_attn_tile_counts", "vs_block_workspace_bytes",
             "vs_block_discover", "vs_block_attn_workspace_bytes", "vs_block_attn_prefill",
             "vs_status_str")
 
@@ -71,6 +75,12 @@ def lib() -> ctypes.CDLL:
         L.vs_sparse_attn_prefill.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P, i32, P, P,
                                              i32, P, P, P, sz, P]
         L.vs_sparse_attn_prefill.restype = i32
+        L.vs_sparse_attn_prefill_qh.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P, i32, P,
+                                                P, i32, P, P, P, sz, P]
+        L.vs_sparse_attn_prefill_qh.restype = i32
+        L.vs_sparse_attn_prefill_varlen.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, i32, i32,
+                                                    P, P, i32, P, P, i32, P, P, P, sz, P]
+        L.vs_sparse_attn_prefill_varlen.restype = i32
         L.vs_attn_tile_counts.argtypes = [P, i32, i32, i32, i32, i32, P, P]
         L.vs_attn_tile_counts.restype = i32
         L.vs_block_workspace_bytes.argtypes = [i32, i32, i32]
@@ -258,6 +268,98 @@ def vs_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                       cap_s, _ptr(out), _ptr(lse), _ptr(workspace),
                                       workspace.numel(), _stream(q, stream))
     _check("vs_sparse_attn_prefill", st)
+    return out, lse
+
+
+def _attn_common(q, k, v, out, lse, want_lse, rows):
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bf16 or fp32")
+    dt = VS_BF16 if q.dtype == torch.bfloat16 else VS_F32
+    _need(q, "q", q.dtype, 3)
+    dev = q.device
+    _need(k, "k", q.dtype, 3, dev)
+    _need(v, "v", q.dtype, 3, dev)
+    h_q, n, d = q.shape
+    h_kv = k.shape[0]
+    if k.shape != (h_kv, n, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [h_kv, rows, d] like q")
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", q.dtype, 3, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    if want_lse and lse is None:
+        lse = torch.empty((h_q, n), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+        if lse.shape != (h_q, n):
+            raise ValueError("lse must be [h_q, rows]")
+    return dt, dev, h_q, h_kv, n, d, out, lse
+
+
+def vs_sparse_attn_prefill_qh(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              v_idx: torch.Tensor, v_cnt: torch.Tensor, s_off: torch.Tensor,
+                              s_cnt: torch.Tensor, scale: float | None = None,
+                              out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                              want_lse: bool = True, workspace: torch.Tensor | None = None,
+                              stream=None):
+    """Vertical-slash prefill with one index set per query head: lists int32
+    [h_q, cap] and counts [h_q]; query head h reads K/V head h // (h_q/h_kv)."""
+    dt, dev, h_q, h_kv, n, d, out, lse = _attn_common(q, k, v, out, lse, want_lse, None)
+    for t, nm in ((v_idx, "v_idx"), (s_off, "s_off")):
+        _need(t, nm, torch.int32, 2, dev)
+    for t, nm in ((v_cnt, "v_cnt"), (s_cnt, "s_cnt")):
+        _need(t, nm, torch.int32, 1, dev)
+    if v_idx.shape[0] != h_q or s_off.shape[0] != h_q or v_cnt.shape != (h_q,) or s_cnt.shape != (h_q,):
+        raise ValueError("vs_sparse_attn_prefill_qh: index lists must have h_q rows")
+    cap_v, cap_s = v_idx.shape[1], s_off.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = vs_attn_workspace_bytes(h_q, n, cap_v, cap_s)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = lib().vs_sparse_attn_prefill_qh(_ptr(q), _ptr(k), _ptr(v), dt, h_q, h_kv, n, d, scale,
+                                         _ptr(v_idx), _ptr(v_cnt), cap_v, _ptr(s_off), _ptr(s_cnt),
+                                         cap_s, _ptr(out), _ptr(lse), _ptr(workspace),
+                                         workspace.numel(), _stream(q, stream))
+    _check("vs_sparse_attn_prefill_qh", st)
+    return out, lse
+
+
+def vs_sparse_attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens,
+                                  v_idx: torch.Tensor, v_cnt: torch.Tensor, s_off: torch.Tensor,
+                                  s_cnt: torch.Tensor, per_query_head: bool = False,
+                                  scale: float | None = None, out: torch.Tensor | None = None,
+                                  lse: torch.Tensor | None = None, want_lse: bool = True,
+                                  workspace: torch.Tensor | None = None, stream=None):
+    """Packed batch of causal sequences: q [h_q, total, d], k/v [h_kv, total, d];
+    cu_seqlens (host sequence of nseq+1 ints from 0 to total); lists int32
+    [nseq, S, cap] and counts [nseq, S] with S = h_kv (or h_q when
+    per_query_head), positions relative to each sequence's first row."""
+    dt, dev, h_q, h_kv, n, d, out, lse = _attn_common(q, k, v, out, lse, want_lse, None)
+    cu = (ctypes.c_int32 * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
+    nseq = len(cu_seqlens) - 1
+    sets = h_q if per_query_head else h_kv
+    for t, nm in ((v_idx, "v_idx"), (s_off, "s_off")):
+        _need(t, nm, torch.int32, 3, dev)
+    for t, nm in ((v_cnt, "v_cnt"), (s_cnt, "s_cnt")):
+        _need(t, nm, torch.int32, 2, dev)
+    if v_idx.shape[:2] != (nseq, sets) or s_off.shape[:2] != (nseq, sets) or \
+            v_cnt.shape != (nseq, sets) or s_cnt.shape != (nseq, sets):
+        raise ValueError("vs_sparse_attn_prefill_varlen: lists must be [nseq, sets, cap]")
+    cap_v, cap_s = v_idx.shape[2], s_off.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    max_len = max([int(cu_seqlens[i + 1]) - int(cu_seqlens[i]) for i in range(nseq)] + [1])
+    need = vs_attn_workspace_bytes(sets, max_len, cap_v, cap_s)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = lib().vs_sparse_attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), dt, h_q, h_kv, n, d, scale,
+                                             ctypes.cast(cu, ctypes.c_void_p), nseq,
+                                             1 if per_query_head else 0, _ptr(v_idx), _ptr(v_cnt),
+                                             cap_v, _ptr(s_off), _ptr(s_cnt), cap_s, _ptr(out),
+                                             _ptr(lse), _ptr(workspace), workspace.numel(),
+                                             _stream(q, stream))
+    _check("vs_sparse_attn_prefill_varlen", st)
     return out, lse
 
 

@@ -103,6 +103,79 @@ vs_status vs_sparse_attn_prefill(const void* q, const void* k, const void* v, vs
                               s_off, s_cnt, cap_s, out, lse, ws, stream));
 }
 
+namespace {
+
+// checks shared by the per-query-head and packed-batch forms
+vs_status check_attn_common(const void* q, const void* k, const void* v, vs_dtype dt, int h_q,
+                            int h_kv, int d, float scale, int cap_v, int cap_s, const void* out,
+                            const void* ws) {
+  if (!q || !k || !v || !out || !ws) return VS_ERR_INVALID;
+  if (dt != VS_BF16 && dt != VS_F32) return VS_ERR_INVALID;
+  if (h_q <= 0 || h_kv <= 0 || d <= 0 || h_q % h_kv) return VS_ERR_INVALID;
+  if (cap_v < 1 || cap_s < 1) return VS_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return VS_ERR_INVALID;
+  if (!group_ok(h_q, h_kv)) return VS_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return VS_ERR_UNSUPPORTED;
+  return VS_OK;
+}
+
+}  // namespace
+
+vs_status vs_sparse_attn_prefill_qh(const void* q, const void* k, const void* v, vs_dtype dt,
+                                    int h_q, int h_kv, int n, int d, float scale,
+                                    const int32_t* v_idx, const int32_t* v_cnt, int cap_v,
+                                    const int32_t* s_off, const int32_t* s_cnt, int cap_s,
+                                    void* out, float* lse, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (!v_idx || !v_cnt || !s_off || !s_cnt) return VS_ERR_INVALID;
+  const vs_status st = check_attn_common(q, k, v, dt, h_q, h_kv, d, scale, cap_v, cap_s, out, ws);
+  if (st != VS_OK) return st;
+  if (n <= 0 || (long long)n > (1LL << 30) || (long long)h_q * n * d > (1LL << 40)) return VS_ERR_INVALID;
+  if ((long long)n * d * (dt == VS_F32 ? 4 : 2) >= (1LL << 31)) return VS_ERR_UNSUPPORTED;
+  if (ws_bytes < vs_attn_workspace_bytes(h_q, n, cap_v, cap_s)) return VS_ERR_WORKSPACE;
+  AttnLayout lay;
+  lay.kvdiv = h_q / h_kv;
+  return from_hip(launch_attn(q, k, v, dt == VS_F32, h_q, h_q, n, d, scale, v_idx, v_cnt, cap_v,
+                              s_off, s_cnt, cap_s, out, lse, ws, stream, lay));
+}
+
+vs_status vs_sparse_attn_prefill_varlen(const void* q, const void* k, const void* v, vs_dtype dt,
+                                        int h_q, int h_kv, int total_n, int d, float scale,
+                                        const int32_t* cu_seqlens, int nseq,
+                                        int sets_per_query_head, const int32_t* v_idx,
+                                        const int32_t* v_cnt, int cap_v, const int32_t* s_off,
+                                        const int32_t* s_cnt, int cap_s, void* out, float* lse,
+                                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!cu_seqlens || !v_idx || !v_cnt || !s_off || !s_cnt) return VS_ERR_INVALID;
+  const vs_status st = check_attn_common(q, k, v, dt, h_q, h_kv, d, scale, cap_v, cap_s, out, ws);
+  if (st != VS_OK) return st;
+  if (nseq <= 0 || total_n <= 0 || (long long)h_q * total_n * d > (1LL << 40)) return VS_ERR_INVALID;
+  if (cu_seqlens[0] != 0 || cu_seqlens[nseq] != total_n) return VS_ERR_INVALID;
+  int max_len = 0;
+  for (int s = 0; s < nseq; ++s) {
+    const int len = cu_seqlens[s + 1] - cu_seqlens[s];
+    if (len < 0) return VS_ERR_INVALID;
+    if (len > max_len) max_len = len;
+  }
+  if ((long long)max_len * d * (dt == VS_F32 ? 4 : 2) >= (1LL << 31)) return VS_ERR_UNSUPPORTED;
+  const int sets = sets_per_query_head ? h_q : h_kv;
+  if (ws_bytes < vs_attn_workspace_bytes(sets, max_len, cap_v, cap_s)) return VS_ERR_WORKSPACE;
+  AttnLayout lay;
+  lay.kvdiv = sets_per_query_head ? h_q / h_kv : 1;
+  lay.hstride = total_n;
+  for (int s = 0; s < nseq; ++s) {
+    const int len = cu_seqlens[s + 1] - cu_seqlens[s];
+    if (len == 0) continue;
+    lay.row0 = cu_seqlens[s];
+    const size_t so = (size_t)s * sets;
+    const hipError_t e = launch_attn(q, k, v, dt == VS_F32, h_q, sets, len, d, scale,
+                                     v_idx + so * cap_v, v_cnt + so, cap_v, s_off + so * cap_s,
+                                     s_cnt + so, cap_s, out, lse, ws, stream, lay);
+    if (e != hipSuccess) return VS_ERR_HIP;
+  }
+  return VS_OK;
+}
+
 size_t vs_aggregate_workspace_bytes(int h_kv, int n) {
   if (h_kv <= 0 || n <= 0) return 0;
   return aggregate_workspace_bytes(h_kv, n);

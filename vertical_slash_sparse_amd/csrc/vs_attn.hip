@@ -207,6 +207,15 @@ struct AttnParams {
   unsigned long long* stats;
   const uint32_t* blk;  // block mode: key-block bitmap per (KV head, query block of 64)
   int blk_wpr;          // its words per row
+  // Addressing.  Index sets belong to "set heads" g (a KV head, or a query
+  // head when every query head has its own sets); set head g reads K/V head
+  // g / kvdiv.  Row r of a head's sequence lives at row hstride * head +
+  // row0 + r of the [heads][rows][d] tensors (hstride = n, row0 = 0 for one
+  // sequence; a packed batch of sequences passes its total length and the
+  // sequence's first row).
+  int kvdiv;
+  long long hstride;
+  long long row0;
 };
 
 template <bool F32>
@@ -291,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   const int i0w = i0 + 32 * (wave / p.hpw);
   const int qrow = i0w + ql;
   const bool wave_rows = i0w < n;
-  const size_t kv_head = (size_t)g * n;
+  const size_t kv_head = (size_t)(g / p.kvdiv) * p.hstride + p.row0;  // first K/V row of the sequence
 
   const uint32_t* bo = p.bitO + (size_t)g * p.stride + kPrePad;
   const uint32_t* bv = p.bitV + (size_t)g * p.stride + kPrePad;
@@ -313,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   // Q^T fragments (B operand): lane holds row qrow, head dims 16s + 8*half .. +7
   bf16x8 qf[KS];
   {
-    const size_t ro = ((size_t)head * n + min(qrow, n - 1)) * D;
+    const size_t ro = ((size_t)head * p.hstride + p.row0 + min(qrow, n - 1)) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 raw = load8<F32>(p.q, ro + 16 * s + 8 * half);
@@ -948,7 +957,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   const float lt = half_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (wave_rows && qrow < n) {
-    const size_t ro = ((size_t)head * n + qrow) * D;
+    const size_t ro = ((size_t)head * p.hstride + p.row0 + qrow) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -964,7 +973,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         }
       }
     if (half == 0 && p.lse)
-      p.lse[(size_t)head * n + qrow] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -__builtin_inff();
+      p.lse[(size_t)head * p.hstride + p.row0 + qrow] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -__builtin_inff();
   }
   if (tid == 0 && p.stats) {
     atomicAdd(&p.stats[0], (unsigned long long)n_dense);
@@ -984,7 +993,7 @@ int attn_query_rows_per_block(int group) {
 hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, int h_q, int h_kv,
                        int n, int d, float scale, const int32_t* v_idx, const int32_t* v_cnt,
                        int cap_v, const int32_t* s_off, const int32_t* s_cnt, int cap_s, void* out,
-                       float* lse, void* ws, hipStream_t stream) {
+                       float* lse, void* ws, hipStream_t stream, const AttnLayout& lay) {
   const AttnWsLayout L(h_kv, n, cap_v, cap_s);
   char* base = static_cast<char*>(ws);
   uint32_t* bitO = reinterpret_cast<uint32_t*>(base + L.off_bitO);
@@ -1045,6 +1054,9 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
   prm.stats = stats;
   prm.blk = nullptr;
   prm.blk_wpr = 0;
+  prm.kvdiv = lay.kvdiv;
+  prm.hstride = lay.hstride ? lay.hstride : n;
+  prm.row0 = lay.row0;
   const dim3 grid((unsigned)((long long)prm.nblocks * h_kv * nsplit));
   if (d == 128) {
     if (f32) hipLaunchKernelGGL((attn_kernel<128, true, false>), grid, dim3(kThreads), 0, stream, prm);
@@ -1082,6 +1094,9 @@ hipError_t launch_attn_blocks(const void* q, const void* k, const void* v, bool 
   prm.stats = stats;
   prm.blk = blk;
   prm.blk_wpr = wpr;
+  prm.kvdiv = 1;
+  prm.hstride = n;
+  prm.row0 = 0;
   const dim3 grid((unsigned)((long long)prm.nblocks * h_kv * nsplit));
   if (d == 128) {
     if (f32) hipLaunchKernelGGL((attn_kernel<128, true, true>), grid, dim3(kThreads), 0, stream, prm);

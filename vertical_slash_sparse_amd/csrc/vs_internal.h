@@ -60,10 +60,19 @@ struct SelectWsLayout {
   }
 };
 
+// Where a call's rows live (see AttnParams): set head g reads K/V head
+// g / kvdiv; row r of head h is row h * hstride + row0 + r (hstride 0 = n).
+struct AttnLayout {
+  int kvdiv = 1;
+  long long hstride = 0;
+  long long row0 = 0;
+};
+
 hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, int h_q, int h_kv,
                        int n, int d, float scale, const int32_t* v_idx, const int32_t* v_cnt,
                        int cap_v, const int32_t* s_off, const int32_t* s_cnt, int cap_s, void* out,
-                       float* lse, void* ws, hipStream_t stream);
+                       float* lse, void* ws, hipStream_t stream,
+                       const AttnLayout& lay = AttnLayout());
 
 int attn_query_rows_per_block(int group);
 
