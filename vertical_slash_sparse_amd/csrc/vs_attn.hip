@@ -622,7 +622,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     int t = 0;
     auto step = [&](auto s_const) -> bool {
       constexpr int S = decltype(s_const)::value;
-      // V(t)
+      // V(t), at raised issue priority: the vector half is the longer chain,
+      // so the SIMD's other wave (in its matrix half) takes the slots it leaves
+      __builtin_amdgcn_s_setprio(3);
       src.begin();
       softmax(kc0, kc1);
       src.key_word(kc0, kc1);
@@ -635,6 +637,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(pk[e]));
       __syncthreads();
       // M(t)
+      __builtin_amdgcn_s_setprio(0);
       mhalf(S, (S + 1) % NST);
       // and S(t+1) is complete before the next vector half starts
       asm volatile("" : "+v"(c0), "+v"(c1));
