@@ -220,7 +220,7 @@ vs_status vs_block_discover(const void* q, const void* k, int h_q, int h_kv, int
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
     return VS_ERR_HIP;
-  if (block_score_lds_bytes(n) + 1024 > (size_t)lds) return VS_ERR_UNSUPPORTED;
+  if (block_score_lds_bytes(n, d) + 1024 > (size_t)lds) return VS_ERR_UNSUPPORTED;
   return from_hip(launch_block_discover(q, k, h_q, h_kv, n, d, scale, skel, alpha, mask,
                                         words_per_row, score, ws, stream));
 }

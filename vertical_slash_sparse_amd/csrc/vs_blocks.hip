@@ -20,9 +20,10 @@
 //    significant bits, so the matrix cores can take it.
 //  * blk_score_kernel: one wave per query block, four per workgroup.  The
 //    wave's 32 probe rows (G heads x skel rows, zero-padded) are one MFMA
-//    operand held in registers; the block means stream through in chunks of
-//    32 blocks straight from L2 (every probe row needs every earlier block
-//    once, so there is nothing to reuse from LDS).  Pass 1 runs
+//    operand held in registers; the block means pass through LDS in chunks
+//    of 32 blocks (hi and lo, 16 KiB at d = 128), brought in once per
+//    workgroup by LDS-DMA two stages deep and read by all four waves, whose
+//    query blocks need nearly the same chunks.  Pass 1 runs
 //    S^T = Kbar Q^T, so each lane owns one probe and keeps its running max
 //    and sum over blocks; pass 2 runs S = Q Kbar^T, so each lane owns one
 //    block and adds the probes' normalised probabilities over its elements.
@@ -85,27 +86,44 @@ __global__ __launch_bounds__(256) void blk_mean_kernel(const uint16_t* __restric
   }
 }
 
+// XOR swizzle of the 16-byte chunks of an LDS row of block means, so that
+// the 32 lanes reading one chunk of 32 consecutive rows hit distinct banks
+template <int D>
+__device__ __forceinline__ int blk_swz(int r) {
+  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+
 template <int D>
 __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
   constexpr int KS = D / 16;
-  extern __shared__ float sc_all[];                 // [kBlkWaves][nb] block scores
+  constexpr int CH = D / 8;                      // 16-byte chunks per row
+  constexpr int ROWB = D * 2;                    // bytes of one mean-key row
+  constexpr int PARTB = 32 * ROWB;               // 32 rows of one part (hi or lo)
+  constexpr int STB = 2 * PARTB;                 // one LDS stage: hi rows, then lo rows
+  constexpr int RPD = 1024 / ROWB;               // rows per 1 KiB DMA
+  constexpr int NDMA = STB / 1024 / kBlkWaves;   // DMAs per wave per chunk
+  static_assert(NDMA >= 1 && NDMA * kBlkWaves * 1024 == STB, "chunk split");
+  extern __shared__ __align__(16) uint8_t dyn[];  // 2 chunk stages, then [kBlkWaves][nb] scores
   __shared__ float st_m[kBlkWaves][32], st_w[kBlkWaves][32];  // per probe: max, weight / sum
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  lds_u8* const stg = (lds_u8*)dyn;
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, ql = lane & 31;
   const int wave = wave_uniform(tid >> 6);
   const int g = blockIdx.x % p.hkv;
   const int nbw = (p.nb + kBlkWaves - 1) / kBlkWaves;
-  const int I = (nbw - 1 - (int)(blockIdx.x / p.hkv)) * kBlkWaves + wave;  // longest rows first
+  const int I0 = (nbw - 1 - (int)(blockIdx.x / p.hkv)) * kBlkWaves;  // longest rows first
+  const int I = I0 + wave;                      // this wave's query block
   const bool active = I < p.nb;
-  float* sc = sc_all + wave * p.nb;
   const int n = p.n, nb = p.nb;
+  float* sc = reinterpret_cast<float*>(dyn + 2 * STB) + wave * nb;
 
   // probe slot ql: head ql / skel of the group, row 64 I + (ql % skel) * (64 / skel)
   const int step = kBN / p.skel;
   const int slot_head = ql / p.skel, slot_m = ql % p.skel;
   const int prow = I * kBN + slot_m * step;
   const bool probe = active && slot_head < p.group && prow < n;
-  // number of probes of this query block: G x (rows below n)
   const int rows_in = active ? min(p.skel, (n - I * kBN + step - 1) / step) : 1;
   const float weight = 1.f / (float)(p.group * rows_in);
   bf16x8 qf[KS];
@@ -119,24 +137,72 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
       qf[s] = as_bf16x8(raw);
     }
   }
-  // mean-key fragment of block J (this lane's row): dims 16 s + 8 half ..
-  auto kfrag = [&](const uint16_t* base, int J, int s) -> bf16x8 {
-    return as_bf16x8(*reinterpret_cast<const u32x4*>(base + ((size_t)g * nb + J) * D + 16 * s + 8 * half));
+
+  // chunk c = mean keys of blocks 32 c .. 32 c + 31 of head g, hi and lo,
+  // brought into stage st by the four waves (rows past nb arrive as zeros)
+  const uint32_t tab_bytes = (uint32_t)((size_t)p.hkv * nb * ROWB);
+  const u32x4 whi = buffer_words(p.khi, tab_bytes);
+  const u32x4 wlo = buffer_words(p.klo, tab_bytes);
+  int dma_part[NDMA], dma_dst[NDMA], dma_row[NDMA], dma_col[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int kib = wave * NDMA + i;               // KiB of the stage this DMA fills
+    const int part = kib / (PARTB / 1024), kin = kib % (PARTB / 1024);
+    const int r = kin * RPD + lane / CH;
+    dma_part[i] = part;
+    dma_dst[i] = part * PARTB + kin * 1024;
+    dma_row[i] = r;
+    dma_col[i] = 16 * ((lane % CH) ^ blk_swz<D>(r));  // LDS slot lane % CH holds this source chunk
+  }
+  unsigned dma_off[NDMA];
+  auto stage = [&](int c, int st) {
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int J = 32 * c + dma_row[i];
+      const unsigned off = J < nb ? (unsigned)(((size_t)g * nb + J) * ROWB) + dma_col[i] : tab_bytes;
+      dma16(dma_part[i] ? wlo : whi, (uint32_t)(uintptr_t)(stg + st * STB + dma_dst[i]), off);
+      dma_off[i] = off;
+    }
   };
-  const int nchunk = active ? (I + 31) / 32 : 0;  // candidates are blocks 0 .. I-1
+  // operand fragment of row ql (block 32 c + ql) in stage st: dims 16 s + 8 half ..
+  auto kfrag = [&](int st, int part, int s) -> bf16x8 {
+    return *(const __attribute__((address_space(3))) bf16x8*)(
+        stg + st * STB + part * PARTB + ql * ROWB + 16 * ((2 * s + half) ^ blk_swz<D>(ql)));
+  };
+  const int Imax = min(I0 + kBlkWaves - 1, nb - 1);
+  const int nch = (Imax + 31) / 32;          // chunks any wave of the workgroup needs
+  const int mych = active ? (I + 31) / 32 : 0;  // candidates of this wave: blocks 0 .. I-1
+
+  // run `body(c, st)` over the chunks, two stages deep
+  auto sweep = [&](auto&& body) {
+    if (nch == 0) return;
+    stage(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      const int st = c & 1;
+      if (c + 1 < nch) {
+        stage(c + 1, st ^ 1);
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) asm volatile("" ::"v"(dma_off[i]));
+      }
+      if (c < mych) body(c, st);
+      __builtin_amdgcn_s_waitcnt(0x0070);  // the next chunk has landed; this one is read
+      __syncthreads();
+    }
+  };
 
   // ---- pass 1: S^T = Kbar Q^T; lane (ql, half) holds probe ql against
   // blocks 32 c + 8 (e / 4) + 4 half + e % 4
   float m2 = kNegBig, l = 0.f;
-  for (int c = 0; c < nchunk; ++c) {
-    const int Jr = min(c * 32 + ql, nb - 1);
+  sweep([&](int c, int st) {
     f32x16 acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) acc = mfma32(kfrag(p.khi, Jr, s), qf[s], acc);
+    for (int s = 0; s < KS; ++s) acc = mfma32(kfrag(st, 0, s), qf[s], acc);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) acc = mfma32(kfrag(p.klo, Jr, s), qf[s], acc);
+    for (int s = 0; s < KS; ++s) acc = mfma32(kfrag(st, 1, s), qf[s], acc);
     float z[16];
     float mloc = kNegBig;
 #pragma unroll
@@ -151,7 +217,7 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
     for (int e = 0; e < 16; ++e) add += z[e] > kNegBig ? __builtin_amdgcn_exp2f(z[e] - mn) : 0.f;
     l = l * __builtin_amdgcn_exp2f(m2 - mn) + add;
     m2 = mn;
-  }
+  });
   {
     // the two halves of the wave saw different blocks of the same probe
     const auto sm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m2), __float_as_uint(m2), false, false);
@@ -176,23 +242,21 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
     nm[e] = -st_m[wave][pr];
     wl[e] = st_w[wave][pr];
   }
-  for (int c = 0; c < nchunk; ++c) {
+  sweep([&](int c, int st) {
     const int J = c * 32 + ql;
-    const int Jr = min(J, nb - 1);
     f32x16 acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) acc = mfma32(qf[s], kfrag(p.khi, Jr, s), acc);
+    for (int s = 0; s < KS; ++s) acc = mfma32(qf[s], kfrag(st, 0, s), acc);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) acc = mfma32(qf[s], kfrag(p.klo, Jr, s), acc);
+    for (int s = 0; s < KS; ++s) acc = mfma32(qf[s], kfrag(st, 1, s), acc);
     float t = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) t += __builtin_amdgcn_exp2f(fmaf(acc[e], p.c, nm[e])) * wl[e];
     t = half_sum(t);
     if (half == 0 && J < nb) sc[J] = J < I ? t : 0.f;
-  }
-  __syncthreads();
+  });
   if (!active) return;
 
   // ---- threshold: alpha times the row's largest score, one fp32 product
@@ -222,8 +286,9 @@ size_t block_workspace_bytes(int h_kv, int n, int d) {
   return 2 * align_up(sizeof(uint16_t) * (size_t)h_kv * nb * d, 256);
 }
 
-size_t block_score_lds_bytes(int n) {
-  return sizeof(float) * (size_t)kBlkWaves * (size_t)((n + kBN - 1) / kBN);
+size_t block_score_lds_bytes(int n, int d) {
+  return 2 * 2 * 32 * (size_t)d * 2 +  // two stages of 32 mean-key rows, hi and lo
+         sizeof(float) * (size_t)kBlkWaves * (size_t)((n + kBN - 1) / kBN);
 }
 
 hipError_t launch_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,
@@ -253,7 +318,11 @@ hipError_t launch_block_discover(const void* q, const void* k, int h_q, int h_kv
   prm.c = scale * 1.4426950408889634f;
   prm.alpha = alpha;
   const dim3 sg((unsigned)(((nb + kBlkWaves - 1) / kBlkWaves) * h_kv));
-  const size_t lds = block_score_lds_bytes(n);
+  const size_t lds = block_score_lds_bytes(n, d);
+  const void* fn = d == 128 ? reinterpret_cast<const void*>(&blk_score_kernel<128>)
+                            : reinterpret_cast<const void*>(&blk_score_kernel<64>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   if (d == 128)
     hipLaunchKernelGGL(blk_score_kernel<128>, sg, dim3(kBlkThreads), lds, stream, prm);
   else
