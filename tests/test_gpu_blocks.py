@@ -177,3 +177,34 @@ def test_full_size_128k_sampled():
     og = to_f64(out)[srows[:, 0], srows[:, 1]]
     lg = lse.cpu().numpy().astype(np.float64)[srows[:, 0], srows[:, 1]]
     assert_attn_close(og, lg, ro, rl, "128k attention rows")
+
+
+def test_full_size_256k_discover_sampled():
+    """32/8 heads, n = 262144 (4096 blocks: the score kernel keeps 64 KiB of
+    scores plus two 16 KiB chunk stages in LDS): the whole mask against the
+    oracle's selection on the GPU's scores, sampled score rows against the
+    oracle, and sampled attention rows under the mask."""
+    _log("case: blocks 256k sampled")
+    q, k, v = workloads.block_structured_inputs("blocks128k", n=262144)
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    nb = n // BS
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    skel, alpha = 8, 0.1
+    mask, score = vsa.vs_block_discover(qd, kd, skel, alpha, want_score=True)
+    out, lse = vsa.vs_block_attn_prefill(qd, kd, vd, mask)
+    torch.cuda.synchronize()
+    got = score.cpu().numpy()
+    del score
+    m = _mask_np(mask)
+    assert np.array_equal(m, oracle.block_select(got, alpha)), "256k mask"
+    rng = np.random.default_rng(4)
+    rows = np.array([[g, I] for g in range(hkv) for I in [1, nb // 3, nb - 1] +
+                     list(rng.choice(nb, 2, replace=False))], np.int32)
+    want = oracle.block_scores(q, k, skel, rows=rows)
+    _check_scores(got[rows[:, 0], rows[:, 1]].astype(np.float64), want, "256k score rows")
+    srows = sample_rows(rng, hq, n, per_head=4)
+    ro, rl = oracle.block_attn(q, k, v, m, rows=srows)
+    og = to_f64(out)[srows[:, 0], srows[:, 1]]
+    lg = lse.cpu().numpy().astype(np.float64)[srows[:, 0], srows[:, 1]]
+    assert_attn_close(og, lg, ro, rl, "256k attention rows")
