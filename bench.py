@@ -142,7 +142,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="zipf128k",
                     choices=["zipf128k", "fixed32k", "indexer128k", "e2e256k", "aggregate32k",
-                             "blocks128k"])
+                             "blocks128k", "blocks256k"])
+    ap.add_argument("--dense-ref", action="store_true",
+                    help="blocks*: also time dense causal attention (the same kernel, every block kept) "
+                         "once, for the speedup")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--alpha", type=float, default=0.01,
@@ -169,7 +172,7 @@ def main():
         return bench_indexer(args, w, torch, vsa, workloads)
     if args.workload == "aggregate32k":
         return bench_aggregate(args, torch, vsa, workloads)
-    if args.workload == "blocks128k":
+    if args.workload in ("blocks128k", "blocks256k"):
         return bench_blocks(args, torch, vsa, workloads)
 
     n, hq, hkv, d = w["n"], w["hq"], w["hkv"], w["d"]
@@ -411,11 +414,12 @@ def bench_blocks(args, torch, vsa, workloads):
     heads, d=128): one step = vs_block_discover (block means, probe scores,
     alpha*max threshold) + vs_block_attn_prefill on inputs resident in HBM."""
     w = workloads.WORKLOADS["blocks128k"]
-    n, hq, hkv, d, bs = w["n"], w["hq"], w["hkv"], w["d"], w["block"]
+    n = 262144 if args.workload == "blocks256k" else w["n"]
+    hq, hkv, d, bs = w["hq"], w["hkv"], w["d"], w["block"]
     group = hq // hkv
     assert group == 4, "tile accounting below assumes one 64-row query block per workgroup"
     t_gen = time.perf_counter()
-    q, k, v = workloads.block_structured_inputs("blocks128k")
+    q, k, v = workloads.block_structured_inputs("blocks128k", n=n)
     print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     qd, kd, vd = _dev(q, torch), _dev(k, torch), _dev(v, torch)
     nb = (n + bs - 1) // bs
@@ -459,14 +463,29 @@ def bench_blocks(args, torch, vsa, workloads):
     probe_flops *= hkv
     eff = f_alg / (ms * 1e-3) / 1e12
     achieved = f_alg / (ms_a * 1e-3) / 1e12
+    dense_ms = None
+    if args.dense_ref:
+        full = np.tril(np.ones((nb, nb), bool))
+        pad = np.zeros((nb, wpr * 32), bool)
+        pad[:, :nb] = full
+        fm = np.packbits(pad, axis=-1, bitorder="little").view(np.int32).reshape(1, nb, wpr)
+        fmask = torch.from_numpy(np.repeat(fm, hkv, 0)).cuda()
+        vsa.vs_block_attn_prefill(qd, kd, vd, fmask, out=out, lse=lse, workspace=aws)
+        e[0].record()
+        vsa.vs_block_attn_prefill(qd, kd, vd, fmask, out=out, lse=lse, workspace=aws)
+        e[1].record()
+        torch.cuda.synchronize()
+        dense_ms = e[0].elapsed_time(e[1])
     res = {
-        "metric": "FlashPrefill block-sparse layer, effective TFLOP/s @128K (discovery + attention)",
+        "metric": f"FlashPrefill block-sparse layer, effective TFLOP/s @{n // 1024}K (discovery + attention)",
         "value": round(eff, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "blocks128k", "n": n, "h_q": hq, "h_kv": hkv, "d": d,
+        "config": {"workload": args.workload, "n": n, "h_q": hq, "h_kv": hkv, "d": d,
                    "alpha": w["alpha"], "skel": w["skel"], "seed": w["seed"]},
         "discover_ms": round(ms_d, 4), "attn_ms": round(ms_a, 4),
+        "dense_causal_ms": None if dense_ms is None else round(dense_ms, 3),
+        "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms, 2),
         "discover_frac": round(ms_d / ms, 4),
         "discover_mfma_tflops": round(probe_flops / (ms_d * 1e-3) / 1e12, 3),
         "tile_density": round(tiles / causal_tiles, 5),

@@ -679,13 +679,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       for (int r = 0; r <= qb1 - qb0; ++r) u |= word_of(r, w);
       return u;
     };
-    int T_total = 0;
-    for (int w0 = 0; w0 < nwords; w0 += kThreads) {
-      const int cnt = w0 + tid < nwords ? __popc(union_word(w0 + tid)) : 0;
-      int tot;
-      block_excl_scan<kThreads>(cnt, &tot, wcnt);
-      T_total += tot;
-    }
     const int tend = nbk;  // a tile index past the keys, in no query block's set
     const int msh = 24 + (i0w / kBN - qb0);
     auto key_word_block = [&](int code, uint32_t& kh0, uint32_t& kh1) {
@@ -731,7 +724,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         ++t;
       }
     };
-    for (int wst = 0; wst < T_total; wst += kListCap) {
+    // lists in windows of kListCap tiles; the pass that fills a window also
+    // counts them all, so a list that fits takes one pass over the mask
+    for (int wst = 0;; wst += kListCap) {
       int base = 0;
       for (int w0 = 0; w0 < nwords; w0 += kThreads) {
         const int w = w0 + tid;
@@ -750,10 +745,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         base += tot;
       }
       __syncthreads();
-      const int T = min(T_total - wst, kListCap);
+      if (base <= wst) break;
+      const int T = min(base - wst, kListCap);
       BlockSrc src{stage_tile, key_word_block, glist, T, tend, 0, 0, 0, 0, 0};
       pipeline(src, T);
       n_dense += T;
+      if (wst + kListCap >= base) break;
     }
   } else {
     // ---- contiguous tiles: the key ranges the slash clusters reach, in
@@ -959,25 +956,49 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   // ---------------- finish: normalise, write O and lse
   const float lt = half_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (wave_rows && qrow < n) {
-    const size_t ro = ((size_t)head * p.hstride + p.row0 + qrow) * D;
+  if constexpr (F32) {
+    if (wave_rows && qrow < n) {
+      const size_t ro = ((size_t)head * p.hstride + p.row0 + qrow) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int d0 = 32 * dt + 8 * a + 4 * half;
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + ro + d0) =
+              float4{acc[dt][4 * a] * inv, acc[dt][4 * a + 1] * inv, acc[dt][4 * a + 2] * inv,
+                     acc[dt][4 * a + 3] * inv};
+        }
+    }
+  } else {
+    // O leaves through LDS (the K/V rings are idle after the last drain
+    // barrier): a wave's 32 rows are contiguous in HBM, so after a transpose
+    // each store moves whole rows, 1 KiB per instruction, instead of 8-byte
+    // pieces of 32 rows.  16-byte chunks are XOR-swizzled by row.
+    constexpr int OCH = D / 8;
+    lds_u8* const ob = kv_base + wave * 32 * ROWB;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int d0 = 32 * dt + 8 * a + 4 * half;
-        const float o0 = acc[dt][4 * a] * inv, o1 = acc[dt][4 * a + 1] * inv;
-        const float o2 = acc[dt][4 * a + 2] * inv, o3 = acc[dt][4 * a + 3] * inv;
-        if constexpr (F32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + ro + d0) = float4{o0, o1, o2, o3};
-        } else {
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + ro + d0) =
-              u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
-        }
+        const int pc = (4 * dt + a) ^ (ql & (OCH - 1));
+        *(__attribute__((address_space(3))) u32x2*)(ob + ql * ROWB + pc * 16 + 8 * half) =
+            u32x2{pack_bf16(acc[dt][4 * a] * inv, acc[dt][4 * a + 1] * inv),
+                  pack_bf16(acc[dt][4 * a + 2] * inv, acc[dt][4 * a + 3] * inv)};
       }
-    if (half == 0 && p.lse)
-      p.lse[(size_t)head * p.hstride + p.row0 + qrow] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -__builtin_inff();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's rows are in LDS
+    __builtin_amdgcn_wave_barrier();
+    constexpr int RPI = 1024 / ROWB;     // rows per store instruction
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int r = it * RPI + lane / OCH, c = lane % OCH;
+      const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(ob + r * ROWB + 16 * (c ^ (r & (OCH - 1))));
+      if (wave_rows && i0w + r < n)
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) +
+                                  ((size_t)head * p.hstride + p.row0 + i0w + r) * D + 8 * c) = val;
+    }
   }
+  if (wave_rows && qrow < n && half == 0 && p.lse)
+    p.lse[(size_t)head * p.hstride + p.row0 + qrow] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -__builtin_inff();
   if (tid == 0 && p.stats) {
     atomicAdd(&p.stats[0], (unsigned long long)n_dense);
     atomicAdd(&p.stats[1], (unsigned long long)n_gath);
