@@ -236,8 +236,8 @@ vs_status vs_attn_aggregate(const void* q, const void* k, const void* v, int h_q
  * Block means are summed in fp32 and held as a bf16 pair (about 16
  * significant bits); the scores run on the matrix cores with fp32
  * accumulation.  Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8, 16};
- * nb <= 8192 (the scores of four query blocks stay in LDS).  The workspace
- * holds the block means.  Nothing is allocated; the calls only enqueue. */
+ * nb <= 16384.  The workspace holds the block means.  Nothing is allocated;
+ * the calls only enqueue. */
 size_t vs_block_workspace_bytes(int h_kv, int n, int d);
 vs_status vs_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,
                             float scale, int skel, float alpha, uint32_t* mask, int words_per_row,

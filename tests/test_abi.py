@@ -126,7 +126,7 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert disc(wpr=0) == vsa.VS_ERR_INVALID             # 16 blocks need one word
     assert disc(d=96) == vsa.VS_ERR_UNSUPPORTED
     assert disc(h_q=6) == vsa.VS_ERR_UNSUPPORTED
-    assert disc(n=8192 * 64 + 1, wpr=257) == vsa.VS_ERR_UNSUPPORTED   # more than 8192 blocks
+    assert disc(n=16384 * 64 + 1, wpr=513) == vsa.VS_ERR_UNSUPPORTED   # more than 16384 blocks
     assert disc(ws_bytes=16) == vsa.VS_ERR_WORKSPACE
     assert L.vs_block_workspace_bytes(2, 1000, 128) == 2 * 2 * 16 * 128 * 2
     # vs_block_attn_prefill

@@ -216,11 +216,6 @@ vs_status vs_block_discover(const void* q, const void* k, int h_q, int h_kv, int
   if ((h_q / h_kv) * skel > 32) return VS_ERR_UNSUPPORTED;
   if (nb > kBlkMaxBlocks) return VS_ERR_UNSUPPORTED;
   if (ws_bytes < vs_block_workspace_bytes(h_kv, n, d)) return VS_ERR_WORKSPACE;
-  int dev = 0, lds = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-    return VS_ERR_HIP;
-  if (block_score_lds_bytes(n, d) + 1024 > (size_t)lds) return VS_ERR_UNSUPPORTED;
   return from_hip(launch_block_discover(q, k, h_q, h_kv, n, d, scale, skel, alpha, mask,
                                         words_per_row, score, ws, stream));
 }

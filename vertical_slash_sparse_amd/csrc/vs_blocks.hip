@@ -25,10 +25,12 @@
 //    workgroup by LDS-DMA two stages deep and read by all four waves, whose
 //    query blocks need nearly the same chunks.  Pass 1 runs
 //    S^T = Kbar Q^T, so each lane owns one probe and keeps its running max
-//    and sum over blocks; pass 2 runs S = Q Kbar^T, so each lane owns one
-//    block and adds the probes' normalised probabilities over its elements.
-//    Scores stay in LDS until the row maximum is known; the threshold is one
-//    fp32 product and the kept flags become mask words through ballots.
+//    and sum over blocks; passes 2 and 3 run S = Q Kbar^T, so each lane owns
+//    one block and adds the probes' normalised probabilities over its
+//    elements: pass 2 for the row's largest score, pass 3 to recompute the
+//    scores and threshold them (one fp32 product) into mask words through
+//    ballots, a word per chunk.  Keeping no score row leaves LDS to the chunk
+//    stages (32 KiB), so several workgroups share a CU.
 #include "vs_common.h"
 #include "vs_internal.h"
 
@@ -104,10 +106,10 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
   constexpr int RPD = 1024 / ROWB;               // rows per 1 KiB DMA
   constexpr int NDMA = STB / 1024 / kBlkWaves;   // DMAs per wave per chunk
   static_assert(NDMA >= 1 && NDMA * kBlkWaves * 1024 == STB, "chunk split");
-  extern __shared__ __align__(16) uint8_t dyn[];  // 2 chunk stages, then [kBlkWaves][nb] scores
+  __shared__ __align__(16) uint8_t stages[2 * STB];                 // two chunk stages
   __shared__ float st_m[kBlkWaves][32], st_w[kBlkWaves][32];  // per probe: max, weight / sum
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
-  lds_u8* const stg = (lds_u8*)dyn;
+  lds_u8* const stg = (lds_u8*)stages;
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, ql = lane & 31;
   const int wave = wave_uniform(tid >> 6);
@@ -117,7 +119,6 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
   const int I = I0 + wave;                      // this wave's query block
   const bool active = I < p.nb;
   const int n = p.n, nb = p.nb;
-  float* sc = reinterpret_cast<float*>(dyn + 2 * STB) + wave * nb;
 
   // probe slot ql: head ql / skel of the group, row 64 I + (ql % skel) * (64 / skel)
   const int step = kBN / p.skel;
@@ -233,8 +234,12 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
   }
   __syncthreads();
 
-  // ---- pass 2: S = Q Kbar^T; lane (ql, half) holds block 32 c + ql against
-  // probes 8 (e / 4) + 4 half + e % 4
+  // ---- passes 2 and 3: S = Q Kbar^T; lane (ql, half) holds block 32 c + ql
+  // against probes 8 (e / 4) + 4 half + e % 4.  Pass 2 finds the row's
+  // largest score, pass 3 recomputes the same scores (same instructions,
+  // explicit fused multiply-adds, so the same fp32 values) and thresholds
+  // them: one chunk of 32 blocks is one mask word.  No score row is kept, so
+  // LDS holds only the two chunk stages.
   float nm[16], wl[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -242,8 +247,7 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
     nm[e] = -st_m[wave][pr];
     wl[e] = st_w[wave][pr];
   }
-  sweep([&](int c, int st) {
-    const int J = c * 32 + ql;
+  auto score_of = [&](int st) -> float {
     f32x16 acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
@@ -253,30 +257,33 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
     for (int s = 0; s < KS; ++s) acc = mfma32(qf[s], kfrag(st, 1, s), acc);
     float t = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) t += __builtin_amdgcn_exp2f(fmaf(acc[e], p.c, nm[e])) * wl[e];
-    t = half_sum(t);
-    if (half == 0 && J < nb) sc[J] = J < I ? t : 0.f;
-  });
-  if (!active) return;
-
-  // ---- threshold: alpha times the row's largest score, one fp32 product
+    for (int e = 0; e < 16; ++e) t = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[e], p.c, nm[e])), wl[e], t);
+    return half_sum(t);
+  };
   float mx = 0.f;
-  for (int J = lane; J < I; J += 64) mx = fmaxf(mx, sc[J]);
+  sweep([&](int c, int st) {
+    const float t = score_of(st);
+    if (c * 32 + ql < I) mx = fmaxf(mx, t);
+  });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  // threshold: alpha times the row's largest score, one fp32 product
   const float thr = __fmul_rn(p.alpha, mx);
   uint32_t* mrow = p.mask + ((size_t)g * nb + I) * p.wpr;
-  for (int w0 = 0; w0 < p.wpr; w0 += 2) {
-    const int J = 32 * w0 + lane;
-    const bool keep = J == I || (J < I && sc[J] >= thr);
+  float* srow = p.score ? p.score + ((size_t)g * nb + I) * nb : nullptr;
+  sweep([&](int c, int st) {
+    const float t = score_of(st);
+    const int J = c * 32 + ql;
+    const bool keep = J == I || (J < I && t >= thr);
     const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
-    if (lane == 0) mrow[w0] = (uint32_t)bal;
-    if (lane == 32 && w0 + 1 < p.wpr) mrow[w0 + 1] = (uint32_t)(bal >> 32);
-  }
-  if (p.score) {
-    float* srow = p.score + ((size_t)g * nb + I) * nb;
-    for (int J = lane; J < nb; J += 64) srow[J] = J < I ? sc[J] : 0.f;
-  }
+    if (lane == 0) mrow[c] = (uint32_t)bal;
+    if (srow && half == 0 && J < nb) srow[J] = J < I ? t : 0.f;
+  });
+  if (!active) return;
+  // words past the last chunk: only the diagonal can be set there
+  for (int w = mych + lane; w < p.wpr; w += 64) mrow[w] = I / 32 == w ? 1u << (I % 32) : 0u;
+  if (srow)
+    for (int J = 32 * mych + lane; J < nb; J += 64) srow[J] = 0.f;
 }
 
 }  // namespace
@@ -284,11 +291,6 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
 size_t block_workspace_bytes(int h_kv, int n, int d) {
   const size_t nb = (size_t)(n + kBN - 1) / kBN;
   return 2 * align_up(sizeof(uint16_t) * (size_t)h_kv * nb * d, 256);
-}
-
-size_t block_score_lds_bytes(int n, int d) {
-  return 2 * 2 * 32 * (size_t)d * 2 +  // two stages of 32 mean-key rows, hi and lo
-         sizeof(float) * (size_t)kBlkWaves * (size_t)((n + kBN - 1) / kBN);
 }
 
 hipError_t launch_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,
@@ -318,15 +320,10 @@ hipError_t launch_block_discover(const void* q, const void* k, int h_q, int h_kv
   prm.c = scale * 1.4426950408889634f;
   prm.alpha = alpha;
   const dim3 sg((unsigned)(((nb + kBlkWaves - 1) / kBlkWaves) * h_kv));
-  const size_t lds = block_score_lds_bytes(n, d);
-  const void* fn = d == 128 ? reinterpret_cast<const void*>(&blk_score_kernel<128>)
-                            : reinterpret_cast<const void*>(&blk_score_kernel<64>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   if (d == 128)
-    hipLaunchKernelGGL(blk_score_kernel<128>, sg, dim3(kBlkThreads), lds, stream, prm);
+    hipLaunchKernelGGL(blk_score_kernel<128>, sg, dim3(kBlkThreads), 0, stream, prm);
   else
-    hipLaunchKernelGGL(blk_score_kernel<64>, sg, dim3(kBlkThreads), lds, stream, prm);
+    hipLaunchKernelGGL(blk_score_kernel<64>, sg, dim3(kBlkThreads), 0, stream, prm);
   return hipGetLastError();
 }
 

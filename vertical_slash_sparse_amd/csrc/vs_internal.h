@@ -83,9 +83,8 @@ hipError_t launch_attn_blocks(const void* q, const void* k, const void* v, bool 
                               void* out, float* lse, void* ws, hipStream_t stream);
 
 // FlashPrefill block discovery
-constexpr int kBlkMaxBlocks = 8192;  // key blocks a discovery call may have
+constexpr int kBlkMaxBlocks = 16384;  // key blocks a discovery call may have
 size_t block_workspace_bytes(int h_kv, int n, int d);
-size_t block_score_lds_bytes(int n, int d);
 hipError_t launch_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,
                                  float scale, int skel, float alpha, uint32_t* mask, int wpr,
                                  float* score, void* ws, hipStream_t stream);
