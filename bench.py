@@ -368,19 +368,22 @@ def bench_aggregate(args, torch, vsa, workloads):
     a_v = torch.empty((hkv, n), dtype=torch.float32, device="cuda")
     a_s = torch.empty((hkv, n), dtype=torch.float32, device="cuda")
     ws = torch.empty(vsa.vs_aggregate_workspace_bytes(hkv, n), dtype=torch.uint8, device="cuda")
-    # pass 1 alone: the same dense attention through the prefill entry point
-    soff = torch.arange(n, dtype=torch.int32, device="cuda").repeat(hkv, 1).contiguous()
-    scnt = torch.full((hkv,), n, dtype=torch.int32, device="cuda")
-    vidx = torch.full((hkv, 1), -1, dtype=torch.int32, device="cuda")
-    vcnt = torch.zeros((hkv,), dtype=torch.int32, device="cuda")
-    aws = torch.empty(vsa.vs_attn_workspace_bytes(hkv, n, 1, n), dtype=torch.uint8, device="cuda")
+    # an estimate of pass 1 alone: dense causal attention through the block
+    # entry point with every block kept (the same full-tile kernel path)
+    nb = n // 64
+    wpr = vsa.block_words_per_row(n)
+    full = np.zeros((nb, wpr * 32), bool)
+    full[:, :nb] = np.tril(np.ones((nb, nb), bool))
+    fm = np.packbits(full, axis=-1, bitorder="little").view(np.int32).reshape(1, nb, wpr)
+    fmask = torch.from_numpy(np.repeat(fm, hkv, 0)).cuda()
+    aws = torch.empty(256, dtype=torch.uint8, device="cuda")
     e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     tt, t1 = [], []
     for it in range(args.warmup + args.steps):
         e[0].record()
         vsa.vs_attn_aggregate(qd, kd, vd, out=out, lse=lse, a_v=a_v, a_s=a_s, workspace=ws)
         e[1].record()
-        vsa.vs_sparse_attn_prefill(qd, kd, vd, vidx, vcnt, soff, scnt, out=out, lse=lse, workspace=aws)
+        vsa.vs_block_attn_prefill(qd, kd, vd, fmask, out=out, lse=lse, workspace=aws)
         e[2].record()
         torch.cuda.synchronize()
         if it >= args.warmup:

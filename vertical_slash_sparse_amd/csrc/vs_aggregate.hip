@@ -275,8 +275,10 @@ hipError_t launch_aggregate(const void* q, const void* k, const void* v, int h_q
   void* attn_ws = base + o;
   hipLaunchKernelGGL(agg_prepare_kernel, dim3((unsigned)((n + 255) / 256), (unsigned)h_kv), dim3(256),
                      0, stream, s_off, s_cnt, v_idx, v_cnt, a_v, a_s, n);
+  AttnLayout dense;
+  dense.full_tiles = true;  // every offset is selected
   hipError_t err = launch_attn(q, k, v, false, h_q, h_kv, n, d, scale, v_idx, v_cnt, 1, s_off, s_cnt, n,
-                               out, lse, attn_ws, stream);
+                               out, lse, attn_ws, stream, dense);
   if (err != hipSuccess) return err;
   AggParams prm;
   prm.q = q;

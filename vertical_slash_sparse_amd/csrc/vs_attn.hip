@@ -267,7 +267,12 @@ struct MhalfOrder {
   }
 };
 
-template <int D, bool F32, bool BLK>
+// FULL: test each tile for "every key in every row's set" and skip the
+// per-element masks there.  Worth it only when most tiles are full (the block
+// mode's interior tiles, every offset selected): a set that leaves a few keys
+// out of most tiles pays for the test and loses the interleaving of masks
+// and maxima (measured 3.5 % slower on a 98 %-dense 256K layer).
+template <int D, bool F32, bool BLK, bool FULL>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   constexpr int KS = D / 16;            // k-steps of Q K^T
   constexpr int DT = D / 32;            // 32-row tiles of O^T
@@ -539,15 +544,33 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   // and leaves the probabilities in pk
   auto softmax = [&](uint32_t kc0, uint32_t kc1) {
     float pm[4];
+    // a full tile (the element bits 0x0F0F0F0F of both key words set in every
+    // lane) skips the masks; FULL = false keeps masking and maxima interleaved
+    bool full = false;
+    if constexpr (FULL) full = __builtin_amdgcn_ballot_w64((kc0 & kc1 & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) == 0;
+    if constexpr (FULL) {
+      if (!full) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int bpos = 8 * (e >> 2) + (e & 3);
+          const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, bpos, 1);
+          const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, bpos, 1);
+          c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
+          c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
+        }
+      }
+    }
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
+      if constexpr (!FULL) {
 #pragma unroll
-      for (int e = 4 * q4; e < 4 * q4 + 4; ++e) {
-        const int bpos = 8 * (e >> 2) + (e & 3);
-        const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, bpos, 1);
-        const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, bpos, 1);
-        c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
-        c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
+        for (int e = 4 * q4; e < 4 * q4 + 4; ++e) {
+          const int bpos = 8 * (e >> 2) + (e & 3);
+          const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, bpos, 1);
+          const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, bpos, 1);
+          c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
+          c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
+        }
       }
       const int e = 4 * q4;
       pm[q4] = __builtin_elementwise_maximum(
@@ -1082,12 +1105,25 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
   prm.hstride = lay.hstride ? lay.hstride : n;
   prm.row0 = lay.row0;
   const dim3 grid((unsigned)((long long)prm.nblocks * h_kv * nsplit));
+  // a caller that knows most tiles are full (every offset selected) takes
+  // the instantiation that skips their masks
+  const bool dense = lay.full_tiles;
   if (d == 128) {
-    if (f32) hipLaunchKernelGGL((attn_kernel<128, true, false>), grid, dim3(kThreads), 0, stream, prm);
-    else hipLaunchKernelGGL((attn_kernel<128, false, false>), grid, dim3(kThreads), 0, stream, prm);
+    if (dense) {
+      if (f32) hipLaunchKernelGGL((attn_kernel<128, true, false, true>), grid, dim3(kThreads), 0, stream, prm);
+      else hipLaunchKernelGGL((attn_kernel<128, false, false, true>), grid, dim3(kThreads), 0, stream, prm);
+    } else {
+      if (f32) hipLaunchKernelGGL((attn_kernel<128, true, false, false>), grid, dim3(kThreads), 0, stream, prm);
+      else hipLaunchKernelGGL((attn_kernel<128, false, false, false>), grid, dim3(kThreads), 0, stream, prm);
+    }
   } else {
-    if (f32) hipLaunchKernelGGL((attn_kernel<64, true, false>), grid, dim3(kThreads), 0, stream, prm);
-    else hipLaunchKernelGGL((attn_kernel<64, false, false>), grid, dim3(kThreads), 0, stream, prm);
+    if (dense) {
+      if (f32) hipLaunchKernelGGL((attn_kernel<64, true, false, true>), grid, dim3(kThreads), 0, stream, prm);
+      else hipLaunchKernelGGL((attn_kernel<64, false, false, true>), grid, dim3(kThreads), 0, stream, prm);
+    } else {
+      if (f32) hipLaunchKernelGGL((attn_kernel<64, true, false, false>), grid, dim3(kThreads), 0, stream, prm);
+      else hipLaunchKernelGGL((attn_kernel<64, false, false, false>), grid, dim3(kThreads), 0, stream, prm);
+    }
   }
   return hipGetLastError();
 }
@@ -1123,11 +1159,11 @@ hipError_t launch_attn_blocks(const void* q, const void* k, const void* v, bool 
   prm.row0 = 0;
   const dim3 grid((unsigned)((long long)prm.nblocks * h_kv * nsplit));
   if (d == 128) {
-    if (f32) hipLaunchKernelGGL((attn_kernel<128, true, true>), grid, dim3(kThreads), 0, stream, prm);
-    else hipLaunchKernelGGL((attn_kernel<128, false, true>), grid, dim3(kThreads), 0, stream, prm);
+    if (f32) hipLaunchKernelGGL((attn_kernel<128, true, true, true>), grid, dim3(kThreads), 0, stream, prm);
+    else hipLaunchKernelGGL((attn_kernel<128, false, true, true>), grid, dim3(kThreads), 0, stream, prm);
   } else {
-    if (f32) hipLaunchKernelGGL((attn_kernel<64, true, true>), grid, dim3(kThreads), 0, stream, prm);
-    else hipLaunchKernelGGL((attn_kernel<64, false, true>), grid, dim3(kThreads), 0, stream, prm);
+    if (f32) hipLaunchKernelGGL((attn_kernel<64, true, true, true>), grid, dim3(kThreads), 0, stream, prm);
+    else hipLaunchKernelGGL((attn_kernel<64, false, true, true>), grid, dim3(kThreads), 0, stream, prm);
   }
   return hipGetLastError();
 }

@@ -66,6 +66,7 @@ struct AttnLayout {
   int kvdiv = 1;
   long long hstride = 0;
   long long row0 = 0;
+  bool full_tiles = false;  // nearly every tile has all its keys selected
 };
 
 hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, int h_q, int h_kv,
