@@ -56,22 +56,6 @@ __global__ __launch_bounds__(kIdxThreads, 2) void index_kernel(const uint16_t* _
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, ql = lane & 31;
   const int wave = wave_uniform(tid >> 6);
 
-  // W1 rows 32*wave + ql as A operands (k-step s: input dims 16s + 8*half ..)
-  bf16x8 wa[kIdxKS];
-#pragma unroll
-  for (int s = 0; s < kIdxKS; ++s)
-    wa[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(w1 + (size_t)(32 * wave + ql) * kIdxX + 16 * s + 8 * half));
-  // W2 for the hidden units this lane's accumulators hold: 32*wave + 8a + 4*half + b
-  float w2v[16], w2s[16];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int h = 32 * wave + 8 * a + 4 * half + b;
-      w2v[4 * a + b] = __uint_as_float((uint32_t)w2[h] << 16);
-      w2s[4 * a + b] = __uint_as_float((uint32_t)w2[kIdxH + h] << 16);
-    }
-
   // DMA: wave w moves kIdxDma KiB of each block; a KiB holds 4 rows, lane l
   // row (l / 16) of them, chunk slot l % 16, which holds source chunk
   // slot ^ swizzle(row)
@@ -108,6 +92,24 @@ __global__ __launch_bounds__(kIdxThreads, 2) void index_kernel(const uint16_t* _
   if (first >= nblk) return;
   const long long mine = (nblk - first + stride - 1) / stride;  // blocks of this workgroup
   for (int j = 0; j < kIdxNst - 1; ++j) stage_block(first + j * stride < nblk ? first + j * stride : nblk, j);
+
+  // The first blocks' loads are already in flight: the weights' own latency
+  // (they come from L2 or HBM on a call's first use) overlaps them.
+  // W1 rows 32*wave + ql as A operands (k-step s: input dims 16s + 8*half ..)
+  bf16x8 wa[kIdxKS];
+#pragma unroll
+  for (int s = 0; s < kIdxKS; ++s)
+    wa[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(w1 + (size_t)(32 * wave + ql) * kIdxX + 16 * s + 8 * half));
+  // W2 for the hidden units this lane's accumulators hold: 32*wave + 8a + 4*half + b
+  float w2v[16], w2s[16];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int h = 32 * wave + 8 * a + 4 * half + b;
+      w2v[4 * a + b] = __uint_as_float((uint32_t)w2[h] << 16);
+      w2s[4 * a + b] = __uint_as_float((uint32_t)w2[kIdxH + h] << 16);
+    }
 
   for (long long it = 0; it <= mine; ++it) {
     // this wave's loads of block `it` have landed once at most the newer
