@@ -151,17 +151,35 @@ def attn_qh(q, k, v, vidx, vcnt, soff, scnt, scale=None, rows=None, nthreads=0):
 
 
 def attn_varlen(q, k, v, cu_seqlens, vidx, vcnt, soff, scnt, per_query_head=False, scale=None,
-                nthreads=0):
+                rows=None, nthreads=0):
     """Packed batch: sequence s is rows cu[s]..cu[s+1]-1 of every head and
     attends only within itself, with its own lists vidx[s] ... (positions
-    relative to its first row).  Returns (out [hq, total, d], lse [hq, total])."""
+    relative to its first row).  Returns (out [hq, total, d], lse [hq, total]),
+    or with ``rows`` (int [m, 2] of (head, packed row)) (out [m, d], lse [m])."""
     q, k, v = _c(q), _c(k), _c(v)
     hq, total, d = q.shape
+    fn = attn_qh if per_query_head else attn
+    cu = [int(x) for x in cu_seqlens]
+    if rows is not None:
+        rows = _c(rows, np.int32).reshape(-1, 2)
+        out = np.zeros((rows.shape[0], d), dtype=np.float64)
+        lse = np.zeros(rows.shape[0], dtype=np.float64)
+        seq = np.searchsorted(np.array(cu), rows[:, 1], side="right") - 1
+        for s in range(len(cu) - 1):
+            sel = np.nonzero(seq == s)[0]
+            if len(sel) == 0:
+                continue
+            a, b = cu[s], cu[s + 1]
+            local = np.stack([rows[sel, 0], rows[sel, 1] - a], axis=1)
+            o, l = fn(q[:, a:b], k[:, a:b], v[:, a:b], vidx[s], vcnt[s], soff[s], scnt[s],
+                      scale=scale, rows=local, nthreads=nthreads)
+            out[sel] = o
+            lse[sel] = l
+        return out, lse
     out = np.zeros((hq, total, d), dtype=np.float64)
     lse = np.zeros((hq, total), dtype=np.float64)
-    fn = attn_qh if per_query_head else attn
-    for s in range(len(cu_seqlens) - 1):
-        a, b = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
         if b == a:
             continue
         o, l = fn(q[:, a:b], k[:, a:b], v[:, a:b], vidx[s], vcnt[s], soff[s], scnt[s],

@@ -10,7 +10,7 @@ import torch
 import oracle
 import vertical_slash_sparse_amd as vsa
 import workloads
-from tests.util import assert_attn_close, to_dev, to_f64
+from tests.util import assert_attn_close, sample_rows, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -98,3 +98,56 @@ def test_varlen(case):
     torch.cuda.synchronize()
     ro, rl = oracle.attn_varlen(q, k, v, cu, *stack, per_query_head=per_qh)
     assert_attn_close(to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl, f"varlen {case}")
+
+
+def _zipf_logits(rng, heads, n, s=1.1):
+    """Zipf(s) scores over a random permutation of ranks, one row per head."""
+    out = np.empty((heads, n), np.float32)
+    for h in range(heads):
+        out[h] = (-s * np.log(rng.permutation(n) + 1.0)).astype(np.float32)
+    return out
+
+
+def test_per_query_head_sets_32k_sampled():
+    """32/8 heads at n = 32768: every query head selects its own columns and
+    offsets from its own Zipf scores (mass 0.95, caps 1024 / 2048); sampled
+    rows against the oracle."""
+    _log("case: qh 32k sampled")
+    rng = np.random.default_rng(41)
+    hq, hkv, n, d = 32, 8, 32768, 128
+    q, k, v = workloads.attention_inputs("fixed32k")
+    vi, vc = vsa.vs_select(to_dev(_zipf_logits(rng, hq, n)), vsa.VS_VERTICAL, 0.95, 1024)
+    si, sc = vsa.vs_select(to_dev(_zipf_logits(rng, hq, n)), vsa.VS_SLASH, 0.95, 2048)
+    out, lse = vsa.vs_sparse_attn_prefill_qh(to_dev(q), to_dev(k), to_dev(v), vi, vc, si, sc)
+    torch.cuda.synchronize()
+    lists = [t.cpu().numpy() for t in (vi, vc, si, sc)]
+    rows = sample_rows(rng, hq, n, per_head=5)
+    ro, rl = oracle.attn_qh(q, k, v, *lists, rows=rows)
+    og = to_f64(out)[rows[:, 0], rows[:, 1]]
+    lg = lse.cpu().numpy().astype(np.float64)[rows[:, 0], rows[:, 1]]
+    assert_attn_close(og, lg, ro, rl, "qh 32k")
+
+
+def test_varlen_48k_sampled():
+    """Three sequences (8192, 24576, 16384 rows) of the 32/8-head layer, per
+    query head sets of 500 columns and 1000 offsets each; sampled rows."""
+    _log("case: varlen 48k sampled")
+    rng = np.random.default_rng(42)
+    hq, hkv, d = 32, 8, 128
+    cu = [0, 8192, 8192 + 24576, 8192 + 24576 + 16384]
+    total = cu[-1]
+    q, k, v = _inputs(rng, hq, hkv, total, d, "bf16")
+    per_seq = [_rand_lists(rng, hq, cu[s + 1] - cu[s], 500, 1000, cap_v=500, cap_s=1001)
+               for s in range(3)]
+    stack = [np.stack([ps[i] for ps in per_seq]) for i in range(4)]
+    out, lse = vsa.vs_sparse_attn_prefill_varlen(to_dev(q), to_dev(k), to_dev(v), cu,
+                                                 *[to_dev(x) for x in stack], per_query_head=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(rng, hq, total, per_head=4)
+    extra = np.array([[h, r] for h in (0, hq - 1) for r in (cu[1] - 1, cu[1], cu[2] - 1, cu[2])],
+                     np.int32)
+    rows = np.concatenate([rows, extra])
+    ro, rl = oracle.attn_varlen(q, k, v, cu, *stack, per_query_head=True, rows=rows)
+    og = to_f64(out)[rows[:, 0], rows[:, 1]]
+    lg = lse.cpu().numpy().astype(np.float64)[rows[:, 0], rows[:, 1]]
+    assert_attn_close(og, lg, ro, rl, "varlen 48k")

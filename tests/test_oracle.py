@@ -583,6 +583,11 @@ def test_varlen_sequences_are_independent_and_match_single_calls():
         o, l = oracle.attn(q[:, a:b], k[:, a:b], v[:, a:b], *per_seq[s])
         np.testing.assert_array_equal(out[:, a:b], o)
         np.testing.assert_array_equal(lse[:, a:b], l)
+    # sampled rows equal the full computation's rows
+    srows = np.array([[0, 0], [3, 69], [1, 70], [2, 150], [3, 200]], np.int32)
+    so, sl = oracle.attn_varlen(q, k, v, cu, *stack, rows=srows)
+    np.testing.assert_array_equal(so, out[srows[:, 0], srows[:, 1]])
+    np.testing.assert_array_equal(sl, lse[srows[:, 0], srows[:, 1]])
     # changing the last sequence's keys leaves the others untouched
     k2 = k.copy()
     k2[:, 200:] += 1.0
