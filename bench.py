@@ -330,6 +330,31 @@ def bench_indexer(args, w, torch, vsa, workloads):
             tt.append(e[0].elapsed_time(e[1]))
     ms_t = float(np.mean(tt))
     kept_t = {"vertical": vc.cpu().tolist(), "slash": sc.cpu().tolist()}
+    # the same step (index + both selections) captured once in a HIP graph and
+    # replayed: the chain is 24 short launches, so launch overhead is visible
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        vsa.vs_index(kd, vd, w1d, w2d, vlog, slog)
+        vsa.vs_select(vlog, vsa.VS_VERTICAL, w["mass"], n, vi, vc, ws)
+        vsa.vs_select(slog, vsa.VS_SLASH, w["mass"], n, si, sc, ws)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        vsa.vs_index(kd, vd, w1d, w2d, vlog, slog)
+        vsa.vs_select(vlog, vsa.VS_VERTICAL, w["mass"], n, vi, vc, ws)
+        vsa.vs_select(slog, vsa.VS_SLASH, w["mass"], n, si, sc, ws)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e[0].record()
+    for _ in range(args.steps):
+        graph.replay()
+    e[1].record()
+    torch.cuda.synchronize()
+    ms_graph = e[0].elapsed_time(e[1]) / args.steps
+    graph_budgets_ok = bool((vc.cpu().numpy() == budgets_v).all() and (sc.cpu().numpy() == budgets_s).all())
     bytes_alg = hkv * n * (2 * d * 2) + hkv * n * 8   # read K,V rows; write two fp32 logits
     # selection, both kinds: read the logits, write the chosen indices and counts
     sel_bytes = 2 * hkv * n * 4 + 4 * int(budgets_v.sum() + budgets_s.sum()) + 2 * hkv * 4
@@ -343,6 +368,7 @@ def bench_indexer(args, w, torch, vsa, workloads):
         "config": {"workload": "indexer128k", "n": n, "h_kv": hkv, "d": d, "hidden": w["hidden"],
                    "mass": w["mass"], "seed": w["seed"]},
         "index_ms": round(ms_i, 4), "select_ms": round(ms_s, 4),
+        "graph_step_ms": round(ms_graph, 4), "graph_matches_eager": graph_budgets_ok,
         "select_gbs": round(sel_bytes / (ms_s * 1e-3) / 1e9, 1),
         "threshold": {"alpha": alpha, "ms": round(ms_t, 4), "kept": kept_t},
         "index_tflops": round(flops / (ms_i * 1e-3) / 1e12, 3),
