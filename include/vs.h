@@ -122,14 +122,16 @@ vs_status vs_select_threshold(const float* logit, int heads, int n, vs_kind kind
  * contiguous key tiles (slash ranges, with a per-element diagonal mask) and
  * gathered tiles (verticals no slash range covers); no n x n mask is built.
  *   q          : [h_q][n][d], k, v : [h_kv][n][d], all of dtype `dt`
- *   v_idx      : int32 [h_kv][cap_v] vertical columns, strictly ascending
+ *   v_idx      : int32 [h_kv][cap_v] vertical columns, in any order (vs_select
+ *                writes them ascending)
  *   v_cnt      : int32 [h_kv] number of valid entries (clamped to [0, cap_v])
- *   s_off      : int32 [h_kv][cap_s] slash offsets, strictly ascending
+ *   s_off      : int32 [h_kv][cap_s] slash offsets, in any order
  *   s_cnt      : int32 [h_kv]
  *   out        : [h_q][n][d] of dtype `dt`;  lse : fp32 [h_q][n] or NULL
  *   ws         : device workspace of at least
  *                vs_attn_workspace_bytes(h_kv, n, cap_v, cap_s)
- * Entries outside [0, n) are ignored; duplicates count once.  bf16 (or fp32
+ * The lists are read into bitmaps, so entries outside [0, n) are ignored and
+ * duplicates count once.  bf16 (or fp32
  * rounded to bf16) MFMA products with fp32 softmax and accumulation.
  * Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8, 16}. */
 size_t vs_attn_workspace_bytes(int h_kv, int n, int cap_v, int cap_s);

@@ -132,8 +132,8 @@ def test_value_ones_gives_ones():
 
 
 def test_index_list_contract():
-    """Duplicates and out-of-range entries are ignored; counts beyond the
-    capacity are clamped."""
+    """Lists may come in any order; duplicates and out-of-range entries are
+    ignored; counts beyond the capacity are clamped."""
     _log("case: list contract")
     rng = np.random.default_rng(8)
     hq, hkv, n, d = 4, 1, 300, 64
