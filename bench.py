@@ -5,8 +5,10 @@ Q/K/V with RoPE, Zipf(1.1) vertical and slash score vectors, budgets chosen by
 cumulative softmax mass 0.95 capped at 4096 columns / 8192 offsets per KV
 head.  One step = vs_select (columns) + vs_select (offsets) +
 vs_sparse_attn_prefill (tile build + attention) on inputs already resident in
-HBM.  Other workloads (``fixed32k``, ``indexer128k``, ``e2e256k``) can be
-timed with ``--workload``; ``e2e256k`` adds vs_index in front.
+HBM.  Other workloads (``fixed32k``, ``indexer128k``, ``e2e256k``,
+``clustered128k``, ...) can be timed with ``--workload``; ``e2e256k`` adds
+vs_index in front, ``clustered128k`` is the 128K layer with the selected
+columns and offsets in contiguous runs (a supplementary workload).
 
 Printed as one JSON line: ms per layer, effective (algorithmic) TFLOP/s =
 4*d*sum_h sum_i |S_i| / time, the computed-tile rate, a roofline object for
@@ -141,8 +143,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="zipf128k",
-                    choices=["zipf128k", "fixed32k", "indexer128k", "e2e256k", "aggregate32k",
-                             "blocks128k", "blocks256k"])
+                    choices=["zipf128k", "clustered128k", "fixed32k", "indexer128k", "e2e256k",
+                             "aggregate32k", "blocks128k", "blocks256k"])
     ap.add_argument("--dense-ref", action="store_true",
                     help="blocks*: also time dense causal attention (the same kernel, every block kept) "
                          "once, for the speedup")
@@ -180,8 +182,9 @@ def main():
     q, k, v = workloads.attention_inputs(args.workload)
     qd, kd, vd = _dev(q, torch), _dev(k, torch), _dev(v, torch)
     w1d = w2d = None
-    if args.workload == "zipf128k":
-        vlog, slog = workloads.zipf_scores(args.workload)
+    if args.workload in ("zipf128k", "clustered128k"):
+        scores = workloads.zipf_scores if args.workload == "zipf128k" else workloads.clustered_scores
+        vlog, slog = scores(args.workload)
         vlog_d, slog_d = _dev(vlog, torch), _dev(slog, torch)
         cap_v, cap_s, mass = w["cap_v"], w["cap_s"], w["mass"]
     elif args.workload == "e2e256k":
@@ -273,6 +276,8 @@ def main():
         "pair_density": round(float(pairs.sum()) / causal_pairs, 5),
         "tile_density": round((dense_t + gath_t) / causal_tiles, 5),
         "tiles": {"contiguous": dense_t, "gathered": gath_t, "rows": rows_t, "keys": keys_t},
+        # K and V rows of the gathered vertical tiles, bf16, over the attention time
+        "gather_gbs": round(float(gath_t) * keys_t * 2 * d * 2 / (attn_avg * 1e-3) / 1e9, 3),
         "flops_alg": f_alg,
         "flops_tile": f_tile,
         "roofline": {"bound": "mfma", "kernel": "attn_kernel (vs_sparse_attn_prefill)",

@@ -151,6 +151,28 @@ def test_zipf128k_layer_sampled():
     assert_attn_close(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, "zipf128k")
 
 
+def test_clustered128k_layer_sampled():
+    """The 128K layer with clustered scores (selected columns and offsets in
+    contiguous runs): both selections bit-exact, attention rows sampled."""
+    _log("case: clustered128k layer")
+    w = workloads.WORKLOADS["clustered128k"]
+    q, k, v = workloads.attention_inputs("clustered128k")
+    vlog, slog = workloads.clustered_scores("clustered128k")
+    vi, vc = vsa.vs_select(to_dev(vlog), vsa.VS_VERTICAL, w["mass"], w["cap_v"])
+    si, sc = vsa.vs_select(to_dev(slog), vsa.VS_SLASH, w["mass"], w["cap_s"])
+    out, lse = vsa.vs_sparse_attn_prefill(to_dev(q), to_dev(k), to_dev(v), vi, vc, si, sc)
+    torch.cuda.synchronize()
+    for kind, lg, gi, gc, cap in ((oracle.VERTICAL, vlog, vi, vc, w["cap_v"]),
+                                  (oracle.SLASH, slog, si, sc, w["cap_s"])):
+        ri, rc = oracle.select(lg, kind, w["mass"], cap)
+        _assert_same_selection(gi.cpu().numpy(), gc.cpu().numpy(), ri, rc, f"clustered kind {kind}")
+    lists = (vi.cpu().numpy(), vc.cpu().numpy(), si.cpu().numpy(), sc.cpu().numpy())
+    out, lse = to_f64(out), lse.cpu().numpy().astype(np.float64)
+    rows = sample_rows(np.random.default_rng(12), 32, w["n"], 12)
+    ro, rl = oracle.attn(q, k, v, *lists, rows=rows)
+    assert_attn_close(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, "clustered128k")
+
+
 THRESH_CASES = [
     # name, heads, n, alpha, cap
     ("normal", 8, 131072, 0.01, 131072),

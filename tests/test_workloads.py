@@ -44,3 +44,31 @@ def test_bf16_single_rounding_with_halfway_cases():
 def test_bf16_from_fp32_unchanged():
     z = np.random.default_rng(1).standard_normal(2000).astype(np.float32)
     assert np.array_equal(workloads.to_bf16_bits(z), _bf16_exact(z.astype(np.float64)))
+
+
+def test_banded_zipf_logits_are_a_permuted_zipf_with_runs():
+    """The clustered recipe keeps the Zipf pmf (its ranks are a permutation of
+    1..n) and puts the best ranks next to its centres: the top 400 indices of
+    each head form at most `centers` contiguous runs (one per centre, the one
+    at 0 cut in half)."""
+    rng = np.random.default_rng(11)
+    n, s, centers = 5000, 1.1, 4
+    lg = workloads.banded_zipf_logits(rng, 3, n, s, centers)
+    for h in range(3):
+        ranks = np.rint(np.exp(-lg[h].astype(np.float64) / s)).astype(np.int64)
+        assert np.array_equal(np.sort(ranks), np.arange(1, n + 1))
+        top = np.sort(np.argsort(ranks)[:400])
+        assert top[0] == 0
+        assert (np.diff(top) > 1).sum() + 1 <= centers
+
+
+def test_clustered_scores_slash_vector_is_position_indexed():
+    """Offset o's slash score sits at position n-1-o.  The centres (distance
+    0) hold the best ranks, and offset 0 is a centre, so position n-1 is among
+    the top s_centers slash logits; column 0 is among the top v_centers."""
+    w = workloads.WORKLOADS["clustered128k"]
+    v, sl = workloads.clustered_scores("clustered128k", n=4096)
+    assert v.shape == sl.shape == (8, 4096)
+    for h in range(8):
+        assert 0 in np.argsort(-v[h])[:w["v_centers"]]
+        assert 4095 in np.argsort(-sl[h])[:w["s_centers"]]

@@ -18,6 +18,11 @@ head dim 128, one of the backbones the VSPrefill pages evaluate on):
 * ``fixed32k`` 32/8 heads, n=32768, bf16, RoPE, fixed 1000 verticals / 2000 slashes
 * ``zipf128k`` 32/8 heads, n=131072, bf16, RoPE, Zipf(1.1) score vectors,
   selection at mass 0.95 capped at 4096 verticals / 8192 slashes
+* ``clustered128k`` the zipf128k layer with the Zipf ranks ordered by distance
+  to a few centres (position / offset 0 plus uniform draws) instead of
+  randomly, so the selected columns and offsets come out as contiguous runs,
+  the shape the pages' real heads show; a supplementary workload, not one of
+  the pages' configurations
 * ``indexer128k`` 8 KV heads, n=131072, [RoPE(K) | V] 256-wide bf16 rows and
   random indexer weights W1 ~ N(0, 1/256), W2 ~ N(0, 1/128)
 * ``e2e256k`` 32/8 heads, n=262144, bf16, RoPE, keys of the first 4 positions
@@ -42,6 +47,9 @@ WORKLOADS = {
                      rope=True, nv_fixed=4, nv_rand=996, ns_fixed=64, ns_rand=1936),
     "zipf128k": dict(seed=1003, hq=32, hkv=8, n=131072, d=128, dtype="bf16",
                      rope=True, zipf_s=1.1, mass=0.95, cap_v=4096, cap_s=8192),
+    "clustered128k": dict(seed=1007, hq=32, hkv=8, n=131072, d=128, dtype="bf16",
+                          rope=True, zipf_s=1.1, mass=0.95, cap_v=4096, cap_s=8192,
+                          v_centers=8, s_centers=4),
     "indexer128k": dict(seed=1004, hkv=8, n=131072, d=128, hidden=128, dtype="bf16",
                         rope=True, mass=0.95),
     "e2e256k": dict(seed=1005, hq=32, hkv=8, n=262144, d=128, hidden=128, dtype="bf16",
@@ -188,6 +196,35 @@ def zipf_scores(name: str = "zipf128k", n: int | None = None, seed: int | None =
     vlog = zipf_logits(rs["score"], w["hkv"], n, w["zipf_s"])
     slog = zipf_logits(rs["score"], w["hkv"], n, w["zipf_s"])
     return vlog, slog
+
+
+def banded_zipf_logits(rng, heads: int, n: int, s: float, centers: int) -> np.ndarray:
+    """Per head, Zipf(s) logits -s*ln(rank) whose ranks grow with the distance
+    of the index to the nearest of ``centers`` centres (index 0 plus uniform
+    draws), equal distances in random order; fp32 [heads, n]."""
+    out = np.empty((heads, n), dtype=np.float32)
+    idx = np.arange(n, dtype=np.int64)
+    for h in range(heads):
+        c = np.concatenate([[0], rng.choice(np.arange(1, n), size=centers - 1, replace=False)])
+        dist = np.abs(idx[:, None] - c[None, :]).min(axis=1)
+        order = np.lexsort((rng.random(n), dist))
+        ranks = np.empty(n, dtype=np.float64)
+        ranks[order] = np.arange(1, n + 1, dtype=np.float64)
+        out[h] = (-s * np.log(ranks)).astype(np.float32)
+    return out
+
+
+def clustered_scores(name: str = "clustered128k", n: int | None = None, seed: int | None = None):
+    """Vertical and slash score vectors [hkv, n] fp32 of the clustered workload.
+    The slash vector is position-indexed like the indexer's output (offset o
+    scores at position n-1-o), so the banded ranks are drawn over offsets and
+    reversed."""
+    w = WORKLOADS[name]
+    n = n or w["n"]
+    rs = streams(w["seed"] if seed is None else seed)
+    vlog = banded_zipf_logits(rs["score"], w["hkv"], n, w["zipf_s"], w["v_centers"])
+    by_offset = banded_zipf_logits(rs["score"], w["hkv"], n, w["zipf_s"], w["s_centers"])
+    return vlog, np.ascontiguousarray(by_offset[:, ::-1])
 
 
 def indexer_weights(rng, d_in: int, hidden: int):
