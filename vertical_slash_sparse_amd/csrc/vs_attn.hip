@@ -441,13 +441,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     kh1 = k1 >> (4 * half);
   };
   // gathered chunk: its 64 keys ascend (padding n sorts last), so the visible
-  // ones are a prefix
+  // ones are a prefix; a chunk that ends at or before the wave's first row is
+  // visible whole, which skips the search for all but the chunks at the
+  // diagonal
   auto key_word_chunk = [&](const int* keys, uint32_t& kh0, uint32_t& kh1) {
-    int lo = 0;
+    int cnt = kBN;
+    if (keys[kBN - 1] > i0w) {
+      int lo = 0;
 #pragma unroll
-    for (int step = 32; step > 0; step >>= 1)
-      if (keys[lo + step - 1] <= qrow) lo += step;
-    const int cnt = lo + (lo == 63 && keys[63] <= qrow ? 1 : 0);
+      for (int step = 32; step > 0; step >>= 1)
+        if (keys[lo + step - 1] <= qrow) lo += step;
+      cnt = lo + (lo == 63 && keys[63] <= qrow ? 1 : 0);
+    }
     const uint32_t k0 = cnt >= 32 ? ~0u : ((1u << cnt) - 1u);
     const uint32_t k1 = cnt >= 64 ? ~0u : (cnt <= 32 ? 0u : ((1u << (cnt - 32)) - 1u));
     kh0 = __builtin_amdgcn_alignbit(k1, k0, 4 * half);
