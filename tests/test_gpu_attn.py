@@ -212,3 +212,31 @@ def test_fixed32k_full_size_sampled():
     rows = sample_rows(np.random.default_rng(3), 32, 32768, 24)
     ro, rl = oracle.attn(q, k, v, *lists, rows=rows)
     assert_attn_close(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, "fixed32k")
+
+
+SOLID_CASES = [
+    # hq, hkv, n, d, dtype, n_runs, run_len, local
+    (8, 2, 3000 + 17, 128, "bf16", 3, 300, 500),
+    (4, 4, 2048, 64, "bf16", 2, 700, 130),
+    (16, 1, 1500, 128, "f32", 1, 1000, 0),
+    (8, 8, 4096 + 63, 128, "bf16", 5, 200, 2000),
+]
+
+
+@pytest.mark.parametrize("case", SOLID_CASES, ids=[f"h{c[0]}x{c[1]}-n{c[2]}-d{c[3]}-{c[4]}" for c in SOLID_CASES])
+def test_solid_offset_runs_and_visible_columns(case):
+    """Gap-free offset runs longer than a tile's 127-offset window make tiles
+    whose every pair is selected (they run unmasked), and columns far below
+    the diagonal make gathered chunks visible whole (unmasked too); the rest
+    of the tiles, at the run edges and the diagonal, stay masked.  Every row
+    against the oracle."""
+    hq, hkv, n, d, dtype, n_runs, run_len, local = case
+    _log(f"case: solid runs {case}")
+    rng = np.random.default_rng(n + 31 * run_len)
+    q, k, v = _inputs(rng, hq, hkv, n, d, dtype)
+    _, _, soff, scnt = workloads.clustered_offsets(rng, hkv, n, n_runs=n_runs, run_len=run_len, local=local)
+    cols = [np.union1d(np.arange(4), rng.choice(np.arange(4, n), 200, replace=False)) for _ in range(hkv)]
+    vidx, vcnt = _pad_lists(cols)
+    out, lse = _run_gpu(q, k, v, vidx, vcnt, soff, scnt)
+    ro, rl = oracle.attn(q, k, v, vidx, vcnt, soff, scnt)
+    assert_attn_close(out, lse, ro, rl, str(case))

@@ -183,6 +183,7 @@ __global__ __launch_bounds__(1024) void ws_cluster_kernel(const int32_t* __restr
 // ---------------------------------------------------------------- attention
 
 constexpr int kWaves = 8;               // waves per workgroup (two per SIMD)
+constexpr int kMasked = 0, kTested = 1, kNoMask = 2;  // softmax masking modes (see softmax)
 constexpr int kThreads = kWaves * 64;
 
 struct AttnParams {
@@ -287,6 +288,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   __shared__ __align__(16) uint8_t kv_lds[2 * NST * TILEB];
   __shared__ __align__(16) int glist[kListCap];
   __shared__ int wcnt[kWaves + 1];
+  // per cluster of one batch while a window of the tile list is written: its
+  // first slot in the window, and its tiles as ranges [a, a + b) then c ..
+  __shared__ int cl_pos[kThreads], cl_a[kThreads], cl_b[kThreads], cl_c[kThreads];
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   lds_u8* const kv_base = (lds_u8*)kv_lds;
 
@@ -546,14 +550,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   };
   // online softmax of S = (c0, c1) under the key words: updates the running
   // max and sum, rescales O when the max has grown past the lazy threshold,
-  // and leaves the probabilities in pk
-  auto softmax = [&](uint32_t kc0, uint32_t kc1) {
+  // and leaves the probabilities in pk.  Masks by mode:
+  //   kMasked  every tile is masked, masking interleaved with the maxima;
+  //   kTested  a tile whose key words cover all its keys in every lane (the
+  //            element bits 0x0F0F0F0F of both words) skips the masks;
+  //   kNoMask  the caller knows every key of the tile is selected for every
+  //            row, so the key words are not even formed.
+  auto softmax = [&](uint32_t kc0, uint32_t kc1, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
     float pm[4];
-    // a full tile (the element bits 0x0F0F0F0F of both key words set in every
-    // lane) skips the masks; FULL = false keeps masking and maxima interleaved
     bool full = false;
-    if constexpr (FULL) full = __builtin_amdgcn_ballot_w64((kc0 & kc1 & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) == 0;
-    if constexpr (FULL) {
+    if constexpr (MODE == kTested) full = __builtin_amdgcn_ballot_w64((kc0 & kc1 & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) == 0;
+    if constexpr (MODE == kTested) {
       if (!full) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -567,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      if constexpr (!FULL) {
+      if constexpr (MODE == kMasked) {
 #pragma unroll
         for (int e = 4 * q4; e < 4 * q4 + 4; ++e) {
           const int bpos = 8 * (e >> 2) + (e & 3);
@@ -638,11 +646,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   // key_word_first() gives the key word of tile 0; within V(t), begin()
   // starts the fetches step t needs, key_word() gives the key word of tile
   // t+1, stage_k()/stage_v() load K(t+3) / V(t+2), and rotate() moves on.
-  // Tiles past the end read as zeros and have empty key words.
-  auto pipeline = [&](auto& src, int T) {
+  // Tiles past the end read as zeros and have empty key words.  `mode_c`
+  // picks the softmax masking (kNoMask skips the key words altogether).
+  auto pipeline = [&](auto& src, int T, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
     src.stage_first();
-    uint32_t kc0, kc1;
-    src.key_word_first(kc0, kc1);
+    uint32_t kc0 = ~0u, kc1 = ~0u;
+    if constexpr (MODE != kNoMask) src.key_word_first(kc0, kc1);
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
     qk0();
@@ -654,8 +664,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       // so the SIMD's other wave (in its matrix half) takes the slots it leaves
       __builtin_amdgcn_s_setprio(3);
       src.begin();
-      softmax(kc0, kc1);
-      src.key_word(kc0, kc1);
+      softmax(kc0, kc1, mode_c);
+      if constexpr (MODE != kNoMask) src.key_word(kc0, kc1);
       src.stage_k(KREG + ((S + 3) % NST) * TILEB);
       src.stage_v(VREG + ((S + 2) % NST) * TILEB);
       hold_dma_offsets();
@@ -682,6 +692,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
   };
+
+  // tiles not known to be full: masked, or tested for fullness first where
+  // nearly all of them are full
+  const std::integral_constant<int, FULL ? kTested : kMasked> rest_mode{};
+  const std::integral_constant<int, kNoMask> full_mode{};
 
   if constexpr (BLK) {
     // ---- block mode: whole 64-key tiles.  The workgroup's rows fall in
@@ -776,7 +791,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       if (base <= wst) break;
       const int T = min(base - wst, kListCap);
       BlockSrc src{stage_tile, key_word_block, glist, T, tend, 0, 0, 0, 0, 0};
-      pipeline(src, T);
+      pipeline(src, T, rest_mode);
       n_dense += T;
       if (wst + kListCap >= base) break;
     }
@@ -813,17 +828,41 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       for (int t = tlo; t <= thi; ++t) k += tile_active(t) ? 1 : 0;
       return k;
     };
-    int T_total = 0;
-    for (int j0 = 0; j0 < ncb; j0 += kThreads) {
-      int cnt = 0;
-      if (j0 + tid < ncb) {
-        int tlo, thi;
-        cluster_tiles(j0 + tid, tlo, thi);
-        cnt = active_count(tlo, thi);
+    // When the j-th cluster has no gap (every offset from its smallest lo to
+    // its largest hi is selected), its tiles [f0, f1] hold only selected
+    // pairs for every row of the block: tile T needs the offsets
+    // i0 - 64T - 63 .. i1 - 64T, which lie in [lo, hi] exactly for those T
+    // (and are then all non-negative, so the tile is causal too).  They run
+    // first, unmasked; otherwise f0 = thi + 1, f1 = thi.
+    auto floor_div = [](int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); };
+    auto cluster_full = [&](int j, int tlo, int thi, int& f0, int& f1) {
+      const int c = ncb - 1 - j;
+      const int lo = p.clLo[(size_t)g * p.cap_s + c], hi = p.clHi[(size_t)g * p.cap_s + c];
+      f0 = thi + 1;
+      f1 = thi;
+      if (prefix(hi + 1) - prefix(lo) != hi - lo + 1) return;
+      const int a = max(tlo, floor_div(i1 - hi + kBN - 1, kBN));
+      const int b = min(thi, floor_div(i0 - (kBN - 1) - lo, kBN));
+      if (a <= b) {
+        f0 = a;
+        f1 = b;
       }
-      int tot;
+    };
+    int T_total = 0, T_full = 0;
+    for (int j0 = 0; j0 < ncb; j0 += kThreads) {
+      int cnt = 0, cntf = 0;
+      if (j0 + tid < ncb) {
+        int tlo, thi, f0, f1;
+        cluster_tiles(j0 + tid, tlo, thi);
+        cluster_full(j0 + tid, tlo, thi, f0, f1);
+        cntf = f1 - f0 + 1;
+        cnt = active_count(tlo, thi) - cntf;
+      }
+      int tot, totf;
       block_excl_scan<kThreads>(cnt, &tot, wcnt);
+      block_excl_scan<kThreads>(cntf, &totf, wcnt);
       T_total += tot;
+      T_full += totf;
     }
     // Tile codes for steps t+1, t+2, t+3 live in scalar registers; the code
     // of t+4 is read from the LDS list one step ahead (unconditionally, from a
@@ -870,27 +909,73 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         ++t;
       }
     };
-    for (int wst = 0; wst < T_total; wst += kListCap) {
+    // Writes window [wst, wst + kListCap) of one pass's tile list into glist:
+    // the clusters' full ranges [f0, f1] (full = true), or the rest of their
+    // tiles.  In a full block a cluster's tiles form one or two ranges, so
+    // after a scan of the counts every slot finds its cluster by a binary
+    // search over the clusters' first slots and all slots are written in
+    // parallel; in the short last block (one per head) each thread lists its
+    // clusters' tiles itself, testing each for an active offset.
+    auto list_window = [&](bool full, int wst) {
       int base = 0;
       for (int j0 = 0; j0 < ncb; j0 += kThreads) {
-        int cnt = 0, tlo = 0, thi = -1;
-        if (j0 + tid < ncb) {
+        const int nb = min(kThreads, ncb - j0);
+        int cnt = 0, tlo = 0, thi = -1, f0 = 0, f1 = -1;
+        if (tid < nb) {
           cluster_tiles(j0 + tid, tlo, thi);
-          cnt = active_count(tlo, thi);
+          cluster_full(j0 + tid, tlo, thi, f0, f1);
+          cnt = full ? f1 - f0 + 1 : active_count(tlo, thi) - (f1 - f0 + 1);
         }
         int tot;
         int pos = base + block_excl_scan<kThreads>(cnt, &tot, wcnt) - wst;
-        for (int t = tlo; t <= thi && pos < kListCap; ++t) {
-          if (partial && !tile_active(t)) continue;
-          if (pos >= 0) glist[pos] = t;
-          ++pos;
+        if (partial) {
+          const int a = full ? f0 : tlo, b = full ? f1 : thi;
+          for (int t = a; t <= b && pos < kListCap; ++t) {
+            if (!full && t == f0) t = f1 + 1;
+            if (t > b) break;
+            if (!full && !tile_active(t)) continue;
+            if (pos >= 0) glist[pos] = t;
+            ++pos;
+          }
+        } else {
+          if (tid < nb) {
+            cl_pos[tid] = pos;
+            cl_a[tid] = full ? f0 : tlo;
+            cl_b[tid] = full ? cnt : f0 - tlo;
+            cl_c[tid] = f1 + 1;
+          }
+          __syncthreads();
+          const int s1 = min(kListCap, base + tot - wst);
+          for (int sl = max(0, base - wst) + tid; sl < s1; sl += kThreads) {
+            int lo = 0, hi = nb - 1;  // the last cluster whose first slot is at or before sl
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (cl_pos[mid] <= sl) lo = mid;
+              else hi = mid - 1;
+            }
+            const int r = sl - cl_pos[lo];
+            glist[sl] = r < cl_b[lo] ? cl_a[lo] + r : cl_c[lo] + (r - cl_b[lo]);
+          }
+          __syncthreads();
         }
         base += tot;
       }
       __syncthreads();
+    };
+    // the full tiles, unmasked
+    for (int wst = 0; wst < T_full; wst += kListCap) {
+      list_window(true, wst);
+      const int T = min(T_full - wst, kListCap);
+      TileSrc src{stage_tile, load_words, key_word_tile, glist, T, tend, 0, 0, 0, 0, 0, {}};
+      pipeline(src, T, full_mode);
+      n_dense += T;
+    }
+    // the rest, masked
+    for (int wst = 0; wst < T_total; wst += kListCap) {
+      list_window(false, wst);
       const int T = min(T_total - wst, kListCap);
       TileSrc src{stage_tile, load_words, key_word_tile, glist, T, tend, 0, 0, 0, 0, 0, {}};
-      pipeline(src, T);
+      pipeline(src, T, rest_mode);
       n_dense += T;
     }
 
@@ -907,10 +992,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       }
       total_v = lo;
     }
-    auto stage_chunk = [&](int which, int t, int nch, int dst) {
+    auto stage_chunk = [&](const int* list, int which, int t, int nch, int dst) {
       int key[NDMA];
   #pragma unroll
-      for (int i = 0; i < NDMA; ++i) key[i] = t < nch ? glist[t * kBN + dma_row[i]] : n;
+      for (int i = 0; i < NDMA; ++i) key[i] = t < nch ? list[t * kBN + dma_row[i]] : n;
       stage_keys(which, key, dst);
     };
     struct ChunkSrc {
@@ -928,17 +1013,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       }
       __device__ void stage_first() {
         t = 0;
-        stage_fn(0, 0, T, KREG);
-        stage_fn(0, 1, T, KREG + TILEB);
-        stage_fn(0, 2, T, KREG + 2 * TILEB);
-        stage_fn(1, 0, T, VREG);
-        stage_fn(1, 1, T, VREG + TILEB);
+        stage_fn(list, 0, 0, T, KREG);
+        stage_fn(list, 0, 1, T, KREG + TILEB);
+        stage_fn(list, 0, 2, T, KREG + 2 * TILEB);
+        stage_fn(list, 1, 0, T, VREG);
+        stage_fn(list, 1, 1, T, VREG + TILEB);
       }
       __device__ void key_word_first(uint32_t& k0, uint32_t& k1) { kw(0, k0, k1); }
       __device__ void begin() {}
       __device__ void key_word(uint32_t& k0, uint32_t& k1) { kw(t + 1, k0, k1); }
-      __device__ void stage_k(int dst) { stage_fn(0, t + 3, T, dst); }
-      __device__ void stage_v(int dst) { stage_fn(1, t + 2, T, dst); }
+      __device__ void stage_k(int dst) { stage_fn(list, 0, t + 3, T, dst); }
+      __device__ void stage_v(int dst) { stage_fn(list, 1, t + 2, T, dst); }
       __device__ void rotate() { ++t; }
     };
     int cursor = 0;
@@ -974,8 +1059,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       for (int r = fill + tid; r < ((fill + kBN - 1) / kBN) * kBN; r += kThreads) glist[r] = n;
       __syncthreads();
       const int nch = (fill + kBN - 1) / kBN;
-      ChunkSrc src{stage_chunk, key_word_chunk, glist, nch, 0};
-      pipeline(src, nch);
+      // chunks whose last column is at or before the block's first row are
+      // visible whole to every row; the columns ascend, so they come first
+      int nfull = 0;
+      for (int step = 32; step > 0; step >>= 1)
+        if (nfull + step <= nch && glist[(nfull + step) * kBN - 1] <= i0) nfull += step;
+      if (nfull > 0) {
+        ChunkSrc src{stage_chunk, key_word_chunk, glist, nfull, 0};
+        pipeline(src, nfull, full_mode);
+      }
+      if (nch > nfull) {
+        ChunkSrc src{stage_chunk, key_word_chunk, glist + nfull * kBN, nch - nfull, 0};
+        pipeline(src, nch - nfull, rest_mode);
+      }
       n_gath += nch;
     }
 
