@@ -63,3 +63,43 @@ def test_e2e256k_stage_by_stage():
     g_lse = lse[hs, ps].cpu().numpy().astype(np.float64)
     ro, rl = oracle.attn(q, k, v, *lists, rows=rows)
     assert_attn_close(g_out, g_lse, ro, rl, "e2e256k")
+
+
+PREFILL_CASES = [
+    # hq, hkv, n, mass, cap_v, cap_s
+    (8, 2, 1500, 0.95, None, None),
+    (16, 4, 3000 + 5, 0.6, 300, 200),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[f"h{c[0]}x{c[1]}-n{c[2]}-m{c[3]}" for c in PREFILL_CASES])
+def test_vs_prefill_pipeline(case):
+    """vs_prefill (index -> select x2 -> attention in one call), every stage
+    against the oracle on the GPU's own inputs to that stage, and every row of
+    the output against the oracle on the GPU's index sets."""
+    hq, hkv, n, mass, cap_v, cap_s = case
+    _log(f"case: vs_prefill {case}")
+    rng = np.random.default_rng(n)
+    d = 128
+    tables = workloads.rope_tables(n, d)
+    q = workloads.gaussian_heads(rng, hq, n, d, "bf16", tables)
+    k = workloads.gaussian_heads(rng, hkv, n, d, "bf16", tables)
+    v = workloads.gaussian_heads(rng, hkv, n, d, "bf16", None)
+    w1, w2 = workloads.indexer_weights(rng, 2 * d, 128)
+    out, lse, (vi, vc, si, sc) = vsa.vs_prefill(to_dev(q), to_dev(k), to_dev(v), to_dev(w1), to_dev(w2),
+                                                mass, cap_v, cap_s)
+    gv, gs = vsa.vs_index(to_dev(k), to_dev(v), to_dev(w1), to_dev(w2))
+    torch.cuda.synchronize()
+    gv_np, gs_np = gv.cpu().numpy(), gs.cpu().numpy()
+    rv, rs = oracle.index(k, v, w1, w2)
+    assert np.abs(gv_np - rv).max() <= INDEX_ATOL
+    assert np.abs(gs_np - rs).max() <= INDEX_ATOL
+    lists = []
+    for kind, lg, gi, gc, cap in ((oracle.VERTICAL, gv_np, vi, vc, cap_v or n), (oracle.SLASH, gs_np, si, sc, cap_s or n)):
+        ri, rc = oracle.select(lg, kind, mass, cap)
+        np.testing.assert_array_equal(gc.cpu().numpy(), rc, err_msg=f"kind {kind}: counts")
+        np.testing.assert_array_equal(gi.cpu().numpy(), ri, err_msg=f"kind {kind}: indices")
+        lists += [ri, rc]
+    ro, rl = oracle.attn(q, k, v, *lists)
+    from tests.util import to_f64
+    assert_attn_close(to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl, f"vs_prefill {case}")

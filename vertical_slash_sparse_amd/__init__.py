@@ -17,6 +17,8 @@ calls raise.
     vs_sparse_attn_prefill_qh(...)                 per-query-head lists [h_q, cap]
     vs_sparse_attn_prefill_varlen(q, k, v, cu_seqlens, v_idx, v_cnt, s_off, s_cnt)
                                                    packed batch of sequences
+    vs_prefill(q, k, v, w1, w2, mass)              -> (out, lse, (v_idx, v_cnt, s_off, s_cnt))
+                                                   index -> select x2 -> attention
 """
 from __future__ import annotations
 
@@ -505,3 +507,30 @@ def vs_block_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mas
 
 def exported_symbols():
     return _SYMBOLS
+
+
+def vs_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
+               mass: float = 0.95, cap_v: int | None = None, cap_s: int | None = None,
+               scale: float | None = None, stream=None):
+    """One vertical-slash sparse prefill layer the way VSPrefill's inference
+    pipeline runs it (VSPrefill, English page, section 3 "Adaptive Inference
+    Pipeline"): the indexer scores every position from [K_rope | V]
+    (vs_index), the cumulative-mass budget picks each KV head's columns and
+    slash offsets (vs_select, twice), and sparse attention runs over their
+    union (vs_sparse_attn_prefill).  q bf16 [h_q, n, d]; k (already rotated)
+    and v bf16 [h_kv, n, d]; w1 bf16 [hidden, 2d]; w2 bf16 [2, hidden].
+    cap_v / cap_s bound the budgets (default n, i.e. uncapped).  Every launch
+    goes on one stream; nothing is synchronised.  Returns (out, lse,
+    (v_idx, v_cnt, s_off, s_cnt))."""
+    h_kv, n, _ = k.shape
+    cap_v = n if cap_v is None else int(cap_v)
+    cap_s = n if cap_s is None else int(cap_s)
+    vlog, slog = vs_index(k, v, w1, w2, stream=stream)
+    ws = torch.empty(max(vs_select_workspace_bytes(h_kv, n), 1), dtype=torch.uint8, device=k.device)
+    v_idx, v_cnt = vs_select(vlog, VS_VERTICAL, mass, cap_v, workspace=ws, stream=stream)
+    s_off, s_cnt = vs_select(slog, VS_SLASH, mass, cap_s, workspace=ws, stream=stream)
+    out, lse = vs_sparse_attn_prefill(q, k, v, v_idx, v_cnt, s_off, s_cnt, scale=scale, stream=stream)
+    if stream is not None:  # the temporaries are freed on return, while `stream` may still use them
+        for t in (vlog, slog, ws):
+            t.record_stream(stream)
+    return out, lse, (v_idx, v_cnt, s_off, s_cnt)
