@@ -19,11 +19,14 @@
 //    32-row sub-blocks), so every K/V tile staged in LDS feeds all G heads.
 //    The sorted cluster list is walked from the largest offset down, which
 //    yields the key-tile ranges of the block in ascending key order (a merge
-//    of the per-cluster ranges, no n x n structure).  Each contiguous tile is
-//    masked per element by (j <= i) and (offset bit or column bit); the lane
-//    masks come from wave-uniform bitmap windows, so a masked element costs
-//    one v_cndmask.  Columns that no processed tile covers are then gathered
-//    64 at a time into tiles of their own.
+//    of the per-cluster ranges, no n x n structure).  Tiles inside a
+//    gap-free cluster hold only selected pairs for every row of the block
+//    and run first without masks; every other tile is masked per element by
+//    (j <= i) and (offset bit or column bit), from a 64-bit key word per lane
+//    built out of wave-uniform bitmap windows (a bit extract and a bitwise
+//    select per element).  Columns that no processed tile covers are then
+//    gathered 64 at a time into tiles of their own (unmasked when they all
+//    lie below the block).
 //  * Math per 64-key tile and 32 query rows: S^T = K Q^T on
 //    v_mfma_f32_32x32x16_bf16 (K from LDS, Q^T held in registers), online
 //    softmax in fp32 on the transposed scores (each lane owns one query row,
