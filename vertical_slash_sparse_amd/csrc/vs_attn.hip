@@ -32,8 +32,11 @@
 //    softmax in fp32 on the transposed scores (each lane owns one query row,
 //    so row statistics need one cross-half exchange), P^T reused directly as
 //    the B operand of O^T += V^T P^T with V^T staged in LDS in a matching
-//    key order.  The running maximum is only moved when it grows by more
-//    than 2^8 (the result is unchanged; p stays below 2^8 in fp32/bf16).
+//    key order.  Probabilities are taken against the running maximum, which
+//    only moves when some p of a tile could exceed 2^8 (the result is
+//    unchanged; p stays at most 2^8 in fp32/bf16); a lane's sum of its p,
+//    needed anyway, bounds each of them, so the tile's own maximum is
+//    computed only when that sum is over 2^8.
 #include <algorithm>
 #include <climits>
 
@@ -47,6 +50,7 @@ namespace vs {
 namespace {
 
 constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
+constexpr float kPMax = 256.0f;         // 2^kTau: the largest p the running maximum allows
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNoMax = -1.0e30f;      // running max before any key was seen
@@ -551,64 +555,26 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       c1 = mfma32(a1, qf[kk], c1);
     }
   };
-  // online softmax of S = (c0, c1) under the key words: updates the running
-  // max and sum, rescales O when the max has grown past the lazy threshold,
-  // and leaves the probabilities in pk.  Masks by mode:
-  //   kMasked  every tile is masked, masking interleaved with the maxima;
+  // online softmax of S = (c0, c1) under the key words, in two parts so
+  // that other work of the vector half can sit between them.  probs() masks
+  // S by mode:
+  //   kMasked  every tile is masked;
   //   kTested  a tile whose key words cover all its keys in every lane (the
   //            element bits 0x0F0F0F0F of both words) skips the masks;
   //   kNoMask  the caller knows every key of the tile is selected for every
-  //            row, so the key words are not even formed.
-  auto softmax = [&](uint32_t kc0, uint32_t kc1, auto mode_c) {
-    constexpr int MODE = decltype(mode_c)::value;
-    float pm[4];
-    bool full = false;
-    if constexpr (MODE == kTested) full = __builtin_amdgcn_ballot_w64((kc0 & kc1 & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) == 0;
-    if constexpr (MODE == kTested) {
-      if (!full) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int bpos = 8 * (e >> 2) + (e & 3);
-          const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, bpos, 1);
-          const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, bpos, 1);
-          c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
-          c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
-        }
-      }
-    }
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      if constexpr (MODE == kMasked) {
-#pragma unroll
-        for (int e = 4 * q4; e < 4 * q4 + 4; ++e) {
-          const int bpos = 8 * (e >> 2) + (e & 3);
-          const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, bpos, 1);
-          const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, bpos, 1);
-          c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
-          c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
-        }
-      }
-      const int e = 4 * q4;
-      pm[q4] = __builtin_elementwise_maximum(
-          __builtin_elementwise_maximum(__builtin_elementwise_maximum(c0[e], c0[e + 1]),
-                                        __builtin_elementwise_maximum(c0[e + 2], c0[e + 3])),
-          __builtin_elementwise_maximum(__builtin_elementwise_maximum(c1[e], c1[e + 1]),
-                                        __builtin_elementwise_maximum(c1[e + 2], c1[e + 3])));
-    }
-    float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(pm[0], pm[1]),
-                                             __builtin_elementwise_maximum(pm[2], pm[3]));
-    mx = half_max(mx);
-    const float mt = mx * p.c;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau)) {
-      const float mnew = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
-      m_run = mnew;
-    }
+  //            row, so the key words are not even formed;
+  // then forms the probabilities against the running maximum as bf16 pairs
+  // in pk (the P^T operand) and returns the sum of the lane's share of them.
+  // commit() makes sure none of them exceeded 2^kTau -- the lane's sum of
+  // non-negative p bounds each, so the tile's own maximum is needed only
+  // when a sum exceeds that (always on a row's first tile, where the running
+  // maximum is still kNoMax, and rarely afterwards); then it moves the
+  // running maximum, rescales O and the row sum, and forms the tile again.
+  // Finally it adds the tile's sum to the row's.  Deciding on the sum, after
+  // the next tile's key word and loads are issued, keeps both the maxima and
+  // the wait for the sums off the critical path.
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto form_probs = [&]() -> float {
     const float nm = -m_run;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -617,12 +583,51 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       pk[8 + e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c1[2 * e], p.c, nm)),
                             __builtin_amdgcn_exp2f(fmaf(c1[2 * e + 1], p.c, nm)));
     }
-    // row sum of the bf16 probabilities the PV product uses
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float ts[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 16; ++e)
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, l_run, false);
+      ts[e & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]), ones, ts[e & 3], false);
+    return (ts[0] + ts[1]) + (ts[2] + ts[3]);
   };
+  auto probs = [&](uint32_t kc0, uint32_t kc1, auto mode_c) -> float {
+    constexpr int MODE = decltype(mode_c)::value;
+    auto mask = [&]() {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int bpos = 8 * (e >> 2) + (e & 3);
+        const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, bpos, 1);
+        const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, bpos, 1);
+        c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
+        c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
+      }
+    };
+    if constexpr (MODE == kTested) {
+      if (__builtin_amdgcn_ballot_w64((kc0 & kc1 & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) != 0) mask();
+    }
+    if constexpr (MODE == kMasked) mask();
+    return form_probs();
+  };
+  auto commit = [&](float t) {
+    if (__builtin_amdgcn_ballot_w64(!(t <= kPMax))) {
+      float mx = c0[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = __builtin_elementwise_maximum(mx, c0[e]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = __builtin_elementwise_maximum(mx, c1[e]);
+      mx = half_max(mx);
+      const float mnew = fmaxf(m_run, mx * p.c);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+      m_run = mnew;
+      t = form_probs();
+    }
+    l_run += t;
+  };
+
   auto hold_dma_offsets = [&]() {
     if constexpr (!F32) {
 #pragma unroll
@@ -667,10 +672,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       // so the SIMD's other wave (in its matrix half) takes the slots it leaves
       __builtin_amdgcn_s_setprio(3);
       src.begin();
-      softmax(kc0, kc1, mode_c);
+      const float tsum = probs(kc0, kc1, mode_c);
       if constexpr (MODE != kNoMask) src.key_word(kc0, kc1);
       src.stage_k(KREG + ((S + 3) % NST) * TILEB);
       src.stage_v(VREG + ((S + 2) % NST) * TILEB);
+      commit(tsum);
       hold_dma_offsets();
       src.rotate();
       // P(t) is finished here, in the vector half, not under the products
