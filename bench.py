@@ -3,7 +3,7 @@
 Default workload ``zipf128k``: 32 query / 8 KV heads, d=128, n=131072, bf16
 Q/K/V with RoPE, Zipf(1.1) vertical and slash score vectors, budgets chosen by
 cumulative softmax mass 0.95 capped at 4096 columns / 8192 offsets per KV
-head.  One step = vs_select (columns) + vs_select (offsets) +
+head.  One step = vs_select_both (columns and offsets in one launch chain) +
 vs_sparse_attn_prefill (tile build + attention) on inputs already resident in
 HBM.  Other workloads (``fixed32k``, ``indexer128k``, ``e2e256k``,
 ``clustered128k``, ...) can be timed with ``--workload``; ``e2e256k`` adds
@@ -213,7 +213,7 @@ def main():
     vc = torch.empty((hkv,), dtype=torch.int32, device="cuda")
     si = torch.empty((hkv, cap_s), dtype=torch.int32, device="cuda")
     sc = torch.empty((hkv,), dtype=torch.int32, device="cuda")
-    sel_ws = torch.empty(max(vsa.vs_select_workspace_bytes(hkv, n), 1), dtype=torch.uint8, device="cuda")
+    sel_ws = torch.empty(max(vsa.vs_select_both_workspace_bytes(hkv, n), 1), dtype=torch.uint8, device="cuda")
     attn_ws = torch.empty(vsa.vs_attn_workspace_bytes(hkv, n, cap_v, cap_s), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(qd)
     lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
@@ -224,8 +224,7 @@ def main():
         if mass is not None:
             if w1d is not None:
                 vsa.vs_index(kd, vd, w1d, w2d, vlog_d, slog_d)
-            vsa.vs_select(vlog_d, vsa.VS_VERTICAL, mass, cap_v, vi, vc, sel_ws)
-            vsa.vs_select(slog_d, vsa.VS_SLASH, mass, cap_s, si, sc, sel_ws)
+            vsa.vs_select_both(vlog_d, slog_d, mass, cap_v, cap_s, vi, vc, si, sc, sel_ws)
             lists = (vi, vc, si, sc)
         else:
             lists = lists0
@@ -306,7 +305,8 @@ def main():
 
 
 def bench_indexer(args, w, torch, vsa, workloads):
-    """vs_index + vs_select (both kinds) at 8 KV heads x 131072 positions."""
+    """vs_index + vs_select_both (both kinds in one chain) at 8 KV heads x 131072
+    positions; the two kinds as separate vs_select calls are timed beside it."""
     n, hkv, d = w["n"], w["hkv"], w["d"]
     k, v, w1, w2 = workloads.indexer_inputs(args.workload)
     kd, vd, w1d, w2d = (_dev(x, torch) for x in (k, v, w1, w2))
@@ -317,20 +317,25 @@ def bench_indexer(args, w, torch, vsa, workloads):
     si = torch.empty((hkv, n), dtype=torch.int32, device="cuda")
     sc = torch.empty((hkv,), dtype=torch.int32, device="cuda")
     ws = torch.empty(vsa.vs_select_workspace_bytes(hkv, n), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(vsa.vs_select_both_workspace_bytes(hkv, n), dtype=torch.uint8, device="cuda")
     e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    ti, ts = [], []
+    ti, ts, ts2 = [], [], []
     for it in range(args.warmup + args.steps):
         e[0].record()
         vsa.vs_index(kd, vd, w1d, w2d, vlog, slog)
         e[1].record()
+        vsa.vs_select_both(vlog, slog, w["mass"], n, n, vi, vc, si, sc, ws2)
+        e[2].record()
+        # the same two selections as separate calls, for comparison
         vsa.vs_select(vlog, vsa.VS_VERTICAL, w["mass"], n, vi, vc, ws)
         vsa.vs_select(slog, vsa.VS_SLASH, w["mass"], n, si, sc, ws)
-        e[2].record()
+        e[3].record()
         torch.cuda.synchronize()
         if it >= args.warmup:
             ti.append(e[0].elapsed_time(e[1]))
             ts.append(e[1].elapsed_time(e[2]))
-    ms_i, ms_s = float(np.mean(ti)), float(np.mean(ts))
+            ts2.append(e[2].elapsed_time(e[3]))
+    ms_i, ms_s, ms_s2 = float(np.mean(ti)), float(np.mean(ts)), float(np.mean(ts2))
     budgets_v, budgets_s = vc.cpu().numpy(), sc.cpu().numpy()
     # the max-based threshold mode on the same logits (both kinds)
     alpha = args.alpha
@@ -346,20 +351,18 @@ def bench_indexer(args, w, torch, vsa, workloads):
     ms_t = float(np.mean(tt))
     kept_t = {"vertical": vc.cpu().tolist(), "slash": sc.cpu().tolist()}
     # the same step (index + both selections) captured once in a HIP graph and
-    # replayed: the chain is 24 short launches, so launch overhead is visible
+    # replayed: the chain is 16 short launches, so launch overhead is visible
     cs = torch.cuda.Stream()
     cs.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cs):
         vsa.vs_index(kd, vd, w1d, w2d, vlog, slog)
-        vsa.vs_select(vlog, vsa.VS_VERTICAL, w["mass"], n, vi, vc, ws)
-        vsa.vs_select(slog, vsa.VS_SLASH, w["mass"], n, si, sc, ws)
+        vsa.vs_select_both(vlog, slog, w["mass"], n, n, vi, vc, si, sc, ws2)
     torch.cuda.current_stream().wait_stream(cs)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         vsa.vs_index(kd, vd, w1d, w2d, vlog, slog)
-        vsa.vs_select(vlog, vsa.VS_VERTICAL, w["mass"], n, vi, vc, ws)
-        vsa.vs_select(slog, vsa.VS_SLASH, w["mass"], n, si, sc, ws)
+        vsa.vs_select_both(vlog, slog, w["mass"], n, n, vi, vc, si, sc, ws2)
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -383,6 +386,7 @@ def bench_indexer(args, w, torch, vsa, workloads):
         "config": {"workload": "indexer128k", "n": n, "h_kv": hkv, "d": d, "hidden": w["hidden"],
                    "mass": w["mass"], "seed": w["seed"]},
         "index_ms": round(ms_i, 4), "select_ms": round(ms_s, 4),
+        "select_two_calls_ms": round(ms_s2, 4),
         "graph_step_ms": round(ms_graph, 4), "graph_matches_eager": graph_budgets_ok,
         "select_gbs": round(sel_bytes / (ms_s * 1e-3) / 1e9, 1),
         "threshold": {"alpha": alpha, "ms": round(ms_t, 4), "kept": kept_t},

@@ -109,6 +109,23 @@ vs_status vs_select_threshold(const float* logit, int heads, int n, vs_kind kind
                               int cap, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
                               hipStream_t stream);
 
+/* Both selections of a layer in one launch chain: vs_select of vlog as
+ * VERTICAL (cap_v) and of slog as SLASH (cap_s), with the same mass.  The
+ * two kinds run side by side as 2 * heads rows of one chain, so the call
+ * costs about what one vs_select of `heads` heads costs (the chain is bound
+ * by the latency of its passes, not by the candidates).  Outputs are
+ * bit-identical to the two separate calls.
+ *   vlog, slog      : fp32 [heads][n] (finite values)
+ *   v_idx, v_cnt    : int32 [heads][cap_v], [heads] -- columns, as vs_select
+ *   s_off, s_cnt    : int32 [heads][cap_s], [heads] -- offsets, as vs_select
+ *   ws              : device workspace of at least
+ *                     vs_select_both_workspace_bytes(heads, n)
+ * Requires 0 < mass <= 1, 1 <= cap_v, cap_s <= n, heads <= 32767. */
+size_t vs_select_both_workspace_bytes(int heads, int n);
+vs_status vs_select_both(const float* vlog, const float* slog, int heads, int n, double mass,
+                         int cap_v, int cap_s, int32_t* v_idx, int32_t* v_cnt, int32_t* s_off,
+                         int32_t* s_cnt, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* -------------------------------------------------------- sparse attention
  * Causal prefill attention restricted to the vertical-slash index set
  * (English page, section 2, "Core Concept: Vertical-Slash Pattern" and

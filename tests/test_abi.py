@@ -71,6 +71,23 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert L.vs_select_threshold(None, 1, 10, 0, 0.5, 5, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
     assert L.vs_select_threshold(p, 1, 10, 0, 0.5, 11, p, p, p, 1 << 20, None) == vsa.VS_ERR_INVALID
     assert L.vs_select_threshold(p, 1, 10, 0, 0.5, 5, p, p, p, 8, None) == vsa.VS_ERR_WORKSPACE
+    # vs_select_both: pointers, heads, mass, both caps, workspace
+    both = lambda **kw: L.vs_select_both(*[kw.get(k, dv) for k, dv in (
+        ("vlog", p), ("slog", p), ("heads", 2), ("n", 10), ("mass", 0.5), ("cap_v", 5), ("cap_s", 5),
+        ("v_idx", p), ("v_cnt", p), ("s_off", p), ("s_cnt", p), ("ws", p), ("ws_bytes", 1 << 20),
+        ("stream", None))])
+    for name in ("vlog", "slog", "v_idx", "v_cnt", "s_off", "s_cnt", "ws"):
+        assert both(**{name: None}) == vsa.VS_ERR_INVALID, name
+    assert both(heads=0) == vsa.VS_ERR_INVALID
+    assert both(heads=32768) == vsa.VS_ERR_INVALID
+    assert both(n=0) == vsa.VS_ERR_INVALID
+    assert both(mass=0.0) == vsa.VS_ERR_INVALID
+    assert both(mass=1.5) == vsa.VS_ERR_INVALID
+    assert both(cap_v=0) == vsa.VS_ERR_INVALID
+    assert both(cap_s=11) == vsa.VS_ERR_INVALID
+    assert both(ws_bytes=8) == vsa.VS_ERR_WORKSPACE
+    assert L.vs_select_both_workspace_bytes(3, 1000) == L.vs_select_workspace_bytes(6, 1000)
+    assert L.vs_select_both_workspace_bytes(0, 1000) == 0
     # vs_attn_aggregate: pointers, shapes, workspace
     agg = lambda **kw: L.vs_attn_aggregate(*[kw.get(k, dv) for k, dv in (
         ("q", p), ("k", p), ("v", p), ("h_q", 8), ("h_kv", 2), ("n", 256), ("d", 128),

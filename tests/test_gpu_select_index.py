@@ -173,6 +173,38 @@ def test_clustered128k_layer_sampled():
     assert_attn_close(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, "clustered128k")
 
 
+BOTH_CASES = [
+    # heads, n, mass, cap_v, cap_s
+    (8, 131072, 0.95, 131072, 131072),
+    (8, 131072, 0.95, 4096, 8192),
+    (3, 5000 + 7, 0.5, 100, 5007),
+    (1, 1, 0.9, 1, 1),
+    (5, 3000, 1.0, 3000, 17),
+]
+
+
+@pytest.mark.parametrize("case", BOTH_CASES, ids=[f"h{c[0]}-n{c[1]}-m{c[2]}-cv{c[3]}-cs{c[4]}" for c in BOTH_CASES])
+def test_select_both_equals_two_selects(case):
+    """vs_select_both runs both kinds as one chain: bit-identical to two
+    vs_select calls and to the oracle's selections."""
+    heads, n, mass, cap_v, cap_s = case
+    _log(f"case: select both {case}")
+    rng = np.random.default_rng(heads * 7 + n)
+    vlog = (rng.standard_normal((heads, n)) * 2).astype(np.float32)
+    slog = rng.choice(np.array([0.0, -0.5, -1.0, -3.0], np.float32), size=(heads, n)) if heads == 3 else \
+        (rng.standard_normal((heads, n)) * 3).astype(np.float32)
+    vi, vc, si, sc = vsa.vs_select_both(to_dev(vlog), to_dev(slog), mass, cap_v, cap_s)
+    vi1, vc1 = vsa.vs_select(to_dev(vlog), vsa.VS_VERTICAL, mass, cap_v)
+    si1, sc1 = vsa.vs_select(to_dev(slog), vsa.VS_SLASH, mass, cap_s)
+    torch.cuda.synchronize()
+    for a, b, what in ((vi, vi1, "v_idx"), (vc, vc1, "v_cnt"), (si, si1, "s_off"), (sc, sc1, "s_cnt")):
+        assert torch.equal(a, b), what
+    ri, rc = oracle.select(vlog, oracle.VERTICAL, mass, cap_v)
+    _assert_same_selection(vi.cpu().numpy(), vc.cpu().numpy(), ri, rc, "both: vertical")
+    ri, rc = oracle.select(slog, oracle.SLASH, mass, cap_s)
+    _assert_same_selection(si.cpu().numpy(), sc.cpu().numpy(), ri, rc, "both: slash")
+
+
 THRESH_CASES = [
     # name, heads, n, alpha, cap
     ("normal", 8, 131072, 0.01, 131072),

@@ -9,6 +9,7 @@ calls raise.
     vs_index(k_rope, v, w1, w2)                    -> (vlog, slog)
     vs_select(logit, kind, mass, cap)              -> (idx, count)
     vs_select_threshold(logit, kind, alpha, cap)   -> (idx, count)
+    vs_select_both(vlog, slog, mass, cap_v, cap_s) -> (v_idx, v_cnt, s_off, s_cnt)
     vs_attn_aggregate(q, k, v)                     -> (out, lse, a_v, a_s)
     vs_block_discover(q, k, skel, alpha)           -> mask (, score)
     vs_block_attn_prefill(q, k, v, mask)           -> (out, lse)
@@ -36,6 +37,7 @@ VS_BF16, VS_F32 = 0, 1
 VS_VERTICAL, VS_SLASH = 0, 1
 
 _SYMBOLS = ("vs_index", "vs_select_workspace_bytes", "vs_select", "vs_select_threshold",
+            "vs_select_both_workspace_bytes", "vs_select_both",
             "vs_attn_workspace_bytes", "vs_aggregate_workspace_bytes", "vs_attn_aggregate",
             "vs_sparse_attn_prefill", "vs_sparse_attn_prefill_qh", "vs_sparse_attn_prefill_varlen",
             "vs_attn_tile_counts", "vs_block_workspace_bytes",
@@ -68,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.vs_select.restype = i32
         L.vs_select_threshold.argtypes = [P, i32, i32, i32, f64, i32, P, P, P, sz, P]
         L.vs_select_threshold.restype = i32
+        L.vs_select_both_workspace_bytes.argtypes = [i32, i32]
+        L.vs_select_both_workspace_bytes.restype = sz
+        L.vs_select_both.argtypes = [P, P, i32, i32, f64, i32, i32, P, P, P, P, P, sz, P]
+        L.vs_select_both.restype = i32
         L.vs_aggregate_workspace_bytes.argtypes = [i32, i32]
         L.vs_aggregate_workspace_bytes.restype = sz
         L.vs_attn_aggregate.argtypes = [P, P, P, i32, i32, i32, i32, f32, P, P, P, P, P, sz, P]
@@ -221,6 +227,44 @@ def vs_select(logit: torch.Tensor, kind: int, mass: float, cap: int, idx: torch.
 
 def vs_attn_workspace_bytes(h_kv: int, n: int, cap_v: int, cap_s: int) -> int:
     return int(lib().vs_attn_workspace_bytes(h_kv, n, cap_v, cap_s))
+
+
+def vs_select_both_workspace_bytes(heads: int, n: int) -> int:
+    return int(lib().vs_select_both_workspace_bytes(heads, n))
+
+
+def vs_select_both(vlog: torch.Tensor, slog: torch.Tensor, mass: float, cap_v: int, cap_s: int,
+                   v_idx: torch.Tensor | None = None, v_cnt: torch.Tensor | None = None,
+                   s_off: torch.Tensor | None = None, s_cnt: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None, stream=None):
+    """Both cumulative-mass selections of a layer in one launch chain:
+    vlog as VERTICAL (cap_v), slog as SLASH (cap_s), fp32 [heads, n] each.
+    Returns int32 (v_idx [heads, cap_v], v_cnt [heads], s_off [heads, cap_s],
+    s_cnt [heads]), bit-identical to two vs_select calls."""
+    _need(vlog, "vlog", torch.float32, 2)
+    dev = vlog.device
+    _need(slog, "slog", torch.float32, 2, dev)
+    if slog.shape != vlog.shape:
+        raise ValueError("vs_select_both: vlog and slog must have the same shape")
+    heads, n = vlog.shape
+    v_idx = torch.empty((heads, cap_v), dtype=torch.int32, device=dev) if v_idx is None else v_idx
+    s_off = torch.empty((heads, cap_s), dtype=torch.int32, device=dev) if s_off is None else s_off
+    v_cnt = torch.empty((heads,), dtype=torch.int32, device=dev) if v_cnt is None else v_cnt
+    s_cnt = torch.empty((heads,), dtype=torch.int32, device=dev) if s_cnt is None else s_cnt
+    for t, nm, shape in ((v_idx, "v_idx", (heads, cap_v)), (s_off, "s_off", (heads, cap_s)),
+                         (v_cnt, "v_cnt", (heads,)), (s_cnt, "s_cnt", (heads,))):
+        _need(t, nm, torch.int32, len(shape), dev)
+        if t.shape != shape:
+            raise ValueError(f"vs_select_both: {nm} must be {list(shape)}")
+    need = vs_select_both_workspace_bytes(heads, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = lib().vs_select_both(_ptr(vlog), _ptr(slog), heads, n, float(mass), int(cap_v), int(cap_s),
+                              _ptr(v_idx), _ptr(v_cnt), _ptr(s_off), _ptr(s_cnt), _ptr(workspace),
+                              workspace.numel(), _stream(vlog, stream))
+    _check("vs_select_both", st)
+    return v_idx, v_cnt, s_off, s_cnt
 
 
 def vs_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -517,7 +561,8 @@ def vs_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tens
     Pipeline"): the indexer scores every position from [K_rope | V]
     (vs_index), the cumulative-mass budget picks each KV head's columns and
     slash offsets (vs_select, twice), and sparse attention runs over their
-    union (vs_sparse_attn_prefill).  q bf16 [h_q, n, d]; k (already rotated)
+    union (vs_sparse_attn_prefill; the two selections run as one chain,
+    vs_select_both).  q bf16 [h_q, n, d]; k (already rotated)
     and v bf16 [h_kv, n, d]; w1 bf16 [hidden, 2d]; w2 bf16 [2, hidden].
     cap_v / cap_s bound the budgets (default n, i.e. uncapped).  Every launch
     goes on one stream; nothing is synchronised.  Returns (out, lse,
@@ -526,9 +571,8 @@ def vs_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tens
     cap_v = n if cap_v is None else int(cap_v)
     cap_s = n if cap_s is None else int(cap_s)
     vlog, slog = vs_index(k, v, w1, w2, stream=stream)
-    ws = torch.empty(max(vs_select_workspace_bytes(h_kv, n), 1), dtype=torch.uint8, device=k.device)
-    v_idx, v_cnt = vs_select(vlog, VS_VERTICAL, mass, cap_v, workspace=ws, stream=stream)
-    s_off, s_cnt = vs_select(slog, VS_SLASH, mass, cap_s, workspace=ws, stream=stream)
+    ws = torch.empty(max(vs_select_both_workspace_bytes(h_kv, n), 1), dtype=torch.uint8, device=k.device)
+    v_idx, v_cnt, s_off, s_cnt = vs_select_both(vlog, slog, mass, cap_v, cap_s, workspace=ws, stream=stream)
     out, lse = vs_sparse_attn_prefill(q, k, v, v_idx, v_cnt, s_off, s_cnt, scale=scale, stream=stream)
     if stream is not None:  # the temporaries are freed on return, while `stream` may still use them
         for t in (vlog, slog, ws):

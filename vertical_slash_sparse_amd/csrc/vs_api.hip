@@ -63,6 +63,24 @@ vs_status vs_select(const float* logit, int heads, int n, vs_kind kind, double m
   return from_hip(launch_select(logit, heads, n, (int)kind, mass, 0ull, cap, idx, count, ws, stream));
 }
 
+size_t vs_select_both_workspace_bytes(int heads, int n) {
+  if (heads <= 0 || n <= 0 || heads > 32767) return 0;
+  return SelectWsLayout(2 * heads, n).total;
+}
+
+vs_status vs_select_both(const float* vlog, const float* slog, int heads, int n, double mass,
+                         int cap_v, int cap_s, int32_t* v_idx, int32_t* v_cnt, int32_t* s_off,
+                         int32_t* s_cnt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!vlog || !slog || !v_idx || !v_cnt || !s_off || !s_cnt || !ws) return VS_ERR_INVALID;
+  if (heads <= 0 || n <= 0 || heads > 32767) return VS_ERR_INVALID;
+  if (!(mass > 0.0 && mass <= 1.0)) return VS_ERR_INVALID;
+  if (cap_v < 1 || cap_v > n || cap_s < 1 || cap_s > n) return VS_ERR_INVALID;
+  if (ws_bytes < vs_select_both_workspace_bytes(heads, n)) return VS_ERR_WORKSPACE;
+  const SelSide sides[2] = {{vlog, v_idx, v_cnt, (int)VS_VERTICAL, cap_v},
+                            {slog, s_off, s_cnt, (int)VS_SLASH, cap_s}};
+  return from_hip(launch_select_sides(sides, 2, heads, n, mass, 0ull, ws, stream));
+}
+
 vs_status vs_select_threshold(const float* logit, int heads, int n, vs_kind kind, double alpha,
                               int cap, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
                               hipStream_t stream) {

@@ -96,6 +96,18 @@ hipError_t launch_aggregate(const void* q, const void* k, const void* v, int h_q
 
 // mass in (0, 1] with thresh == 0: cumulative-mass budget; thresh > 0: keep
 // quantised masses >= thresh (max-based threshold)
+// One kind of candidates of a selection: [heads][n] scores in, [heads][cap]
+// indices and [heads] counts out.
+struct SelSide {
+  const float* logit;
+  int32_t* idx;
+  int32_t* count;
+  int kind, cap;
+};
+// The selection chain over nsides (1 or 2) kinds at once, each for `heads`
+// heads; the workspace holds nsides * heads rows (SelectWsLayout).
+hipError_t launch_select_sides(const SelSide* sides, int nsides, int heads, int n, double mass,
+                               unsigned long long thresh, void* ws, hipStream_t stream);
 hipError_t launch_select(const float* logit, int heads, int n, int kind, double mass,
                          unsigned long long thresh, int cap, int32_t* idx, int32_t* count, void* ws,
                          hipStream_t stream);

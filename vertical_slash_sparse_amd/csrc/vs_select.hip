@@ -143,20 +143,34 @@ __device__ int block_count(bool flag, int* total, int* sh) {
   return before + below;
 }
 
+// Workspace rows r < hk select side[0]'s candidates, rows hk .. 2 hk - 1
+// side[1]'s (when two kinds share one chain).
 struct SelArgs {
-  const float* logit;
-  int n, kind, cap, chunks;
+  SelSide side[2];
+  int hk;  // heads per side
+  int n, chunks;
   double mass;
   unsigned long long thresh;  // threshold mode: keep u >= thresh; 0 for the mass budget
-  int32_t* idx;
-  int32_t* count;
   uint32_t* key;
   uint64_t* um;
-  unsigned long long* state;  // [heads][16]
-  uint32_t* hcnt;             // [heads][2][256]
-  unsigned long long* hmass;  // [heads][2][256]
-  int32_t* cc;                // [heads][chunks][4]: strict, ties, strict before, ties before
+  unsigned long long* state;  // [rows][16]
+  uint32_t* hcnt;             // [rows][2][256]
+  unsigned long long* hmass;  // [rows][2][256]
+  int32_t* cc;                // [rows][chunks][4]: strict, ties, strict before, ties before
 };
+
+// what workspace row r selects from and where it writes
+struct RowRef {
+  const float* row;  // its candidates' scores
+  int kind, cap;
+  int32_t* idx;      // its [cap] output
+  int32_t* count;    // its count
+};
+__device__ __forceinline__ RowRef row_ref(const SelArgs& a, int r) {
+  const int s = r >= a.hk ? 1 : 0, h = r - s * a.hk;
+  const SelSide& sd = a.side[s];
+  return RowRef{sd.logit + (size_t)h * a.n, sd.kind, sd.cap, sd.idx + (size_t)h * sd.cap, sd.count + h};
+}
 
 __global__ __launch_bounds__(kSelThreads) void sel_init_kernel(SelArgs a) {
   const int h = blockIdx.x, tid = threadIdx.x;
@@ -172,10 +186,10 @@ __global__ __launch_bounds__(kSelThreads) void sel_init_kernel(SelArgs a) {
 __global__ __launch_bounds__(kSelThreads) void sel_max_kernel(SelArgs a) {
   __shared__ uint32_t sh[kSelWaves];
   const int h = blockIdx.y, c0 = blockIdx.x * kSelChunk;
-  const float* row = a.logit + (size_t)h * a.n;
+  const RowRef rr = row_ref(a, h);
   uint32_t km = 0u;
   for (int c = c0 + threadIdx.x; c < min(c0 + kSelChunk, a.n); c += kSelThreads)
-    km = max(km, order_key(load_score(row, a.n, a.kind, c)));
+    km = max(km, order_key(load_score(rr.row, a.n, rr.kind, c)));
   km = block_reduce(km, [](uint32_t x, uint32_t y) { return max(x, y); }, sh);
   if (threadIdx.x == 0) atomicMax(&a.state[16 * (size_t)h + kStMaxKey], (unsigned long long)km);
 }
@@ -185,13 +199,13 @@ __global__ __launch_bounds__(kSelThreads) void sel_mass_kernel(SelArgs a) {
   __shared__ unsigned long long shu[kSelWaves];
   __shared__ uint32_t shk[kSelWaves];
   const int h = blockIdx.y, c0 = blockIdx.x * kSelChunk;
-  const float* row = a.logit + (size_t)h * a.n;
+  const RowRef rr = row_ref(a, h);
   unsigned long long* st = a.state + 16 * (size_t)h;
   const float mx = key_score((uint32_t)st[kStMaxKey]);
   unsigned long long usum = 0, ncand = 0, nabove = 0;
   uint32_t kmin = 0xffffffffu;
   for (int c = c0 + threadIdx.x; c < min(c0 + kSelChunk, a.n); c += kSelThreads) {
-    float s = load_score(row, a.n, a.kind, c);
+    float s = load_score(rr.row, a.n, rr.kind, c);
     if (s == 0.0f) s = 0.0f;
     const float x = s - mx;
     const bool cand = x >= -32.0f;
@@ -226,10 +240,10 @@ __global__ void sel_prep_kernel(SelArgs a) {
     // threshold mode: the budget is the count at or above the threshold; no
     // mass target can stop the walk first (T exceeds the total mass)
     st[kStT] = U + 1ull;
-    st[kStCap] = min((unsigned long long)a.cap, st[kStAbove]);
+    st[kStCap] = min((unsigned long long)row_ref(a, h).cap, st[kStAbove]);
   } else {
     st[kStT] = (unsigned long long)__builtin_ceil(a.mass * (double)U);
-    st[kStCap] = (unsigned long long)a.cap;
+    st[kStCap] = (unsigned long long)row_ref(a, h).cap;
   }
   const uint32_t kmin = (uint32_t)st[kStKmin], kmax = (uint32_t)st[kStMaxKey];
   const uint32_t range = kmax - kmin;
@@ -422,7 +436,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_scan_kernel(SelArgs a) {
   if (threadIdx.x == 0) {
     st[kStR] = r;
     st[kStK] = (unsigned long long)K;
-    a.count[h] = K;
+    *row_ref(a, h).count = K;
   }
 }
 
@@ -441,7 +455,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_write_kernel(SelArgs a) {
   const long long ties_taken_before = min((long long)tie_before, r);
   int written = strict_before + (int)ties_taken_before;
   int ties_seen = tie_before;
-  int32_t* out = a.idx + (size_t)h * a.cap;
+  const RowRef rr = row_ref(a, h);
+  int32_t* out = rr.idx;
   for (int base = c0; base < min(c0 + kSelChunk, a.n); base += kSelThreads) {
     const int c = base + threadIdx.x;
     const bool in = c < min(c0 + kSelChunk, a.n);
@@ -453,55 +468,61 @@ __global__ __launch_bounds__(kSelThreads) void sel_write_kernel(SelArgs a) {
     const bool take = strict || (tie && (long long)tie_rank < r);
     int take_total;
     const int pos = written + block_count(take, &take_total, sh);
-    if (take && pos < a.cap) out[pos] = c;
+    if (take && pos < rr.cap) out[pos] = c;
     ties_seen += tie_total;
     written += take_total;
   }
   // this chunk's share of the unused slots
-  const int spare = a.cap - K;
+  const int spare = rr.cap - K;
   if (spare > 0) {
     const int per = (spare + a.chunks - 1) / a.chunks;
-    const int lo = K + q * per, hi = min(K + (q + 1) * per, a.cap);
+    const int lo = K + q * per, hi = min(K + (q + 1) * per, rr.cap);
     for (int t = lo + threadIdx.x; t < hi; t += kSelThreads) out[t] = -1;
   }
 }
 
 }  // namespace
 
-hipError_t launch_select(const float* logit, int heads, int n, int kind, double mass,
-                         unsigned long long thresh, int cap, int32_t* idx, int32_t* count, void* ws,
-                         hipStream_t stream) {
-  const SelectWsLayout L(heads, n);
+hipError_t launch_select_sides(const SelSide* sides, int nsides, int heads, int n, double mass,
+                               unsigned long long thresh, void* ws, hipStream_t stream) {
+  const int rows = nsides * heads;
+  const SelectWsLayout L(rows, n);
   char* base = static_cast<char*>(ws);
   SelArgs a;
-  a.logit = logit;
+  a.side[0] = sides[0];
+  a.side[1] = nsides > 1 ? sides[1] : sides[0];
+  a.hk = heads;
   a.n = n;
-  a.kind = kind;
-  a.cap = cap;
   a.chunks = L.chunks;
   a.mass = mass;
   a.thresh = thresh;
-  a.idx = idx;
-  a.count = count;
   a.key = reinterpret_cast<uint32_t*>(base + L.off_key);
   a.um = reinterpret_cast<uint64_t*>(base + L.off_mass);
   a.state = reinterpret_cast<unsigned long long*>(base + L.off_state);
   a.hcnt = reinterpret_cast<uint32_t*>(base + L.off_hcnt);
   a.hmass = reinterpret_cast<unsigned long long*>(base + L.off_hmass);
   a.cc = reinterpret_cast<int32_t*>(base + L.off_cc);
-  const dim3 chunks((unsigned)L.chunks, (unsigned)heads);
-  hipLaunchKernelGGL(sel_init_kernel, dim3((unsigned)heads), dim3(kSelThreads), 0, stream, a);
+  const unsigned nrow = (unsigned)rows;
+  const dim3 chunks((unsigned)L.chunks, nrow);
+  hipLaunchKernelGGL(sel_init_kernel, dim3(nrow), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_max_kernel, chunks, dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_mass_kernel, chunks, dim3(kSelThreads), 0, stream, a);
-  hipLaunchKernelGGL(sel_prep_kernel, dim3((unsigned)heads), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(sel_prep_kernel, dim3(nrow), dim3(64), 0, stream, a);
   for (int pass = 0; pass < kMaxPasses; ++pass) {
     hipLaunchKernelGGL(sel_hist_kernel, chunks, dim3(kSelThreads), 0, stream, a, pass);
-    hipLaunchKernelGGL(sel_decide_kernel, dim3((unsigned)heads), dim3(64), 0, stream, a, pass);
+    hipLaunchKernelGGL(sel_decide_kernel, dim3(nrow), dim3(64), 0, stream, a, pass);
   }
   hipLaunchKernelGGL(sel_count_kernel, chunks, dim3(kSelThreads), 0, stream, a);
-  hipLaunchKernelGGL(sel_scan_kernel, dim3((unsigned)heads), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_scan_kernel, dim3(nrow), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_write_kernel, chunks, dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_select(const float* logit, int heads, int n, int kind, double mass,
+                         unsigned long long thresh, int cap, int32_t* idx, int32_t* count, void* ws,
+                         hipStream_t stream) {
+  const SelSide side{logit, idx, count, kind, cap};
+  return launch_select_sides(&side, 1, heads, n, mass, thresh, ws, stream);
 }
 
 }  // namespace vs
