@@ -240,3 +240,46 @@ def test_solid_offset_runs_and_visible_columns(case):
     out, lse = _run_gpu(q, k, v, vidx, vcnt, soff, scnt)
     ro, rl = oracle.attn(q, k, v, vidx, vcnt, soff, scnt)
     assert_attn_close(out, lse, ro, rl, str(case))
+
+
+def test_one_million_tokens_sampled():
+    """n = 2^20 (1M positions), 4 query heads on 1 KV head, d = 128, bf16:
+    64 columns (4 sinks, a run at 2^19 and random ones) and 64 offsets (a local
+    band plus random ones up to n - 1), so positions, bitmap words and offsets
+    run to their largest values; sampled rows, including the last ones,
+    against the oracle.  Then the block path on the same inputs: discovery
+    at its 16384-block limit and block attention, rows sampled."""
+    n, hq, hkv, d = 1 << 20, 4, 1, 128
+    _log("case: 1M tokens")
+    rng = np.random.default_rng(2024)
+    q = workloads.to_bf16_bits(rng.standard_normal((hq, n, d), dtype=np.float32))
+    k = workloads.to_bf16_bits(rng.standard_normal((hkv, n, d), dtype=np.float32))
+    v = workloads.to_bf16_bits(rng.standard_normal((hkv, n, d), dtype=np.float32))
+    cols = np.unique(np.concatenate([np.arange(4), np.arange(1 << 19, (1 << 19) + 20),
+                                     rng.choice(np.arange(4, n), 40, replace=False)]))
+    offs = np.unique(np.concatenate([np.arange(16), [n - 1, n - 2, n // 2],
+                                     rng.choice(np.arange(16, n), 45, replace=False)]))
+    vidx, vcnt = _pad_lists([cols])
+    soff, scnt = _pad_lists([offs])
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    out, lse = vsa.vs_sparse_attn_prefill(qd, kd, vd, to_dev(vidx), to_dev(vcnt), to_dev(soff), to_dev(scnt))
+    torch.cuda.synchronize()
+    rows = sample_rows(np.random.default_rng(5), hq, n, 8)
+    ro, rl = oracle.attn(q, k, v, vidx, vcnt, soff, scnt, rows=rows)
+    og = to_f64(out)[rows[:, 0], rows[:, 1]]
+    lg = lse.cpu().numpy().astype(np.float64)[rows[:, 0], rows[:, 1]]
+    del out, lse
+    assert_attn_close(og, lg, ro, rl, "1M vertical-slash")
+
+    _log("case: 1M tokens, block path")
+    mask = vsa.vs_block_discover(qd, kd, 8, 0.9)
+    out, lse = vsa.vs_block_attn_prefill(qd, kd, vd, mask)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy().view(np.uint32)
+    nb = n // 64
+    assert m.shape == (hkv, nb, oracle.words_per_row(nb))
+    diag = (m[0, np.arange(nb), np.arange(nb) // 32] >> (np.arange(nb) % 32)) & 1
+    assert diag.all(), "every query block keeps its diagonal block"
+    ro, rl = oracle.block_attn(q, k, v, m, rows=rows)
+    assert_attn_close(to_f64(out)[rows[:, 0], rows[:, 1]], lse.cpu().numpy().astype(np.float64)[rows[:, 0], rows[:, 1]],
+                      ro, rl, "1M block path")
