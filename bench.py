@@ -154,7 +154,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="zipf128k",
                     choices=["zipf128k", "clustered128k", "fixed32k", "indexer128k", "e2e256k",
-                             "aggregate32k", "blocks128k", "blocks256k"])
+                             "aggregate32k", "blocks128k", "blocks256k", "qh32k", "varlen64k"])
     ap.add_argument("--dense-ref", action="store_true",
                     help="blocks*: also time dense causal attention (the same kernel, every block kept) "
                          "once, for the speedup")
@@ -186,6 +186,8 @@ def main():
         return bench_aggregate(args, torch, vsa, workloads)
     if args.workload in ("blocks128k", "blocks256k"):
         return bench_blocks(args, torch, vsa, workloads)
+    if args.workload in ("qh32k", "varlen64k"):
+        return bench_layouts(args, torch, vsa, workloads)
 
     n, hq, hkv, d = w["n"], w["hq"], w["hkv"], w["d"]
     group = hq // hkv
@@ -454,6 +456,85 @@ def bench_aggregate(args, torch, vsa, workloads):
                      "unit": "TFLOP/s", "frac": round(f2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
     }
+    print(json.dumps(res), flush=True)
+
+
+def bench_layouts(args, torch, vsa, workloads):
+    """The other two index layouts of the sparse attention: one index set per
+    query head (qh32k: vs_sparse_attn_prefill_qh on the 32K layer, sets from
+    per-head Zipf scores) and a packed batch of sequences (varlen64k:
+    vs_sparse_attn_prefill_varlen).  Attention only; the sets are chosen
+    before the timed region."""
+    w = workloads.WORKLOADS[args.workload]
+    hq, hkv, d = w["hq"], w["hkv"], w["d"]
+    if args.workload == "qh32k":
+        n = w["n"]
+        q, k, v = workloads.attention_inputs(args.workload)
+        vl, sl = workloads.qh_scores(args.workload)
+        vi, vc = vsa.vs_select(_dev(vl, torch), vsa.VS_VERTICAL, w["mass"], w["cap_v"])
+        si, sc = vsa.vs_select(_dev(sl, torch), vsa.VS_SLASH, w["mass"], w["cap_s"])
+        lists = (vi, vc, si, sc)
+        lists_np = [x.cpu().numpy() for x in lists]
+        # per query head: group of one
+        pairs = pair_counts(*lists_np, n)
+        f_alg = 4.0 * d * float(pairs.sum())
+        causal = hq * n * (n + 1) / 2
+        metric = "ms/layer + effective TFLOP/s, per-query-head VS sparse prefill @32K"
+        cfg = {"workload": args.workload, "n": n, "h_q": hq, "h_kv": hkv, "d": d, "mass": w["mass"],
+               "cap_v": w["cap_v"], "cap_s": w["cap_s"], "seed": w["seed"]}
+    else:
+        cu, q, k, v, lists_np = workloads.varlen_batch(args.workload)
+        n = int(cu[-1])
+        lists = [_dev(x, torch) for x in lists_np]
+        pairs = np.array([pair_counts(lists_np[0][s], lists_np[1][s], lists_np[2][s], lists_np[3][s],
+                                      int(cu[s + 1] - cu[s])).sum() for s in range(len(cu) - 1)])
+        f_alg = 4.0 * d * (hq // hkv) * float(pairs.sum())
+        causal = hkv * float(sum((L * (L + 1)) // 2 for L in np.diff(cu).tolist()))
+        metric = "ms/batch + effective TFLOP/s, varlen VS sparse prefill (16 sequences, 64K tokens)"
+        cfg = {"workload": args.workload, "total": n, "nseq": len(cu) - 1, "len_lo": w["len_lo"],
+               "len_hi": w["len_hi"], "h_q": hq, "h_kv": hkv, "d": d, "seed": w["seed"]}
+    qd, kd, vd = _dev(q, torch), _dev(k, torch), _dev(v, torch)
+    out = torch.empty_like(qd)
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+
+    def call():
+        if args.workload == "qh32k":
+            vsa.vs_sparse_attn_prefill_qh(qd, kd, vd, *lists, out=out, lse=lse)
+        else:
+            vsa.vs_sparse_attn_prefill_varlen(qd, kd, vd, cu.tolist(), *lists, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    eff = f_alg / (ms * 1e-3) / 1e12
+    res = {
+        "metric": metric, "value": round(eff, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "config": cfg,
+        "pct_peak_effective": round(100.0 * eff / PEAK_BF16_TFLOPS, 3),
+        "pair_density": round(float(pairs.sum()) / causal, 5),
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel", "achieved": round(eff, 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(eff / PEAK_BF16_TFLOPS, 5),
+                     "traffic": None},
+    }
+    if args.workload == "qh32k":
+        ws = torch.empty(vsa.vs_attn_workspace_bytes(hq, n, lists[0].shape[1], lists[2].shape[1]),
+                         dtype=torch.uint8, device="cuda")
+        vsa.vs_sparse_attn_prefill_qh(qd, kd, vd, *lists, out=out, lse=lse, workspace=ws)
+        dense_t, gath_t, rows_t, keys_t = vsa.vs_attn_tile_counts(ws, hq, n, lists[0].shape[1],
+                                                                  lists[2].shape[1], hq)
+        f_tile = 4.0 * d * float(dense_t + gath_t) * rows_t * keys_t
+        res["tile_tflops"] = round(f_tile / (ms * 1e-3) / 1e12, 3)
+        res["pct_peak_tile"] = round(100.0 * f_tile / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 3)
+        res["tiles"] = {"contiguous": dense_t, "gathered": gath_t, "rows": rows_t, "keys": keys_t}
     print(json.dumps(res), flush=True)
 
 

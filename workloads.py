@@ -23,6 +23,12 @@ head dim 128, one of the backbones the VSPrefill pages evaluate on):
   randomly, so the selected columns and offsets come out as contiguous runs,
   the shape the pages' real heads show; a supplementary workload, not one of
   the pages' configurations
+* ``qh32k`` the 32/8-head layer at n=32768 with one index set per query
+  head: Zipf(1.1) vertical and slash scores per query head over random
+  permutations, mass 0.95, caps 1024 / 2048
+* ``varlen64k`` a packed batch of 16 sequences of 32/8 heads (lengths
+  uniform in [1024, 8192]), per KV head and sequence 4 sink columns plus 3 %
+  random columns and offsets 0..63 plus 6 % random offsets
 * ``indexer128k`` 8 KV heads, n=131072, [RoPE(K) | V] 256-wide bf16 rows and
   random indexer weights W1 ~ N(0, 1/256), W2 ~ N(0, 1/128)
 * ``e2e256k`` 32/8 heads, n=262144, bf16, RoPE, keys of the first 4 positions
@@ -50,6 +56,10 @@ WORKLOADS = {
     "clustered128k": dict(seed=1007, hq=32, hkv=8, n=131072, d=128, dtype="bf16",
                           rope=True, zipf_s=1.1, mass=0.95, cap_v=4096, cap_s=8192,
                           v_centers=8, s_centers=4),
+    "qh32k": dict(seed=1008, hq=32, hkv=8, n=32768, d=128, dtype="bf16", rope=True,
+                  zipf_s=1.1, mass=0.95, cap_v=1024, cap_s=2048),
+    "varlen64k": dict(seed=1009, hq=32, hkv=8, d=128, dtype="bf16", rope=True, nseq=16,
+                      len_lo=1024, len_hi=8192, nv_fixed=4, v_frac=0.03, ns_fixed=64, s_frac=0.06),
     "indexer128k": dict(seed=1004, hkv=8, n=131072, d=128, hidden=128, dtype="bf16",
                         rope=True, mass=0.95),
     "e2e256k": dict(seed=1005, hq=32, hkv=8, n=262144, d=128, hidden=128, dtype="bf16",
@@ -225,6 +235,48 @@ def clustered_scores(name: str = "clustered128k", n: int | None = None, seed: in
     vlog = banded_zipf_logits(rs["score"], w["hkv"], n, w["zipf_s"], w["v_centers"])
     by_offset = banded_zipf_logits(rs["score"], w["hkv"], n, w["zipf_s"], w["s_centers"])
     return vlog, np.ascontiguousarray(by_offset[:, ::-1])
+
+
+def qh_scores(name: str = "qh32k"):
+    """Vertical and slash score vectors [hq, n] fp32, one pair per query head."""
+    w = WORKLOADS[name]
+    rs = streams(w["seed"])
+    return (zipf_logits(rs["score"], w["hq"], w["n"], w["zipf_s"]),
+            zipf_logits(rs["score"], w["hq"], w["n"], w["zipf_s"]))
+
+
+def varlen_batch(name: str = "varlen64k"):
+    """cu_seqlens (nseq + 1 ints), Q [hq, total, d], K, V [hkv, total, d] (bf16
+    bits, RoPE restarting at each sequence) and per-sequence index lists
+    stacked as [nseq, hkv, cap] with counts [nseq, hkv]."""
+    w = WORKLOADS[name]
+    rs = streams(w["seed"])
+    lens = rs["idx"].integers(w["len_lo"], w["len_hi"] + 1, size=w["nseq"])
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    total, d = int(cu[-1]), w["d"]
+    q = np.empty((w["hq"], total, d), np.uint16)
+    k = np.empty((w["hkv"], total, d), np.uint16)
+    v = np.empty((w["hkv"], total, d), np.uint16)
+    per = []
+    for s, n in enumerate(lens.tolist()):
+        tables = rope_tables(n, d)
+        a, b = int(cu[s]), int(cu[s + 1])
+        q[:, a:b] = gaussian_heads(rs["q"], w["hq"], n, d, "bf16", tables)
+        k[:, a:b] = gaussian_heads(rs["k"], w["hkv"], n, d, "bf16", tables)
+        v[:, a:b] = gaussian_heads(rs["v"], w["hkv"], n, d, "bf16", None)
+        per.append(fixed_index_sets(rs["idx"], w["hkv"], n, w["nv_fixed"], int(w["v_frac"] * n),
+                                    w["ns_fixed"], int(w["s_frac"] * n)))
+    cap_v = max(p[0].shape[1] for p in per)
+    cap_s = max(p[2].shape[1] for p in per)
+    vidx = np.full((w["nseq"], w["hkv"], cap_v), -1, np.int32)
+    soff = np.full((w["nseq"], w["hkv"], cap_s), -1, np.int32)
+    vcnt = np.zeros((w["nseq"], w["hkv"]), np.int32)
+    scnt = np.zeros((w["nseq"], w["hkv"]), np.int32)
+    for s, (vi, vc, si, sc) in enumerate(per):
+        vidx[s, :, :vi.shape[1]] = vi
+        soff[s, :, :si.shape[1]] = si
+        vcnt[s], scnt[s] = vc, sc
+    return cu, q, k, v, (vidx, vcnt, soff, scnt)
 
 
 def indexer_weights(rng, d_in: int, hidden: int):
