@@ -525,16 +525,23 @@ def bench_layouts(args, torch, vsa, workloads):
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(eff / PEAK_BF16_TFLOPS, 5),
                      "traffic": None},
     }
+    cap_v, cap_s = lists[0].shape[-1], lists[2].shape[-1]
     if args.workload == "qh32k":
-        ws = torch.empty(vsa.vs_attn_workspace_bytes(hq, n, lists[0].shape[1], lists[2].shape[1]),
-                         dtype=torch.uint8, device="cuda")
+        ws = torch.empty(vsa.vs_attn_workspace_bytes(hq, n, cap_v, cap_s), dtype=torch.uint8, device="cuda")
         vsa.vs_sparse_attn_prefill_qh(qd, kd, vd, *lists, out=out, lse=lse, workspace=ws)
-        dense_t, gath_t, rows_t, keys_t = vsa.vs_attn_tile_counts(ws, hq, n, lists[0].shape[1],
-                                                                  lists[2].shape[1], hq)
-        f_tile = 4.0 * d * float(dense_t + gath_t) * rows_t * keys_t
-        res["tile_tflops"] = round(f_tile / (ms * 1e-3) / 1e12, 3)
-        res["pct_peak_tile"] = round(100.0 * f_tile / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 3)
-        res["tiles"] = {"contiguous": dense_t, "gathered": gath_t, "rows": rows_t, "keys": keys_t}
+        counts = vsa.vs_attn_tile_counts(ws, hq, n, cap_v, cap_s, hq)
+    else:
+        # one tile build over every sequence's rows; the counters sum the batch
+        nseq, longest = len(cu) - 1, int(np.diff(cu).max())
+        ws = torch.empty(vsa.vs_attn_varlen_workspace_bytes(hkv, nseq, longest, cap_v, cap_s),
+                         dtype=torch.uint8, device="cuda")
+        vsa.vs_sparse_attn_prefill_varlen(qd, kd, vd, cu.tolist(), *lists, out=out, lse=lse, workspace=ws)
+        counts = vsa.vs_attn_tile_counts(ws, nseq * hkv, longest, cap_v, cap_s, nseq * hq)
+    dense_t, gath_t, rows_t, keys_t = counts
+    f_tile = 4.0 * d * float(dense_t + gath_t) * rows_t * keys_t
+    res["tile_tflops"] = round(f_tile / (ms * 1e-3) / 1e12, 3)
+    res["pct_peak_tile"] = round(100.0 * f_tile / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 3)
+    res["tiles"] = {"contiguous": dense_t, "gathered": gath_t, "rows": rows_t, "keys": keys_t}
     print(json.dumps(res), flush=True)
 
 

@@ -182,11 +182,17 @@ vs_status vs_sparse_attn_prefill_qh(const void* q, const void* k, const void* v,
  * 0 to total_n (empty sequences allowed).  Lists are per sequence:
  * v_idx [nseq][S][cap_v], v_cnt [nseq][S], s_off [nseq][S][cap_s], s_cnt
  * [nseq][S], with S = h_kv, or h_q when sets_per_query_head is nonzero.
- * The sequences run one after another on `stream` through one workspace of
- * vs_attn_workspace_bytes(S, longest sequence, cap_v, cap_s) bytes (the
- * tile counters then describe the last non-empty sequence).  Supported:
- * as vs_sparse_attn_prefill, with each sequence's K/V of one head under
- * 2 GiB. */
+ * The whole batch is one tile build and one attention launch on `stream`:
+ * the workspace, of vs_attn_varlen_workspace_bytes(S, nseq, longest
+ * sequence, cap_v, cap_s) bytes, holds the tile lists of all nseq * S
+ * index-set rows and a table of the sequences, which the call writes there
+ * with small kernels (no host buffer outlives the call).  The attention
+ * grid takes the sequences longest first.  The tile counters sum over the
+ * batch: vs_attn_tile_counts(ws, nseq * S, longest, cap_v, cap_s,
+ * nseq * h_q, ...).  Supported: as vs_sparse_attn_prefill, with each
+ * sequence's K/V of one head under 2 GiB and nseq * S below 2^30; the
+ * workspace is too small (VS_ERR_WORKSPACE) if sized for one sequence. */
+size_t vs_attn_varlen_workspace_bytes(int sets, int nseq, int max_len, int cap_v, int cap_s);
 vs_status vs_sparse_attn_prefill_varlen(const void* q, const void* k, const void* v, vs_dtype dt,
                                         int h_q, int h_kv, int total_n, int d, float scale,
                                         const int32_t* cu_seqlens, int nseq,

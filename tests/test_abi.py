@@ -48,6 +48,14 @@ def test_workspace_sizes():
     b = vsa.vs_attn_workspace_bytes(8, 262144, 262144, 262144)
     assert 0 < a < b
     assert vsa.vs_attn_workspace_bytes(8, 0, 1, 1) == 0
+    # a packed batch holds every sequence's rows plus the sequence table
+    one = vsa.vs_attn_varlen_workspace_bytes(8, 1, 4096, 64, 128)
+    many = vsa.vs_attn_varlen_workspace_bytes(8, 16, 4096, 64, 128)
+    assert many >= vsa.vs_attn_workspace_bytes(8 * 16, 4096, 64, 128) > one > 0
+    assert vsa.vs_attn_varlen_workspace_bytes(8, 16, 4096, 64, 128) > vsa.vs_attn_workspace_bytes(8, 4096, 64, 128)
+    assert vsa.vs_attn_varlen_workspace_bytes(8, 0, 4096, 64, 128) == 0
+    assert vsa.vs_attn_varlen_workspace_bytes(0, 4, 4096, 64, 128) == 0
+    assert vsa.vs_attn_varlen_workspace_bytes(8, 4, 4096, 0, 128) == 0
 
 
 def _fake(addr=0x1000):

@@ -151,3 +151,87 @@ def test_varlen_48k_sampled():
     og = to_f64(out)[rows[:, 0], rows[:, 1]]
     lg = lse.cpu().numpy().astype(np.float64)[rows[:, 0], rows[:, 1]]
     assert_attn_close(og, lg, ro, rl, "varlen 48k")
+
+
+def _varlen_lists(rng, cu, sets, nv, ns, cap_v, cap_s, spill=0):
+    """Per-sequence random lists stacked to [nseq, sets, cap]; `spill` more
+    entries per head point past the sequence's end (the call must drop
+    them, as the oracle does)."""
+    per_seq = []
+    for s in range(len(cu) - 1):
+        ln = max(cu[s + 1] - cu[s], 1)
+        vi, vc, so, sc = _rand_lists(rng, sets, ln, min(ln, nv), min(ln, ns), cap_v=cap_v, cap_s=cap_s)
+        for h in range(sets):
+            for arr, cnt, cap in ((vi, vc, cap_v), (so, sc, cap_s)):
+                extra = min(spill, cap - cnt[h])
+                arr[h, cnt[h]:cnt[h] + extra] = ln + np.sort(rng.choice(3 * ln + 64, size=extra,
+                                                                         replace=False))
+                cnt[h] += extra
+        per_seq.append((vi, vc, so, sc))
+    return [np.stack([ps[i] for ps in per_seq]) for i in range(4)]
+
+
+def test_varlen_many_sequences_and_spilled_indices():
+    """70 sequences of 0..400 rows (several empty, several of one row), so the
+    sequence table spans more than one table write, with every list also
+    holding indices past its sequence's end."""
+    _log("case: varlen 70 sequences")
+    rng = np.random.default_rng(43)
+    hq, hkv, d = 8, 2, 128
+    lens = rng.integers(0, 401, size=70)
+    lens[[3, 17, 40]] = 0
+    lens[[5, 6, 69]] = 1
+    lens[10] = 64
+    lens[11] = 65
+    cu = [0] + np.cumsum(lens).tolist()
+    total = cu[-1]
+    q, k, v = _inputs(rng, hq, hkv, total, d, "bf16")
+    stack = _varlen_lists(rng, cu, hkv, 12, 30, cap_v=20, cap_s=40, spill=5)
+    out, lse = vsa.vs_sparse_attn_prefill_varlen(to_dev(q), to_dev(k), to_dev(v), cu,
+                                                 *[to_dev(x) for x in stack])
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_varlen(q, k, v, cu, *stack)
+    assert_attn_close(to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl, "varlen 70 seq")
+
+
+def test_varlen_workspace_reuse_and_batch_counters():
+    """One workspace serves a batch of long, densely selected sequences and
+    then a batch of shorter ones: the second result matches the oracle (no
+    stale selection survives), and the batch's tile counters equal the sums
+    of the counters of single-sequence calls on the same lists."""
+    _log("case: varlen workspace reuse")
+    rng = np.random.default_rng(44)
+    hq, hkv, d, cap_v, cap_s = 8, 2, 128, 64, 200
+    cu1 = [0, 3000, 3100, 5000]
+    cu2 = [0, 700, 1500, 1501, 2600]
+    longest = max(int(np.diff(cu1).max()), int(np.diff(cu2).max()))
+    nseq = max(len(cu1), len(cu2)) - 1
+    ws = torch.empty(vsa.vs_attn_varlen_workspace_bytes(hkv, nseq, longest, cap_v, cap_s),
+                     dtype=torch.uint8, device="cuda")
+    for it, (cu, nv, ns) in enumerate(((cu1, 64, 199), (cu2, 10, 25))):
+        total = cu[-1]
+        q, k, v = _inputs(rng, hq, hkv, total, d, "bf16")
+        stack = _varlen_lists(rng, cu, hkv, nv, ns, cap_v=cap_v, cap_s=cap_s)
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        out, lse = vsa.vs_sparse_attn_prefill_varlen(qd, kd, vd, cu, *[to_dev(x) for x in stack],
+                                                     workspace=ws)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attn_varlen(q, k, v, cu, *stack)
+        assert_attn_close(to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl, f"varlen reuse {it}")
+        ns_ = len(cu) - 1
+        got = vsa.vs_attn_tile_counts(ws, ns_ * hkv, int(np.diff(cu).max()), cap_v, cap_s, ns_ * hq)
+        want = [0, 0]
+        for s in range(ns_):
+            a, b = cu[s], cu[s + 1]
+            if a == b:
+                continue
+            sws = torch.empty(vsa.vs_attn_workspace_bytes(hkv, b - a, cap_v, cap_s), dtype=torch.uint8,
+                              device="cuda")
+            vsa.vs_sparse_attn_prefill(qd[:, a:b].contiguous(), kd[:, a:b].contiguous(),
+                                       vd[:, a:b].contiguous(), *[to_dev(x[s]) for x in stack],
+                                       workspace=sws)
+            c = vsa.vs_attn_tile_counts(sws, hkv, b - a, cap_v, cap_s, hq)
+            want[0] += c[0]
+            want[1] += c[1]
+            assert c[2:] == got[2:]
+        assert list(got[:2]) == want, (got, want)

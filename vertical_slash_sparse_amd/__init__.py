@@ -38,7 +38,8 @@ VS_VERTICAL, VS_SLASH = 0, 1
 
 _SYMBOLS = ("vs_index", "vs_select_workspace_bytes", "vs_select", "vs_select_threshold",
             "vs_select_both_workspace_bytes", "vs_select_both",
-            "vs_attn_workspace_bytes", "vs_aggregate_workspace_bytes", "vs_attn_aggregate",
+            "vs_attn_workspace_bytes", "vs_attn_varlen_workspace_bytes",
+            "vs_aggregate_workspace_bytes", "vs_attn_aggregate",
             "vs_sparse_attn_prefill", "vs_sparse_attn_prefill_qh", "vs_sparse_attn_prefill_varlen",
             "vs_attn_tile_counts", "vs_block_workspace_bytes",
             "vs_block_discover", "vs_block_attn_workspace_bytes", "vs_block_attn_prefill",
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.vs_attn_aggregate.restype = i32
         L.vs_attn_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.vs_attn_workspace_bytes.restype = sz
+        L.vs_attn_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.vs_attn_varlen_workspace_bytes.restype = sz
         L.vs_sparse_attn_prefill.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P, i32, P, P,
                                              i32, P, P, P, sz, P]
         L.vs_sparse_attn_prefill.restype = i32
@@ -227,6 +230,12 @@ def vs_select(logit: torch.Tensor, kind: int, mass: float, cap: int, idx: torch.
 
 def vs_attn_workspace_bytes(h_kv: int, n: int, cap_v: int, cap_s: int) -> int:
     return int(lib().vs_attn_workspace_bytes(h_kv, n, cap_v, cap_s))
+
+
+def vs_attn_varlen_workspace_bytes(sets: int, nseq: int, max_len: int, cap_v: int, cap_s: int) -> int:
+    """Workspace bytes of a packed batch: nseq sequences of at most max_len
+    positions, `sets` index-set rows each."""
+    return int(lib().vs_attn_varlen_workspace_bytes(sets, nseq, max_len, cap_v, cap_s))
 
 
 def vs_select_both_workspace_bytes(heads: int, n: int) -> int:
@@ -395,7 +404,7 @@ def vs_sparse_attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Ten
     cap_v, cap_s = v_idx.shape[2], s_off.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     max_len = max([int(cu_seqlens[i + 1]) - int(cu_seqlens[i]) for i in range(nseq)] + [1])
-    need = vs_attn_workspace_bytes(sets, max_len, cap_v, cap_s)
+    need = vs_attn_varlen_workspace_bytes(sets, max(nseq, 1), max_len, cap_v, cap_s)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)

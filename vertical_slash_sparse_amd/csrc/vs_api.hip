@@ -2,6 +2,7 @@
 // checks, workspace sizing, launches.  Everything that can be checked on the
 // host is checked before anything is enqueued; nothing here allocates,
 // frees or synchronises except vs_attn_tile_counts, which reads counters back.
+#include <limits.h>
 #include <math.h>
 
 #include "vs.h"
@@ -177,21 +178,19 @@ vs_status vs_sparse_attn_prefill_varlen(const void* q, const void* k, const void
   }
   if ((long long)max_len * d * (dt == VS_F32 ? 4 : 2) >= (1LL << 31)) return VS_ERR_UNSUPPORTED;
   const int sets = sets_per_query_head ? h_q : h_kv;
-  if (ws_bytes < vs_attn_workspace_bytes(sets, max_len, cap_v, cap_s)) return VS_ERR_WORKSPACE;
-  AttnLayout lay;
-  lay.kvdiv = sets_per_query_head ? h_q / h_kv : 1;
-  lay.hstride = total_n;
-  for (int s = 0; s < nseq; ++s) {
-    const int len = cu_seqlens[s + 1] - cu_seqlens[s];
-    if (len == 0) continue;
-    lay.row0 = cu_seqlens[s];
-    const size_t so = (size_t)s * sets;
-    const hipError_t e = launch_attn(q, k, v, dt == VS_F32, h_q, sets, len, d, scale,
-                                     v_idx + so * cap_v, v_cnt + so, cap_v, s_off + so * cap_s,
-                                     s_cnt + so, cap_s, out, lse, ws, stream, lay);
-    if (e != hipSuccess) return VS_ERR_HIP;
-  }
-  return VS_OK;
+  if ((long long)nseq * sets > INT_MAX / 2) return VS_ERR_UNSUPPORTED;
+  if (ws_bytes < vs_attn_varlen_workspace_bytes(sets, nseq, max_len, cap_v, cap_s))
+    return VS_ERR_WORKSPACE;
+  return from_hip(launch_attn_varlen(q, k, v, dt == VS_F32, h_q, sets,
+                                     sets_per_query_head ? h_q / h_kv : 1, total_n, d, scale,
+                                     cu_seqlens, nseq, max_len, v_idx, v_cnt, cap_v, s_off, s_cnt,
+                                     cap_s, out, lse, ws, stream));
+}
+
+size_t vs_attn_varlen_workspace_bytes(int sets, int nseq, int max_len, int cap_v, int cap_s) {
+  if (sets <= 0 || nseq <= 0 || max_len < 0 || cap_v < 1 || cap_s < 1) return 0;
+  if ((long long)nseq * sets > INT_MAX / 2) return 0;
+  return AttnWsLayout(nseq * sets, max_len, cap_v, cap_s, attn_varlen_table_ints(nseq)).total;
 }
 
 size_t vs_aggregate_workspace_bytes(int h_kv, int n) {

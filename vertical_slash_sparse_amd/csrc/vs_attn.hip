@@ -41,6 +41,7 @@
 #include <climits>
 
 #include <type_traits>
+#include <vector>
 
 #include "vs_common.h"
 #include "vs_internal.h"
@@ -98,12 +99,29 @@ __global__ void ws_clear_kernel(uint32_t* bitO, uint32_t* bitV, size_t nwords,
   if (blockIdx.x == 0 && threadIdx.x < 4) stats[threadIdx.x] = 0ull;
 }
 
+// A packed batch's rows: sequence r / sets has lens[r / sets] positions, and
+// only the words its tiles can read are cleared (pads, then its bitmap).
+__global__ void ws_clear_rows_kernel(uint32_t* bitO, uint32_t* bitV, int stride,
+                                     const int* __restrict__ lens, int sets,
+                                     unsigned long long* stats) {
+  const int r = blockIdx.x;
+  const int nw = min(kPrePad + (lens[r / sets] + 31) / 32 + kPostPad, stride);
+  for (int w = threadIdx.x; w < nw; w += blockDim.x) {
+    bitO[(size_t)r * stride + w] = 0u;
+    bitV[(size_t)r * stride + w] = 0u;
+  }
+  if (r == 0 && threadIdx.x < 4) stats[threadIdx.x] = 0ull;
+}
+
+// lens (packed batch) null: every row covers positions [0, n)
 __global__ void ws_setbits_kernel(const int32_t* __restrict__ v_idx, const int32_t* __restrict__ v_cnt,
                                   int cap_v, const int32_t* __restrict__ s_off,
                                   const int32_t* __restrict__ s_cnt, int cap_s, int n,
+                                  const int* __restrict__ lens, int sets,
                                   uint32_t* bitO, uint32_t* bitV, int stride) {
-  const int g = blockIdx.y;
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int g = blockIdx.x;
+  const int t = blockIdx.y * blockDim.x + threadIdx.x;
+  if (lens) n = lens[g / sets];
   const int cv = min(max(v_cnt[g], 0), cap_v);
   const int cs = min(max(s_cnt[g], 0), cap_s);
   if (t < cv) {
@@ -122,9 +140,12 @@ __global__ __launch_bounds__(1024) void ws_scan_kernel(const uint32_t* __restric
                                                        int stride, int words, uint32_t* prefO,
                                                        int32_t* cleanO, int cap_s,
                                                        int32_t* cleanV, int cap_v,
-                                                       int32_t* counts) {
+                                                       int32_t* counts,
+                                                       const int* __restrict__ lens, int sets) {
   __shared__ int sh[17];
   const int g = blockIdx.x, tid = threadIdx.x;
+  const size_t prow = (size_t)g * (words + 1);  // this row's prefix counts
+  if (lens) words = (lens[g / sets] + 31) / 32;
   const uint32_t* bo = bitO + (size_t)g * stride + kPrePad;
   const uint32_t* bv = bitV + (size_t)g * stride + kPrePad;
   const int per = (words + 1023) / 1024;
@@ -137,7 +158,7 @@ __global__ __launch_bounds__(1024) void ws_scan_kernel(const uint32_t* __restric
   int to, tv;
   int ro = block_excl_scan<1024>(co, &to, sh);
   int rv = block_excl_scan<1024>(cv, &tv, sh);
-  uint32_t* pf = prefO + (size_t)g * (words + 1);
+  uint32_t* pf = prefO + prow;
   int32_t* lo = cleanO + (size_t)g * cap_s;
   int32_t* lv = cleanV + (size_t)g * cap_v;
   for (int w = w0; w < w1; ++w) {
@@ -224,6 +245,13 @@ struct AttnParams {
   int kvdiv;
   long long hstride;
   long long row0;
+  // A packed batch in one launch (seq_tab null otherwise): the sequences in
+  // workgroup order (longest first) as five int arrays of nseq + 1 entries,
+  // seq_tab[0..]: first workgroup of each (then the grid size), [1]: its
+  // length, [2]: its first row, [3]: its index s in the caller's lists, whose
+  // set heads use workspace rows s * hkv .. s * hkv + hkv - 1.
+  const int* seq_tab;
+  int nseq;
 };
 
 template <bool F32>
@@ -303,24 +331,41 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, ql = lane & 31;
   const int wave = wave_uniform(tid >> 6);  // keep everything derived from it in SGPRs
-  const int n = p.n;
+  int n = p.n, nblocks = p.nblocks, bid = blockIdx.x, wrow0 = 0;
+  long long row0 = p.row0;
+  if (p.seq_tab) {  // the sequence of this workgroup: the last one starting at or before it
+    const int* tw = p.seq_tab;
+    int lo = 0, hi = p.nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ldc(tw, mid) <= bid) lo = mid;
+      else hi = mid - 1;
+    }
+    const int stride = p.nseq + 1;
+    bid -= ldc(tw, lo);
+    n = ldc(tw, stride + lo);
+    row0 = ldc(tw, 2 * stride + lo);
+    wrow0 = ldc(tw, 3 * stride + lo) * p.hkv;
+    nblocks = (n + p.bmp - 1) / p.bmp;
+  }
   // block -> (KV head, head split, query block); consecutive blocks go to
   // different XCDs, so head g lands on XCD g and its K/V stays in that L2
-  const int g = blockIdx.x % p.hkv;
-  const int rest = blockIdx.x / p.hkv;
+  const int g = bid % p.hkv;
+  const int wr = wrow0 + g;  // the workspace row of set head g's index sets
+  const int rest = bid / p.hkv;
   const int split = rest % p.nsplit;
-  const int b = p.nblocks - 1 - rest / p.nsplit;  // longest causal rows first
+  const int b = nblocks - 1 - rest / p.nsplit;  // longest causal rows first
   const int i0 = b * p.bmp;
   const int i1 = min(i0 + p.bmp, n) - 1;
   const int head = g * p.group + split * p.hpw + (wave % p.hpw);
   const int i0w = i0 + 32 * (wave / p.hpw);
   const int qrow = i0w + ql;
   const bool wave_rows = i0w < n;
-  const size_t kv_head = (size_t)(g / p.kvdiv) * p.hstride + p.row0;  // first K/V row of the sequence
+  const size_t kv_head = (size_t)(g / p.kvdiv) * p.hstride + row0;  // first K/V row of the sequence
 
-  const uint32_t* bo = p.bitO + (size_t)g * p.stride + kPrePad;
-  const uint32_t* bv = p.bitV + (size_t)g * p.stride + kPrePad;
-  const uint32_t* pfo = p.prefO + (size_t)g * (p.words + 1);
+  const uint32_t* bo = p.bitO + (size_t)wr * p.stride + kPrePad;
+  const uint32_t* bv = p.bitV + (size_t)wr * p.stride + kPrePad;
+  const uint32_t* pfo = p.prefO + (size_t)wr * (p.words + 1);
   // number of selected offsets below x (0 <= x <= n)
   auto prefix = [&](int x) -> int {
     const int w = x >> 5, sh = x & 31;
@@ -338,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   // Q^T fragments (B operand): lane holds row qrow, head dims 16s + 8*half .. +7
   bf16x8 qf[KS];
   {
-    const size_t ro = ((size_t)head * p.hstride + p.row0 + min(qrow, n - 1)) * D;
+    const size_t ro = ((size_t)head * p.hstride + row0 + min(qrow, n - 1)) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 raw = load8<F32>(p.q, ro + 16 * s + 8 * half);
@@ -809,11 +854,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     // ascending key order.  Cluster ranges are disjoint (clusters are split
     // wherever neighbouring offsets differ by more than bmp + 63), so the list
     // is their concatenation; it is built in LDS windows of kListCap tiles.
-    const int32_t* clo = p.clLo + (size_t)g * p.cap_s;
-    const int32_t* chi = p.clHi + (size_t)g * p.cap_s;
+    const int32_t* clo = p.clLo + (size_t)wr * p.cap_s;
+    const int32_t* chi = p.clHi + (size_t)wr * p.cap_s;
     int ncb;  // clusters whose smallest offset is at most i1
     {
-      const int ncl = ldc(p.counts, 4 * g + 2);
+      const int ncl = ldc(p.counts, 4 * wr + 2);
       int lo = 0, hi = ncl;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -827,9 +872,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     // every one of them is active, in the short last block they are tested
     auto cluster_tiles = [&](int j, int& tlo, int& thi) {
       const int c = ncb - 1 - j;
-      tlo = max(0, i0 - p.clHi[(size_t)g * p.cap_s + c]) / kBN;
-      thi = (i1 - p.clLo[(size_t)g * p.cap_s + c]) / kBN;
-      if (j > 0) tlo = max(tlo, (i1 - p.clLo[(size_t)g * p.cap_s + c + 1]) / kBN + 1);
+      tlo = max(0, i0 - chi[c]) / kBN;
+      thi = (i1 - clo[c]) / kBN;
+      if (j > 0) tlo = max(tlo, (i1 - clo[c + 1]) / kBN + 1);
     };
     auto active_count = [&](int tlo, int thi) -> int {
       if (!partial) return max(0, thi - tlo + 1);
@@ -846,7 +891,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     auto floor_div = [](int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); };
     auto cluster_full = [&](int j, int tlo, int thi, int& f0, int& f1) {
       const int c = ncb - 1 - j;
-      const int lo = p.clLo[(size_t)g * p.cap_s + c], hi = p.clHi[(size_t)g * p.cap_s + c];
+      const int lo = clo[c], hi = chi[c];
       f0 = thi + 1;
       f1 = thi;
       if (prefix(hi + 1) - prefix(lo) != hi - lo + 1) return;
@@ -989,10 +1034,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     }
 
     // ---- gathered tiles: selected columns in no active tile, 64 per tile
-    const int32_t* cv = p.cleanV + (size_t)g * p.cap_v;
+    const int32_t* cv = p.cleanV + (size_t)wr * p.cap_v;
     int total_v;
     {
-      const int nv = ldc(p.counts, 4 * g + 1);
+      const int nv = ldc(p.counts, 4 * wr + 1);
       int lo = 0, hi = nv;  // columns <= i1
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -1091,7 +1136,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if constexpr (F32) {
     if (wave_rows && qrow < n) {
-      const size_t ro = ((size_t)head * p.hstride + p.row0 + qrow) * D;
+      const size_t ro = ((size_t)head * p.hstride + row0 + qrow) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -1127,11 +1172,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(ob + r * ROWB + 16 * (c ^ (r & (OCH - 1))));
       if (wave_rows && i0w + r < n)
         *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) +
-                                  ((size_t)head * p.hstride + p.row0 + i0w + r) * D + 8 * c) = val;
+                                  ((size_t)head * p.hstride + row0 + i0w + r) * D + 8 * c) = val;
     }
   }
   if (wave_rows && qrow < n && half == 0 && p.lse)
-    p.lse[(size_t)head * p.hstride + p.row0 + qrow] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -__builtin_inff();
+    p.lse[(size_t)head * p.hstride + row0 + qrow] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -__builtin_inff();
   if (tid == 0 && p.stats) {
     atomicAdd(&p.stats[0], (unsigned long long)n_dense);
     atomicAdd(&p.stats[1], (unsigned long long)n_gath);
@@ -1147,12 +1192,25 @@ int attn_query_rows_per_block(int group) {
   return 32 * kWaves;
 }
 
-hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, int h_q, int h_kv,
-                       int n, int d, float scale, const int32_t* v_idx, const int32_t* v_cnt,
-                       int cap_v, const int32_t* s_off, const int32_t* s_cnt, int cap_s, void* out,
-                       float* lse, void* ws, hipStream_t stream, const AttnLayout& lay) {
-  const AttnWsLayout L(h_kv, n, cap_v, cap_s);
-  char* base = static_cast<char*>(ws);
+namespace {
+
+// A packed batch as one launch: the device sequence table and, per sequence
+// in the caller's order, its length (both inside the workspace).
+struct Packed {
+  const int* tab = nullptr;   // AttnParams::seq_tab (null: one sequence)
+  const int* lens = nullptr;  // [nseq] lengths, caller order
+  int nrun = 0;               // non-empty sequences, in the table's order
+  int sets = 1;               // index-set rows per sequence
+  long long wgs = 0;          // workgroups of the attention launch
+};
+
+// tile build over `rows` index-set rows (positions below n, or below their
+// sequence's length) and the attention launch
+hipError_t run_attn(const void* q, const void* k, const void* v, bool f32, int h_q, int h_kv,
+                    int rows, int n, int d, float scale, const int32_t* v_idx,
+                    const int32_t* v_cnt, int cap_v, const int32_t* s_off, const int32_t* s_cnt,
+                    int cap_s, void* out, float* lse, const AttnWsLayout& L, char* base,
+                    hipStream_t stream, const AttnLayout& lay, const Packed& pk) {
   uint32_t* bitO = reinterpret_cast<uint32_t*>(base + L.off_bitO);
   uint32_t* bitV = reinterpret_cast<uint32_t*>(base + L.off_bitV);
   uint32_t* prefO = reinterpret_cast<uint32_t*>(base + L.off_prefO);
@@ -1168,17 +1226,23 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
   const int nsplit = group / hpw;           // workgroups sharing one block of a group
   const int bmp = 32 * (kWaves / hpw);      // query positions per workgroup
 
-  const size_t nwords = (size_t)h_kv * L.stride;
-  hipLaunchKernelGGL(ws_clear_kernel, dim3((unsigned)std::min<size_t>((nwords + 255) / 256, 2048)),
-                     dim3(256), 0, stream, bitO, bitV, nwords, stats);
+  if (pk.tab) {
+    hipLaunchKernelGGL(ws_clear_rows_kernel, dim3((unsigned)rows), dim3(256), 0, stream, bitO,
+                       bitV, L.stride, pk.lens, pk.sets, stats);
+  } else {
+    const size_t nwords = (size_t)rows * L.stride;
+    hipLaunchKernelGGL(ws_clear_kernel, dim3((unsigned)std::min<size_t>((nwords + 255) / 256, 2048)),
+                       dim3(256), 0, stream, bitO, bitV, nwords, stats);
+  }
   const int capm = std::max(cap_v, cap_s);
-  hipLaunchKernelGGL(ws_setbits_kernel, dim3((unsigned)((capm + 255) / 256), (unsigned)h_kv),
-                     dim3(256), 0, stream, v_idx, v_cnt, cap_v, s_off, s_cnt, cap_s, n, bitO, bitV,
-                     L.stride);
-  hipLaunchKernelGGL(ws_scan_kernel, dim3((unsigned)h_kv), dim3(1024), 0, stream, bitO, bitV,
-                     L.stride, L.words, prefO, cleanO, cap_s, cleanV, cap_v, counts);
+  hipLaunchKernelGGL(ws_setbits_kernel, dim3((unsigned)rows, (unsigned)((capm + 255) / 256)),
+                     dim3(256), 0, stream, v_idx, v_cnt, cap_v, s_off, s_cnt, cap_s, n, pk.lens,
+                     pk.sets, bitO, bitV, L.stride);
+  hipLaunchKernelGGL(ws_scan_kernel, dim3((unsigned)rows), dim3(1024), 0, stream, bitO, bitV,
+                     L.stride, L.words, prefO, cleanO, cap_s, cleanV, cap_v, counts, pk.lens,
+                     pk.sets);
   // offsets closer than bmp + 64 reach one contiguous run of 64-key tiles
-  hipLaunchKernelGGL(ws_cluster_kernel, dim3((unsigned)h_kv), dim3(1024), 0, stream, cleanO,
+  hipLaunchKernelGGL(ws_cluster_kernel, dim3((unsigned)rows), dim3(1024), 0, stream, cleanO,
                      cap_s, bmp + kBN - 1, clLo, clHi, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -1214,7 +1278,11 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
   prm.kvdiv = lay.kvdiv;
   prm.hstride = lay.hstride ? lay.hstride : n;
   prm.row0 = lay.row0;
-  const dim3 grid((unsigned)((long long)prm.nblocks * h_kv * nsplit));
+  prm.seq_tab = pk.tab;
+  prm.nseq = pk.nrun;
+  const long long wgs = pk.tab ? pk.wgs : (long long)prm.nblocks * h_kv * nsplit;
+  if (wgs <= 0) return hipSuccess;
+  const dim3 grid((unsigned)wgs);
   // a caller that knows most tiles are full (every offset selected) takes
   // the instantiation that skips their masks
   const bool dense = lay.full_tiles;
@@ -1236,6 +1304,84 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
     }
   }
   return hipGetLastError();
+}
+
+// copies up to kTabChunk ints from the kernel's arguments into device memory,
+// so the sequence table needs no host buffer that outlives the call
+constexpr int kTabChunk = 240;
+struct TabChunk {
+  int v[kTabChunk];
+};
+__global__ void ws_table_kernel(int* dst, int cnt, TabChunk c) {
+  if ((int)threadIdx.x < cnt) dst[threadIdx.x] = c.v[threadIdx.x];
+}
+
+}  // namespace
+
+hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, int h_q, int h_kv,
+                       int n, int d, float scale, const int32_t* v_idx, const int32_t* v_cnt,
+                       int cap_v, const int32_t* s_off, const int32_t* s_cnt, int cap_s, void* out,
+                       float* lse, void* ws, hipStream_t stream, const AttnLayout& lay) {
+  const AttnWsLayout L(h_kv, n, cap_v, cap_s);
+  return run_attn(q, k, v, f32, h_q, h_kv, h_kv, n, d, scale, v_idx, v_cnt, cap_v, s_off, s_cnt,
+                  cap_s, out, lse, L, static_cast<char*>(ws), stream, lay, Packed());
+}
+
+int attn_varlen_table_ints(int nseq) { return 5 * (nseq + 1); }
+
+hipError_t launch_attn_varlen(const void* q, const void* k, const void* v, bool f32, int h_q,
+                              int sets, int kvdiv, int total_n, int d, float scale,
+                              const int32_t* cu_seqlens, int nseq, int max_len,
+                              const int32_t* v_idx, const int32_t* v_cnt, int cap_v,
+                              const int32_t* s_off, const int32_t* s_cnt, int cap_s, void* out,
+                              float* lse, void* ws, hipStream_t stream) {
+  const AttnWsLayout L(nseq * sets, max_len, cap_v, cap_s, attn_varlen_table_ints(nseq));
+  char* base = static_cast<char*>(ws);
+  const int group = h_q / sets;
+  const int hpw = heads_per_block(group);
+  const int nsplit = group / hpw;
+  const int bmp = 32 * (kWaves / hpw);
+  // the table: non-empty sequences longest first (their last query blocks
+  // carry the most keys), as workgroup starts, lengths, first rows and
+  // indices, each nrun + 1 ints; then every sequence's length
+  std::vector<int> order;
+  for (int s = 0; s < nseq; ++s)
+    if (cu_seqlens[s + 1] > cu_seqlens[s]) order.push_back(s);
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+    return cu_seqlens[x + 1] - cu_seqlens[x] > cu_seqlens[y + 1] - cu_seqlens[y];
+  });
+  const int nrun = (int)order.size();
+  std::vector<int> tab(4 * (nrun + 1) + nseq, 0);
+  long long wg = 0;
+  for (int i = 0; i < nrun; ++i) {
+    const int s = order[i], len = cu_seqlens[s + 1] - cu_seqlens[s];
+    tab[i] = (int)wg;
+    tab[(nrun + 1) + i] = len;
+    tab[2 * (nrun + 1) + i] = cu_seqlens[s];
+    tab[3 * (nrun + 1) + i] = s;
+    wg += (long long)((len + bmp - 1) / bmp) * sets * nsplit;
+  }
+  if (wg >= (1LL << 31)) return hipErrorInvalidValue;
+  tab[nrun] = (int)wg;
+  for (int s = 0; s < nseq; ++s) tab[4 * (nrun + 1) + s] = cu_seqlens[s + 1] - cu_seqlens[s];
+  int* dtab = reinterpret_cast<int*>(base + L.off_tab);
+  for (size_t at = 0; at < tab.size(); at += kTabChunk) {
+    TabChunk c;
+    const int cnt = (int)std::min<size_t>(kTabChunk, tab.size() - at);
+    std::copy(tab.begin() + at, tab.begin() + at + cnt, c.v);
+    hipLaunchKernelGGL(ws_table_kernel, dim3(1), dim3(256), 0, stream, dtab + at, cnt, c);
+  }
+  Packed pk;
+  pk.tab = dtab;
+  pk.lens = dtab + 4 * (nrun + 1);
+  pk.nrun = nrun;
+  pk.sets = sets;
+  pk.wgs = wg;
+  AttnLayout lay;
+  lay.kvdiv = kvdiv;
+  lay.hstride = total_n;
+  return run_attn(q, k, v, f32, h_q, sets, nseq * sets, max_len, d, scale, v_idx, v_cnt, cap_v,
+                  s_off, s_cnt, cap_s, out, lse, L, base, stream, lay, pk);
 }
 
 hipError_t launch_attn_blocks(const void* q, const void* k, const void* v, bool f32, int h_q,

@@ -20,8 +20,10 @@ struct AttnWsLayout {
   int words;        // bitmap words covering positions [0, n)
   int stride;       // words per head in a bitmap array (pads included)
   size_t off_bitO, off_bitV, off_prefO, off_cleanO, off_cleanV, off_clLo, off_clHi, off_counts,
-      off_stats, total;
-  AttnWsLayout(int h_kv, int n, int cap_v, int cap_s) {
+      off_stats, off_tab, total;
+  // h_kv rows of index sets over positions [0, n); tab_ints more ints hold a
+  // packed batch's sequence table
+  AttnWsLayout(int h_kv, int n, int cap_v, int cap_s, int tab_ints = 0) {
     words = (n + 31) / 32;
     stride = kPrePad + words + kPostPad;
     size_t o = 0;
@@ -35,6 +37,7 @@ struct AttnWsLayout {
     off_clHi = take(sizeof(int32_t) * (size_t)h_kv * cap_s);
     off_counts = take(sizeof(int32_t) * 4 * (size_t)h_kv);
     off_stats = take(sizeof(unsigned long long) * 4);
+    off_tab = take(sizeof(int32_t) * (size_t)tab_ints);
     total = o;
   }
 };
@@ -74,6 +77,18 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, bool f32, in
                        int cap_v, const int32_t* s_off, const int32_t* s_cnt, int cap_s, void* out,
                        float* lse, void* ws, hipStream_t stream,
                        const AttnLayout& lay = AttnLayout());
+
+// A packed batch (cu_seqlens on the host, nseq + 1 entries) in one tile
+// build and one attention launch: sets index-set heads per sequence, lists
+// [nseq][sets][cap], workspace AttnWsLayout(nseq * sets, max_len, cap_v,
+// cap_s, attn_varlen_table_ints(nseq)).
+int attn_varlen_table_ints(int nseq);
+hipError_t launch_attn_varlen(const void* q, const void* k, const void* v, bool f32, int h_q,
+                              int sets, int kvdiv, int total_n, int d, float scale,
+                              const int32_t* cu_seqlens, int nseq, int max_len,
+                              const int32_t* v_idx, const int32_t* v_cnt, int cap_v,
+                              const int32_t* s_off, const int32_t* s_cnt, int cap_s, void* out,
+                              float* lse, void* ws, hipStream_t stream);
 
 int attn_query_rows_per_block(int group);
 
