@@ -211,6 +211,7 @@ __global__ __launch_bounds__(1024) void ws_cluster_kernel(const int32_t* __restr
 // ---------------------------------------------------------------- attention
 
 constexpr int kWaves = 8;               // waves per workgroup (two per SIMD)
+constexpr int kRotRows = 32;            // blocks per XCD between head rotations
 constexpr int kMasked = 0, kTested = 1, kNoMask = 2;  // softmax masking modes (see softmax)
 constexpr int kThreads = kWaves * 64;
 
@@ -348,11 +349,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     wrow0 = ldc(tw, 3 * stride + lo) * p.hkv;
     nblocks = (n + p.bmp - 1) / p.bmp;
   }
-  // block -> (KV head, head split, query block); consecutive blocks go to
-  // different XCDs, so head g lands on XCD g and its K/V stays in that L2
-  const int g = bid % p.hkv;
-  const int wr = wrow0 + g;  // the workspace row of set head g's index sets
+  // block -> (KV head, head split, query block).  Consecutive blocks go to
+  // different XCDs, so the workgroups an XCD runs at one time serve one head
+  // and share its K/V in that XCD's L2.  Heads can differ in work (their sets
+  // differ), so the head an XCD serves moves on every kRotRows of its blocks:
+  // each XCD then takes a slice of every head and they finish together.
   const int rest = bid / p.hkv;
+  const int g = (bid % p.hkv + rest / kRotRows) % p.hkv;
+  const int wr = wrow0 + g;  // the workspace row of set head g's index sets
   const int split = rest % p.nsplit;
   const int b = nblocks - 1 - rest / p.nsplit;  // longest causal rows first
   const int i0 = b * p.bmp;
