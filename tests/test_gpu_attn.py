@@ -85,6 +85,7 @@ CASES = [
     (513, 128, 4, 4, "bf16", 0.01, 0.01, True),   # group of 1, very sparse
     (777, 64, 6, 3, "bf16", 0.03, 0.02, False),   # group of 2
     (1000, 128, 8, 2, "bf16", 0.0, 0.0, False),   # nothing selected: all rows empty
+    (4100, 128, 12, 3, "bf16", 0.02, 0.03, False),  # 65 blocks: XCD head rotation, 3 KV heads
 ]
 
 
