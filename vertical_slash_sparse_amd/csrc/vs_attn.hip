@@ -384,9 +384,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   // block may be shorter than BMP rows, so there tiles are tested.
   const bool partial = i1 < i0 + p.bmp - 1;
 
-  // Q^T fragments (B operand): lane holds row qrow, head dims 16s + 8*half .. +7
+  // Q^T fragments (B operand): lane holds row qrow, head dims 16s + 8*half .. +7.
+  // Loaded when the first pipeline starts, together with its first K/V tiles:
+  // loads complete in order, so Q loaded up front would be waited for by the
+  // tile-list build's own loads, and a block with no tiles never needs it.
   bf16x8 qf[KS];
-  {
+  bool q_ready = false;
+  auto load_q = [&]() {
+    if (q_ready) return;
+    q_ready = true;
     const size_t ro = ((size_t)head * p.hstride + row0 + min(qrow, n - 1)) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       if (qrow >= n) raw = u32x4{0u, 0u, 0u, 0u};
       qf[s] = as_bf16x8(raw);
     }
-  }
+  };
 
   f32x16 acc[DT];
 #pragma unroll
@@ -707,6 +713,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   // picks the softmax masking (kNoMask skips the key words altogether).
   auto pipeline = [&](auto& src, int T, auto mode_c) {
     constexpr int MODE = decltype(mode_c)::value;
+    load_q();
     src.stage_first();
     uint32_t kc0 = ~0u, kc1 = ~0u;
     if constexpr (MODE != kNoMask) src.key_word_first(kc0, kc1);
