@@ -261,7 +261,10 @@ vs_status vs_attn_aggregate(const void* q, const void* k, const void* v, int h_q
  * Block means are summed in fp32 and held as a bf16 pair (about 16
  * significant bits); the scores run on the matrix cores with fp32
  * accumulation.  Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8, 16};
- * nb <= 16384.  The workspace holds the block means.  Nothing is allocated;
+ * nb <= 16384.  The workspace holds the block means (bf16 hi and lo,
+ * 4 * h_kv * nb * d bytes) and every block score of the call (fp32
+ * [h_kv][nb][nb], 134 MB at n = 131072 with 8 KV heads), which the threshold
+ * pass reads back instead of computing them again.  Nothing is allocated;
  * the calls only enqueue. */
 size_t vs_block_workspace_bytes(int h_kv, int n, int d);
 vs_status vs_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,

@@ -153,7 +153,8 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert disc(h_q=6) == vsa.VS_ERR_UNSUPPORTED
     assert disc(n=16384 * 64 + 1, wpr=513) == vsa.VS_ERR_UNSUPPORTED   # more than 16384 blocks
     assert disc(ws_bytes=16) == vsa.VS_ERR_WORKSPACE
-    assert L.vs_block_workspace_bytes(2, 1000, 128) == 2 * 2 * 16 * 128 * 2
+    # block means (bf16 hi and lo) and the fp32 block scores of every pair
+    assert L.vs_block_workspace_bytes(2, 1000, 128) == 2 * 2 * 16 * 128 * 2 + 256 * ((2 * 16 * 16 * 4 + 255) // 256)
     # vs_block_attn_prefill
     def battn(**kw):
         a = dict(q=p, k=p, v=p, dt=0, h_q=8, h_kv=2, n=1000, d=128, scale=ctypes.c_float(0.088),

@@ -75,6 +75,8 @@ VARLEN_CASES = [
     (8, 2, [0, 64, 700, 2000], 128, "bf16", True),
     (16, 2, [0, 1, 2, 3, 500], 64, "fp32", False),
     (32, 8, [0, 1024, 3072], 128, "bf16", True),
+    # 40 sequences (empty, one-row and block-edge lengths among them), per query head, fp32, group of 8
+    (16, 2, [0] + np.cumsum([0, 1, 63, 64, 65, 127, 128, 129, 0, 300] * 4).tolist(), 64, "fp32", True),
 ]
 
 

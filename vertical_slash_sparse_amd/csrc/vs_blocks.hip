@@ -27,10 +27,11 @@
 //    S^T = Kbar Q^T, so each lane owns one probe and keeps its running max
 //    and sum over blocks; passes 2 and 3 run S = Q Kbar^T, so each lane owns
 //    one block and adds the probes' normalised probabilities over its
-//    elements: pass 2 for the row's largest score, pass 3 to recompute the
-//    scores and threshold them (one fp32 product) into mask words through
-//    ballots, a word per chunk.  Keeping no score row leaves LDS to the chunk
-//    stages (32 KiB), so several workgroups share a CU.
+//    elements, keeps the row's largest score and stores every score in a
+//    workspace row; pass 3 reads the row back and thresholds it (one fp32
+//    product) into mask words through ballots, a word per chunk.  The score
+//    rows live in HBM (4 nb^2 bytes per KV head), not LDS, which keeps LDS to
+//    the chunk stages (32 KiB), so several workgroups share a CU.
 #include "vs_common.h"
 #include "vs_internal.h"
 
@@ -48,6 +49,7 @@ struct BlkParams {
   const uint16_t* klo;  // low part
   uint32_t* mask;       // [hkv][nb][wpr]
   float* score;         // optional [hkv][nb][nb]
+  float* sc;            // workspace [hkv][nb][nb]: pass 2's scores for pass 3
   int n, nb, hkv, group, skel, wpr;
   float c;              // scale * log2(e)
   float alpha;
@@ -236,10 +238,8 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
 
   // ---- passes 2 and 3: S = Q Kbar^T; lane (ql, half) holds block 32 c + ql
   // against probes 8 (e / 4) + 4 half + e % 4.  Pass 2 finds the row's
-  // largest score, pass 3 recomputes the same scores (same instructions,
-  // explicit fused multiply-adds, so the same fp32 values) and thresholds
-  // them: one chunk of 32 blocks is one mask word.  No score row is kept, so
-  // LDS holds only the two chunk stages.
+  // largest score and stores the scores; pass 3 thresholds the stored values,
+  // one chunk of 32 blocks to a mask word.
   float nm[16], wl[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -260,10 +260,16 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
     for (int e = 0; e < 16; ++e) t = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[e], p.c, nm[e])), wl[e], t);
     return half_sum(t);
   };
+  // pass 2 keeps each score in its lane's slot of the workspace row (lanes
+  // of the low half; both halves hold the same sum), where pass 3 reads it
+  // back in the same lane
+  float* const wrow = p.sc + ((size_t)g * nb + (active ? I : 0)) * nb;
   float mx = 0.f;
   sweep([&](int c, int st) {
     const float t = score_of(st);
-    if (c * 32 + ql < I) mx = fmaxf(mx, t);
+    const int J = c * 32 + ql;
+    if (J < I) mx = fmaxf(mx, t);
+    if (half == 0 && J < nb) wrow[J] = t;
   });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
@@ -271,15 +277,15 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
   const float thr = __fmul_rn(p.alpha, mx);
   uint32_t* mrow = p.mask + ((size_t)g * nb + I) * p.wpr;
   float* srow = p.score ? p.score + ((size_t)g * nb + I) * nb : nullptr;
-  sweep([&](int c, int st) {
-    const float t = score_of(st);
+  if (!active) return;
+  for (int c = 0; c < mych; ++c) {
     const int J = c * 32 + ql;
+    const float t = half == 0 && J < nb ? wrow[J] : 0.f;
     const bool keep = J == I || (J < I && t >= thr);
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);  // the mask word takes the low half
     if (lane == 0) mrow[c] = (uint32_t)bal;
     if (srow && half == 0 && J < nb) srow[J] = J < I ? t : 0.f;
-  });
-  if (!active) return;
+  }
   // words past the last chunk: only the diagonal can be set there
   for (int w = mych + lane; w < p.wpr; w += 64) mrow[w] = I / 32 == w ? 1u << (I % 32) : 0u;
   if (srow)
@@ -290,7 +296,8 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
 
 size_t block_workspace_bytes(int h_kv, int n, int d) {
   const size_t nb = (size_t)(n + kBN - 1) / kBN;
-  return 2 * align_up(sizeof(uint16_t) * (size_t)h_kv * nb * d, 256);
+  return 2 * align_up(sizeof(uint16_t) * (size_t)h_kv * nb * d, 256) +
+         align_up(sizeof(float) * (size_t)h_kv * nb * nb, 256);
 }
 
 hipError_t launch_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,
@@ -311,6 +318,8 @@ hipError_t launch_block_discover(const void* q, const void* k, int h_q, int h_kv
   prm.klo = klo;
   prm.mask = mask;
   prm.score = score;
+  prm.sc = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                    2 * align_up(sizeof(uint16_t) * (size_t)h_kv * nb * d, 256));
   prm.n = n;
   prm.nb = nb;
   prm.hkv = h_kv;
