@@ -180,10 +180,10 @@ def test_full_size_128k_sampled():
 
 
 def test_full_size_256k_discover_sampled():
-    """32/8 heads, n = 262144 (4096 blocks: the score kernel keeps 64 KiB of
-    scores plus two 16 KiB chunk stages in LDS): the whole mask against the
-    oracle's selection on the GPU's scores, sampled score rows against the
-    oracle, and sampled attention rows under the mask."""
+    """32/8 heads, n = 262144 (4096 blocks, 537 MB of score rows in the
+    workspace): the whole mask against the oracle's selection on the GPU's
+    scores, sampled score rows against the oracle, and sampled attention rows
+    under the mask."""
     _log("case: blocks 256k sampled")
     q, k, v = workloads.block_structured_inputs("blocks128k", n=262144)
     hq, n, d = q.shape
@@ -208,3 +208,26 @@ def test_full_size_256k_discover_sampled():
     og = to_f64(out)[srows[:, 0], srows[:, 1]]
     lg = lse.cpu().numpy().astype(np.float64)[srows[:, 0], srows[:, 1]]
     assert_attn_close(og, lg, ro, rl, "256k attention rows")
+
+
+def test_max_blocks_discover_sampled():
+    """The largest discovery call: nb = 16384 key blocks (n = 1048576), one KV
+    head of 4 query heads, unit Gaussian bf16 inputs.  The whole mask against
+    the oracle's selection on the GPU's scores; sampled score rows, the last
+    block among them, against the oracle."""
+    _log("case: blocks nb=16384 discover sampled")
+    rng = np.random.default_rng(12)
+    hq, hkv, d = 4, 1, 128
+    nb = 16384
+    n = nb * BS
+    q = workloads.to_bf16_bits(rng.standard_normal((hq, n, d), dtype=np.float32))
+    k = workloads.to_bf16_bits(rng.standard_normal((hkv, n, d), dtype=np.float32))
+    skel, alpha = 8, 0.5
+    mask, score = vsa.vs_block_discover(to_dev(q), to_dev(k), skel, alpha, want_score=True)
+    torch.cuda.synchronize()
+    got = score.cpu().numpy()
+    del score
+    assert np.array_equal(_mask_np(mask), oracle.block_select(got, alpha)), "nb=16384 mask"
+    rows = np.array([[0, I] for I in (1, 5000, nb - 2, nb - 1)], np.int32)
+    want = oracle.block_scores(q, k, skel, rows=rows)
+    _check_scores(got[rows[:, 0], rows[:, 1]].astype(np.float64), want, "nb=16384 score rows")
