@@ -201,8 +201,9 @@ vs_status vs_sparse_attn_prefill_varlen(const void* q, const void* k, const void
                                         const int32_t* s_cnt, int cap_s, void* out, float* lse,
                                         void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Work counters of the most recent vs_sparse_attn_prefill that used `ws`
- * (read synchronously after `stream` finishes):
+/* Work counters of the most recent vs_sparse_attn_prefill (or its _qh or
+ * _varlen form, with the arguments given there) that used `ws`, read
+ * synchronously after `stream` finishes:
  *   tiles[0] = contiguous key tiles computed, summed over KV heads and query
  *              blocks; tiles[1] = gathered vertical tiles; tiles[2] = query
  *              rows per tile (for every query head of a KV group together);
