@@ -63,9 +63,10 @@ typedef enum { VS_VERTICAL = 0, VS_SLASH = 1 } vs_kind;
  *   w2        : bf16 [2][hidden]      (row 0 vertical head, row 1 slash head)
  *   vlog,slog : fp32 [h_kv][n]        (outputs, indexed by position j)
  * First layer: bf16 MFMA with fp32 accumulation.  Second layer: fp32.
- * Supported: d == 128, hidden == 128.  n >= 1, h_kv >= 1, and each of
- * k_rope and v below 4 GiB (h_kv * n * d * 2 < 2^32 bytes); larger inputs
- * return VS_ERR_UNSUPPORTED -- call per group of KV heads instead. */
+ * Supported: d in {64, 128}; hidden a multiple of 32 from 32 to 256 (the
+ * first-layer weights stay in registers); n >= 1, h_kv >= 1, and each of
+ * k_rope and v below 4 GiB (h_kv * n * d * 2 < 2^32 bytes).  Other shapes
+ * return VS_ERR_UNSUPPORTED -- for larger inputs call per group of KV heads. */
 vs_status vs_index(const void* k_rope, const void* v, int h_kv, int n, int d, int hidden,
                    const void* w1, const void* w2, float* vlog, float* slog,
                    hipStream_t stream);
@@ -150,7 +151,12 @@ vs_status vs_select_both(const float* vlog, const float* slog, int heads, int n,
  * The lists are read into bitmaps, so entries outside [0, n) are ignored and
  * duplicates count once.  bf16 (or fp32
  * rounded to bf16) MFMA products with fp32 softmax and accumulation.
- * Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8, 16}. */
+ * `scale` may be any finite value (negative flips every score, zero makes
+ * each row the plain mean of V over S_i); NaN or infinity is VS_ERR_INVALID.
+ * Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8, 16}; each launch's
+ * grid must fit 2^32 work-items per dimension (fewer than 2^22 index-set
+ * rows, and fewer than 2^23 attention workgroups of 64 (G = 4) to 256
+ * (G = 1) query positions per set), else VS_ERR_UNSUPPORTED. */
 size_t vs_attn_workspace_bytes(int h_kv, int n, int cap_v, int cap_s);
 vs_status vs_sparse_attn_prefill(const void* q, const void* k, const void* v, vs_dtype dt,
                                  int h_q, int h_kv, int n, int d, float scale,
@@ -190,8 +196,9 @@ vs_status vs_sparse_attn_prefill_qh(const void* q, const void* k, const void* v,
  * grid takes the sequences longest first.  The tile counters sum over the
  * batch: vs_attn_tile_counts(ws, nseq * S, longest, cap_v, cap_s,
  * nseq * h_q, ...).  Supported: as vs_sparse_attn_prefill, with each
- * sequence's K/V of one head under 2 GiB and nseq * S below 2^30; the
- * workspace is too small (VS_ERR_WORKSPACE) if sized for one sequence. */
+ * sequence's K/V of one head under 2 GiB, nseq * S below 2^22 and the
+ * whole batch's attention grid below 2^23 workgroups; the workspace is too
+ * small (VS_ERR_WORKSPACE) if sized for one sequence. */
 size_t vs_attn_varlen_workspace_bytes(int sets, int nseq, int max_len, int cap_v, int cap_s);
 vs_status vs_sparse_attn_prefill_varlen(const void* q, const void* k, const void* v, vs_dtype dt,
                                         int h_q, int h_kv, int total_n, int d, float scale,
@@ -232,9 +239,9 @@ vs_status vs_attn_tile_counts(const void* ws, int h_kv, int n, int cap_v, int ca
  * workgroup (at most 512 rows) is kept in fixed point with 22 fraction bits,
  * each weight rounded to nearest (at most 2^-23 off), and the partials meet
  * through fp32 atomics, so the last bits of both may vary run to run.
- * Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8, 16}; K per head under
- * 2 GiB.  The workspace holds the list of all offsets and the attention
- * workspace. */
+ * Any finite scale.  Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8,
+ * 16}; K per head under 2 GiB; h_kv <= 65535.  The workspace holds the list
+ * of all offsets and the attention workspace. */
 size_t vs_aggregate_workspace_bytes(int h_kv, int n);
 vs_status vs_attn_aggregate(const void* q, const void* k, const void* v, int h_q, int h_kv, int n,
                             int d, float scale, void* out, float* lse, float* a_v, float* a_s,
@@ -261,8 +268,8 @@ vs_status vs_attn_aggregate(const void* q, const void* k, const void* v, int h_q
  *            scores the mask was decided on (zero for J >= I)
  * Block means are summed in fp32 and held as a bf16 pair (about 16
  * significant bits); the scores run on the matrix cores with fp32
- * accumulation.  Supported: d in {64, 128}; h_q / h_kv in {1, 2, 4, 8, 16};
- * nb <= 16384.  The workspace holds the block means (bf16 hi and lo,
+ * accumulation.  Any finite scale.  Supported: d in {64, 128}; h_q / h_kv
+ * in {1, 2, 4, 8, 16}; nb <= 16384; h_kv <= 65535.  The workspace holds the block means (bf16 hi and lo,
  * 4 * h_kv * nb * d bytes) and every block score of the call (fp32
  * [h_kv][nb][nb], 134 MB at n = 131072 with 8 KV heads), which the threshold
  * pass reads back instead of computing them again.  Nothing is allocated;
@@ -280,8 +287,8 @@ vs_status vs_block_discover(const void* q, const void* k, int h_q, int h_kv, int
  * lse = -inf.  Arguments as vs_sparse_attn_prefill, with the mask of
  * vs_block_discover (or any caller-made mask of that layout) in place of the
  * index lists.  The workspace (vs_block_attn_workspace_bytes() bytes) holds
- * work counters.  Supported: as vs_sparse_attn_prefill, with
- * n <= 2^30 - 64. */
+ * work counters.  Supported: as vs_sparse_attn_prefill (any finite scale),
+ * with n <= 2^30 - 64. */
 size_t vs_block_attn_workspace_bytes(void);
 vs_status vs_block_attn_prefill(const void* q, const void* k, const void* v, vs_dtype dt, int h_q,
                                 int h_kv, int n, int d, float scale, const uint32_t* mask,

@@ -107,9 +107,11 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert agg(d=96) == vsa.VS_ERR_UNSUPPORTED
     assert agg(ws_bytes=16) == vsa.VS_ERR_WORKSPACE
     assert L.vs_aggregate_workspace_bytes(2, 256) > L.vs_attn_workspace_bytes(2, 256, 1, 256)
-    # vs_index: shapes
-    assert L.vs_index(p, p, 8, 100, 64, 128, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED
-    assert L.vs_index(p, p, 8, 100, 128, 64, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED
+    # vs_index: shapes (d in {64, 128}; hidden a multiple of 32 up to 256)
+    assert L.vs_index(p, p, 8, 100, 96, 128, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED
+    assert L.vs_index(p, p, 8, 100, 128, 48, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED
+    assert L.vs_index(p, p, 8, 100, 128, 288, p, p, p, p, None) == vsa.VS_ERR_UNSUPPORTED
+    assert L.vs_index(p, p, 8, 100, 64, 0, p, p, p, p, None) == vsa.VS_ERR_INVALID
     assert L.vs_index(p, p, 0, 100, 128, 128, p, p, p, p, None) == vsa.VS_ERR_INVALID
     assert L.vs_index(None, p, 8, 100, 128, 128, p, p, p, p, None) == vsa.VS_ERR_INVALID
     # one KV-head tensor must fit a 32-bit byte range (8 x 2^21 x 128 x 2 B = 4 GiB)
@@ -129,8 +131,11 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert attn(h_q=24) == vsa.VS_ERR_UNSUPPORTED      # group 3
     assert attn(d=96) == vsa.VS_ERR_UNSUPPORTED
     assert attn(dt=5) == vsa.VS_ERR_INVALID
-    assert attn(scale=-1.0) == vsa.VS_ERR_INVALID
     assert attn(scale=float("nan")) == vsa.VS_ERR_INVALID
+    assert attn(scale=float("-inf")) == vsa.VS_ERR_INVALID
+    # any finite scale passes the checks (the workspace check comes later)
+    for sc in (-1.0, 0.0, -0.0, 1e-30, 12.5):
+        assert attn(scale=sc, ws_bytes=16) == vsa.VS_ERR_WORKSPACE, sc
     assert attn(cap_v=0) == vsa.VS_ERR_INVALID
     assert attn(n=0) == vsa.VS_ERR_INVALID
     assert attn(ws_bytes=16) == vsa.VS_ERR_WORKSPACE
@@ -202,3 +207,45 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         vsa.vs_index(x, x, torch.zeros(128, 256, dtype=torch.bfloat16), torch.zeros(2, 128, dtype=torch.bfloat16))
+
+
+def test_grid_limits_are_rejected_before_launch():
+    """Shapes whose launches would not fit 2^32 work-items along one grid
+    dimension return VS_ERR_UNSUPPORTED; the largest shapes that fit pass on
+    to the workspace check."""
+    L = vsa.lib()
+    p = _fake()
+
+    def attn(h_q, h_kv, n, d=64, ws_bytes=16):
+        return L.vs_sparse_attn_prefill(p, p, p, 0, h_q, h_kv, n, d, ctypes.c_float(0.1), p, p, 4,
+                                        p, p, 4, p, None, p, ws_bytes, None)
+
+    # the tile builder: one 1024-thread workgroup per index-set row
+    assert attn(1 << 22, 1 << 22, 1) == vsa.VS_ERR_UNSUPPORTED
+    assert attn((1 << 22) - 1, (1 << 22) - 1, 1) == vsa.VS_ERR_WORKSPACE
+    # the attention grid: 512 threads per (row, 64-position block) at G = 4
+    n = (1 << 23) - 1
+    assert attn(256, 64, n) == vsa.VS_ERR_UNSUPPORTED
+    assert attn(252, 63, n) == vsa.VS_ERR_WORKSPACE
+    # per-query-head sets: one set per query head, 256 positions per workgroup
+    assert L.vs_sparse_attn_prefill_qh(p, p, p, 0, 1 << 22, 1 << 22, 1, 64, ctypes.c_float(0.1), p, p, 4,
+                                       p, p, 4, p, None, p, 16, None) == vsa.VS_ERR_UNSUPPORTED
+    # packed batches: nseq * sets index-set rows
+    nseq = (1 << 22) // 8
+    cu = (ctypes.c_int32 * (nseq + 1))(*([0] * nseq + [1]))
+    assert L.vs_sparse_attn_prefill_varlen(p, p, p, 0, 32, 8, 1, 64, ctypes.c_float(0.1),
+                                           ctypes.cast(cu, ctypes.c_void_p), nseq, 0, p, p, 4, p, p, 4,
+                                           p, None, p, 1 << 40, None) == vsa.VS_ERR_UNSUPPORTED
+    nseq -= 1
+    cu = (ctypes.c_int32 * (nseq + 1))(*([0] * nseq + [1]))
+    assert L.vs_sparse_attn_prefill_varlen(p, p, p, 0, 32, 8, 1, 64, ctypes.c_float(0.1),
+                                           ctypes.cast(cu, ctypes.c_void_p), nseq, 0, p, p, 4, p, p, 4,
+                                           p, None, p, 16, None) == vsa.VS_ERR_WORKSPACE
+    # list capacities have no grid limit (the bit-setting pass strides over them)
+    assert L.vs_sparse_attn_prefill(p, p, p, 0, 32, 8, 1024, 128, ctypes.c_float(0.1), p, p, 1 << 26,
+                                    p, p, 1 << 26, p, None, p, 16, None) == vsa.VS_ERR_WORKSPACE
+    # aggregation and discovery launch h_kv along a 65535-limited dimension
+    assert L.vs_attn_aggregate(p, p, p, 65536, 65536, 16, 64, ctypes.c_float(0.1), p, p, p, p, p,
+                               1 << 40, None) == vsa.VS_ERR_UNSUPPORTED
+    assert L.vs_block_discover(p, p, 65536, 65536, 16, 64, ctypes.c_float(0.1), 8, ctypes.c_float(0.5),
+                               p, 1, None, p, 1 << 40, None) == vsa.VS_ERR_UNSUPPORTED

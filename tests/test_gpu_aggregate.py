@@ -73,6 +73,24 @@ def test_aggregate_vs_oracle(case):
     assert_attn_close(to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl, f"{case} attention")
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.3])
+def test_aggregate_any_finite_scale(scale):
+    """Any finite scale: negative, zero (uniform rows) and large."""
+    _log(f"case: aggregate scale {scale}")
+    rng = np.random.default_rng(55)
+    hq, hkv, n, d = 8, 2, 500, 128
+    q, k, v = _bf16_inputs(rng, hq, hkv, n, d)
+    out, lse, a_v, a_s = vsa.vs_attn_aggregate(to_dev(q), to_dev(k), to_dev(v), scale=scale)
+    torch.cuda.synchronize()
+    r_v, r_s = oracle.aggregate(q, k, scale=scale)
+    _check_sums(a_v.cpu().numpy().astype(np.float64), r_v, f"scale {scale} a_v")
+    _check_sums(a_s.cpu().numpy().astype(np.float64), r_s, f"scale {scale} a_s")
+    soff = np.stack([np.arange(n)] * hkv).astype(np.int32)
+    ro, rl = oracle.attn(q, k, v, np.full((hkv, 1), -1, np.int32), np.zeros(hkv, np.int32), soff,
+                         np.full(hkv, n, np.int32), scale=scale)
+    assert_attn_close(to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl, f"scale {scale}")
+
+
 def test_aggregate_sums_total_group_times_n():
     """Rows of P sum to 1: each KV head's sums total G*n (4096 rows, G = 4)."""
     _log("case: aggregate totals")
@@ -102,3 +120,29 @@ def test_aggregate_uniform_rows_closed_form():
     want = 4 * (H[n] - H[:n])
     _check_sums(a_v[0].cpu().numpy().astype(np.float64), want, "uniform a_v")
     _check_sums(a_s[0].cpu().numpy().astype(np.float64), want, "uniform a_s")
+
+
+def test_aggregate32k_one_kv_head_whole():
+    """The 32K aggregation layer (32/8 heads, d = 128, n = 32768, the fixed
+    32K layer's RoPE'd inputs): every entry of a_v and a_s of one KV head,
+    drawn by seed, against the oracle over that head's 4 query heads, at the
+    tolerance above.  A diagonal's partials add at most 512 rows of 2^-23
+    rounding each per workgroup, at most 4 * 32768 * 2^-23 ~ 0.016 in all,
+    well inside 5e-3 of the diagonal sums near o = 0 (G * H_n ~ 44)."""
+    _log("case: aggregate32k one KV head")
+    q, k, v = workloads.attention_inputs("fixed32k")
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    G = hq // hkv
+    _, _, a_v, a_s = vsa.vs_attn_aggregate(to_dev(q), to_dev(k), to_dev(v))
+    torch.cuda.synchronize()
+    g = int(np.random.default_rng(32).integers(hkv))
+    gv = a_v[g].cpu().numpy().astype(np.float64)
+    gs = a_s[g].cpu().numpy().astype(np.float64)
+    del a_v, a_s
+    _log(f"case: aggregate32k oracle on KV head {g}")
+    r_v, r_s = oracle.aggregate(q[G * g:G * (g + 1)], k[g:g + 1])
+    _check_sums(gv, r_v[0], f"aggregate32k a_v[{g}]")
+    _check_sums(gs, r_s[0], f"aggregate32k a_s[{g}]")
+    np.testing.assert_allclose(gv.sum(), G * n, rtol=REL)
+    np.testing.assert_allclose(gs.sum(), G * n, rtol=REL)

@@ -15,7 +15,7 @@ import torch
 import oracle
 import vertical_slash_sparse_amd as vsa
 import workloads
-from tests.util import assert_attn_close, sample_rows, to_dev, to_f64
+from tests.util import assert_attn_close, sample_rows, stratified_rows, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -148,6 +148,64 @@ def test_index_list_contract():
     assert_attn_close(out, lse, ro, rl, "contract")
 
 
+SCALES = [-0.125, 0.0, -0.0, 0.5, -2.0]
+
+
+@pytest.mark.parametrize("scale", SCALES, ids=[repr(s) for s in SCALES])
+def test_any_finite_scale(scale):
+    """The softmax scale may be any finite value: negative (every score's
+    sign flips), zero (each row is the mean of V over its set) or large.
+    Vertical-slash and block-sparse attention against the oracle at that
+    scale."""
+    _log(f"case: scale {scale}")
+    rng = np.random.default_rng(int(abs(scale) * 1000) + 3)
+    hq, hkv, n, d = 8, 2, 700, 128
+    q, k, v = _inputs(rng, hq, hkv, n, d, "bf16")
+    lists = _random_sets(rng, hkv, n, 0.05, 0.1)
+    out, lse = _run_gpu(q, k, v, *lists, scale=scale)
+    ro, rl = oracle.attn(q, k, v, *lists, scale=scale)
+    assert_attn_close(out, lse, ro, rl, f"scale {scale}")
+    nb = (n + 63) // 64
+    dense = rng.random((hkv, nb, nb)) < 0.4
+    dense[:, np.arange(nb), np.arange(nb)] = True
+    wpr = oracle.words_per_row(nb)
+    padded = np.zeros((hkv, nb, wpr * 32), bool)
+    padded[..., :nb] = dense
+    mask = np.packbits(padded, axis=-1, bitorder="little").view(np.uint32).reshape(hkv, nb, wpr)
+    bo, bl = vsa.vs_block_attn_prefill(to_dev(q), to_dev(k), to_dev(v), to_dev(mask.view(np.int32)),
+                                       scale=scale)
+    torch.cuda.synchronize()
+    rbo, rbl = oracle.block_attn(q, k, v, mask, scale=scale)
+    assert_attn_close(to_f64(bo), bl.cpu().numpy().astype(np.float64), rbo, rbl, f"block scale {scale}")
+
+
+def test_long_lists_with_out_of_range_entries():
+    """Lists of 1.5 M entries per KV head (the bit-setting pass covers more
+    than 2^20 entries by striding), nearly all of them outside [0, n), with
+    the in-range ones placed far down the lists: the sets are those entries."""
+    _log("case: 1.5M-entry lists")
+    rng = np.random.default_rng(15)
+    hq, hkv, n, d = 4, 2, 3000, 64
+    q, k, v = _inputs(rng, hq, hkv, n, d, "bf16")
+    cap = 1_500_000
+    raws, cleans = [], []
+    for _ in range(2 * hkv):
+        raw = rng.integers(n, 2**31 - 1, size=cap, dtype=np.int64)
+        raw[rng.choice(cap, cap // 3, replace=False)] *= -1
+        good = rng.choice(n, 40, replace=False)
+        at = np.concatenate([[cap - 1], rng.choice(np.arange(1_100_000, cap - 1), 39, replace=False)])
+        raw[at] = good
+        raws.append(raw.astype(np.int32))
+        cleans.append(np.sort(good))
+    vraw, sraw = np.stack(raws[:hkv]), np.stack(raws[hkv:])
+    cnt = np.full(hkv, cap, np.int32)
+    out, lse = _run_gpu(q, k, v, vraw, cnt, sraw, cnt)
+    vidx, vcnt = _pad_lists(cleans[:hkv])
+    soff, scnt = _pad_lists(cleans[hkv:])
+    ro, rl = oracle.attn(q, k, v, vidx, vcnt, soff, scnt)
+    assert_attn_close(out, lse, ro, rl, "long lists")
+
+
 def test_clustered_offsets_and_gathered_columns():
     """Slash offsets in a few runs (few active tiles) plus scattered columns,
     most of which no slash tile covers, so the gathered path carries them."""
@@ -210,7 +268,7 @@ def test_fixed32k_full_size_sampled():
     q, k, v = workloads.attention_inputs("fixed32k")
     lists = workloads.small_index_sets("fixed32k")
     out, lse = _run_gpu(q, k, v, *lists)
-    rows = sample_rows(np.random.default_rng(3), 32, 32768, 24)
+    rows = stratified_rows(np.random.default_rng(3), 32, 32768)
     ro, rl = oracle.attn(q, k, v, *lists, rows=rows)
     assert_attn_close(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, "fixed32k")
 
@@ -265,7 +323,7 @@ def test_one_million_tokens_sampled():
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     out, lse = vsa.vs_sparse_attn_prefill(qd, kd, vd, to_dev(vidx), to_dev(vcnt), to_dev(soff), to_dev(scnt))
     torch.cuda.synchronize()
-    rows = sample_rows(np.random.default_rng(5), hq, n, 8)
+    rows = stratified_rows(np.random.default_rng(5), hq, n)
     ro, rl = oracle.attn(q, k, v, vidx, vcnt, soff, scnt, rows=rows)
     og = to_f64(out)[rows[:, 0], rows[:, 1]]
     lg = lse.cpu().numpy().astype(np.float64)[rows[:, 0], rows[:, 1]]

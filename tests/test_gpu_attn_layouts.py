@@ -10,7 +10,7 @@ import torch
 import oracle
 import vertical_slash_sparse_amd as vsa
 import workloads
-from tests.util import assert_attn_close, sample_rows, to_dev, to_f64
+from tests.util import assert_attn_close, sample_rows, stratified_rows, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -123,7 +123,7 @@ def test_per_query_head_sets_32k_sampled():
     out, lse = vsa.vs_sparse_attn_prefill_qh(to_dev(q), to_dev(k), to_dev(v), vi, vc, si, sc)
     torch.cuda.synchronize()
     lists = [t.cpu().numpy() for t in (vi, vc, si, sc)]
-    rows = sample_rows(rng, hq, n, per_head=5)
+    rows = stratified_rows(rng, hq, n)
     ro, rl = oracle.attn_qh(q, k, v, *lists, rows=rows)
     og = to_f64(out)[rows[:, 0], rows[:, 1]]
     lg = lse.cpu().numpy().astype(np.float64)[rows[:, 0], rows[:, 1]]
@@ -145,7 +145,7 @@ def test_varlen_48k_sampled():
     out, lse = vsa.vs_sparse_attn_prefill_varlen(to_dev(q), to_dev(k), to_dev(v), cu,
                                                  *[to_dev(x) for x in stack], per_query_head=True)
     torch.cuda.synchronize()
-    rows = sample_rows(rng, hq, total, per_head=4)
+    rows = stratified_rows(rng, hq, total)
     extra = np.array([[h, r] for h in (0, hq - 1) for r in (cu[1] - 1, cu[1], cu[2] - 1, cu[2])],
                      np.int32)
     rows = np.concatenate([rows, extra])

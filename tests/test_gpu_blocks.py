@@ -26,7 +26,7 @@ import torch
 import oracle
 import vertical_slash_sparse_amd as vsa
 import workloads
-from tests.util import assert_attn_close, sample_rows, to_dev, to_f64
+from tests.util import assert_attn_close, stratified_rows, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -172,7 +172,7 @@ def test_full_size_128k_sampled():
                      list(rng.choice(nb, 3, replace=False))], np.int32)
     want = oracle.block_scores(q, k, skel, rows=rows)
     _check_scores(got[rows[:, 0], rows[:, 1]].astype(np.float64), want, "128k score rows")
-    srows = sample_rows(rng, hq, n, per_head=6)
+    srows = stratified_rows(rng, hq, n)
     ro, rl = oracle.block_attn(q, k, v, m, rows=srows)
     og = to_f64(out)[srows[:, 0], srows[:, 1]]
     lg = lse.cpu().numpy().astype(np.float64)[srows[:, 0], srows[:, 1]]
@@ -203,7 +203,7 @@ def test_full_size_256k_discover_sampled():
                      list(rng.choice(nb, 2, replace=False))], np.int32)
     want = oracle.block_scores(q, k, skel, rows=rows)
     _check_scores(got[rows[:, 0], rows[:, 1]].astype(np.float64), want, "256k score rows")
-    srows = sample_rows(rng, hq, n, per_head=4)
+    srows = stratified_rows(rng, hq, n)
     ro, rl = oracle.block_attn(q, k, v, m, rows=srows)
     og = to_f64(out)[srows[:, 0], srows[:, 1]]
     lg = lse.cpu().numpy().astype(np.float64)[srows[:, 0], srows[:, 1]]

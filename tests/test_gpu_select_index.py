@@ -11,7 +11,7 @@ import torch
 import oracle
 import vertical_slash_sparse_amd as vsa
 import workloads
-from tests.util import INDEX_ATOL, assert_attn_close, sample_rows, to_dev, to_f64
+from tests.util import INDEX_ATOL, assert_attn_close, stratified_rows, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -111,6 +111,38 @@ def test_index_small_vs_oracle():
     assert np.abs(gs.cpu().numpy() - rs).max() <= INDEX_ATOL
 
 
+INDEX_SHAPES = [
+    # hkv, n, d, hidden
+    (2, 1000, 64, 128),
+    (3, 777, 128, 32),
+    (1, 2048 + 5, 128, 64),
+    (2, 1500, 64, 96),
+    (2, 999, 128, 160),
+    (4, 3000, 128, 256),
+    (2, 333, 64, 256),
+    (1, 31, 64, 224),
+]
+
+
+@pytest.mark.parametrize("case", INDEX_SHAPES, ids=[f"h{c[0]}-n{c[1]}-d{c[2]}-hid{c[3]}" for c in INDEX_SHAPES])
+def test_index_shapes_vs_oracle(case):
+    """Head dims 64 and 128 and hidden widths from 32 to 256 (multiples of
+    32; up to four chunks of 32 hidden units leave some waves idle, more
+    than four give a wave two chunks), weights N(0, 1/fan_in), every logit
+    against the oracle within 1e-3."""
+    hkv, n, d, hidden = case
+    _log(f"case: index shape {case}")
+    rng = np.random.default_rng(hkv * 131 + n + d + hidden)
+    k = workloads.to_bf16_bits(rng.standard_normal((hkv, n, d)))
+    v = workloads.to_bf16_bits(rng.standard_normal((hkv, n, d)))
+    w1, w2 = workloads.indexer_weights(rng, 2 * d, hidden)
+    gv, gs = vsa.vs_index(to_dev(k), to_dev(v), to_dev(w1), to_dev(w2))
+    torch.cuda.synchronize()
+    rv, rs = oracle.index(k, v, w1, w2)
+    assert np.abs(gv.cpu().numpy() - rv).max() <= INDEX_ATOL
+    assert np.abs(gs.cpu().numpy() - rs).max() <= INDEX_ATOL
+
+
 def test_indexer_workload_full_size():
     """8 KV heads x 131072 positions: sampled logits vs the oracle, then the
     selection of the GPU logits bit-exact against the oracle's selection of
@@ -146,7 +178,7 @@ def test_zipf128k_layer_sampled():
     _assert_same_selection(vi.cpu().numpy(), vc.cpu().numpy(), ri, rc, "zipf vertical")
     lists = (vi.cpu().numpy(), vc.cpu().numpy(), si.cpu().numpy(), sc.cpu().numpy())
     out, lse = to_f64(out), lse.cpu().numpy().astype(np.float64)
-    rows = sample_rows(np.random.default_rng(11), 32, w["n"], 12)
+    rows = stratified_rows(np.random.default_rng(11), 32, w["n"])
     ro, rl = oracle.attn(q, k, v, *lists, rows=rows)
     assert_attn_close(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, "zipf128k")
 
@@ -168,7 +200,7 @@ def test_clustered128k_layer_sampled():
         _assert_same_selection(gi.cpu().numpy(), gc.cpu().numpy(), ri, rc, f"clustered kind {kind}")
     lists = (vi.cpu().numpy(), vc.cpu().numpy(), si.cpu().numpy(), sc.cpu().numpy())
     out, lse = to_f64(out), lse.cpu().numpy().astype(np.float64)
-    rows = sample_rows(np.random.default_rng(12), 32, w["n"], 12)
+    rows = stratified_rows(np.random.default_rng(12), 32, w["n"])
     ro, rl = oracle.attn(q, k, v, *lists, rows=rows)
     assert_attn_close(out[rows[:, 0], rows[:, 1]], lse[rows[:, 0], rows[:, 1]], ro, rl, "clustered128k")
 

@@ -50,13 +50,46 @@ def assert_attn_close(out_gpu: np.ndarray, lse_gpu: np.ndarray, out_ref: np.ndar
         assert le.mean() <= ATOL_MEAN, f"{what}: lse mean-abs {le.mean():.3e}"
 
 
+def _edge_rows(n: int, block: int) -> list:
+    return sorted({0, 1, block - 1, block, n - block, n - 2, n - 1} & set(range(n)))
+
+
 def sample_rows(rng, hq: int, n: int, per_head: int, block: int = 64) -> np.ndarray:
     """(head, row) pairs: first and last rows, both ends of the first and last
-    query blocks, plus random rows, for every head."""
-    fixed = sorted({0, 1, block - 1, block, n - block, n - 2, n - 1} & set(range(n)))
+    query blocks, and on top of those `per_head` random rows, for every head."""
+    fixed = _edge_rows(n, block)
     rows = []
     for h in range(hq):
-        extra = rng.choice(n, size=max(per_head - len(fixed), 0), replace=False)
+        extra = rng.choice(n, size=min(per_head, n), replace=False)
         for i in sorted(set(fixed) | set(int(x) for x in extra)):
             rows.append((h, i))
     return np.array(rows, dtype=np.int32)
+
+
+def stratified_rows(rng, hq: int, n: int, strata: int = 64, per_block: int = 2,
+                    whole_blocks: int = 2, block: int = 64) -> np.ndarray:
+    """(head, row) pairs spread over the whole sequence, for full-size parity:
+    - the edge rows of sample_rows, for every head;
+    - per head, the query blocks are cut into `strata` equal runs and one
+      block is drawn from each run, `per_block` random rows of it;
+    - `whole_blocks` interior query blocks (neither the first nor the last)
+      drawn once, every row of them for every head.
+    Rows are unique and sorted by (head, row)."""
+    nb = (n + block - 1) // block
+    fixed = _edge_rows(n, block)
+    edges = np.linspace(0, nb, min(strata, nb) + 1).astype(np.int64)
+    rows = set()
+    for h in range(hq):
+        rows.update((h, i) for i in fixed)
+        for s in range(len(edges) - 1):
+            if edges[s + 1] <= edges[s]:
+                continue
+            b = int(rng.integers(edges[s], edges[s + 1]))
+            r0, r1 = b * block, min(n, (b + 1) * block)
+            take = rng.choice(np.arange(r0, r1), size=min(per_block, r1 - r0), replace=False)
+            rows.update((h, int(i)) for i in take)
+    if nb > 2 and whole_blocks > 0:
+        for b in rng.choice(np.arange(1, nb - 1), size=min(whole_blocks, nb - 2), replace=False):
+            r0, r1 = int(b) * block, min(n, (int(b) + 1) * block)
+            rows.update((h, i) for h in range(hq) for i in range(r0, r1))
+    return np.array(sorted(rows), dtype=np.int32)

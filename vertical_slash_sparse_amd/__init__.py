@@ -24,6 +24,8 @@ calls raise.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import math
 import os
 
@@ -130,6 +132,24 @@ def _stream(t: torch.Tensor, stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a wrapper with `stream` (when given) as torch's current stream, so
+    that every tensor it allocates -- outputs, workspaces, temporaries -- comes
+    from that stream's pool.  A temporary freed on return then cannot be handed
+    to work on another stream while the kernels enqueued on `stream` still
+    read or write it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _need(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -145,6 +165,7 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+@_on_stream
 def vs_index(k_rope: torch.Tensor, v: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
              vlog: torch.Tensor | None = None, slog: torch.Tensor | None = None, stream=None):
     """VSIndexer logits.  k_rope, v: bf16 [h_kv, n, d]; w1: bf16 [hidden, 2d];
@@ -190,6 +211,7 @@ def _select_outputs(fn, logit, cap, idx, count, workspace):
     return heads, n, idx, count, workspace
 
 
+@_on_stream
 def vs_select_threshold(logit: torch.Tensor, kind: int, alpha: float, cap: int,
                         idx: torch.Tensor | None = None, count: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None, stream=None):
@@ -205,6 +227,7 @@ def vs_select_threshold(logit: torch.Tensor, kind: int, alpha: float, cap: int,
     return idx, count
 
 
+@_on_stream
 def vs_select(logit: torch.Tensor, kind: int, mass: float, cap: int, idx: torch.Tensor | None = None,
               count: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
     """Cumulative-mass selection.  logit: fp32 [heads, n].  kind: VS_VERTICAL
@@ -242,6 +265,7 @@ def vs_select_both_workspace_bytes(heads: int, n: int) -> int:
     return int(lib().vs_select_both_workspace_bytes(heads, n))
 
 
+@_on_stream
 def vs_select_both(vlog: torch.Tensor, slog: torch.Tensor, mass: float, cap_v: int, cap_s: int,
                    v_idx: torch.Tensor | None = None, v_cnt: torch.Tensor | None = None,
                    s_off: torch.Tensor | None = None, s_cnt: torch.Tensor | None = None,
@@ -276,6 +300,7 @@ def vs_select_both(vlog: torch.Tensor, slog: torch.Tensor, mass: float, cap_v: i
     return v_idx, v_cnt, s_off, s_cnt
 
 
+@_on_stream
 def vs_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                            v_idx: torch.Tensor, v_cnt: torch.Tensor, s_off: torch.Tensor,
                            s_cnt: torch.Tensor, scale: float | None = None,
@@ -351,6 +376,7 @@ def _attn_common(q, k, v, out, lse, want_lse, rows):
     return dt, dev, h_q, h_kv, n, d, out, lse
 
 
+@_on_stream
 def vs_sparse_attn_prefill_qh(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               v_idx: torch.Tensor, v_cnt: torch.Tensor, s_off: torch.Tensor,
                               s_cnt: torch.Tensor, scale: float | None = None,
@@ -380,6 +406,7 @@ def vs_sparse_attn_prefill_qh(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, lse
 
 
+@_on_stream
 def vs_sparse_attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens,
                                   v_idx: torch.Tensor, v_cnt: torch.Tensor, s_off: torch.Tensor,
                                   s_cnt: torch.Tensor, per_query_head: bool = False,
@@ -422,6 +449,7 @@ def vs_aggregate_workspace_bytes(h_kv: int, n: int) -> int:
     return int(lib().vs_aggregate_workspace_bytes(h_kv, n))
 
 
+@_on_stream
 def vs_attn_aggregate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                       a_v: torch.Tensor | None = None, a_s: torch.Tensor | None = None,
@@ -479,6 +507,7 @@ def block_words_per_row(n: int) -> int:
     return ((n + BLOCK - 1) // BLOCK + 31) // 32
 
 
+@_on_stream
 def vs_block_discover(q: torch.Tensor, k: torch.Tensor, skel: int, alpha: float,
                       scale: float | None = None, mask: torch.Tensor | None = None,
                       want_score: bool = False, workspace: torch.Tensor | None = None,
@@ -514,6 +543,7 @@ def vs_block_discover(q: torch.Tensor, k: torch.Tensor, skel: int, alpha: float,
     return (mask, score) if want_score else mask
 
 
+@_on_stream
 def vs_block_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor,
                           scale: float | None = None, out: torch.Tensor | None = None,
                           lse: torch.Tensor | None = None, want_lse: bool = True,
@@ -562,6 +592,7 @@ def exported_symbols():
     return _SYMBOLS
 
 
+@_on_stream
 def vs_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
                mass: float = 0.95, cap_v: int | None = None, cap_s: int | None = None,
                scale: float | None = None, stream=None):
@@ -583,7 +614,4 @@ def vs_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tens
     ws = torch.empty(max(vs_select_both_workspace_bytes(h_kv, n), 1), dtype=torch.uint8, device=k.device)
     v_idx, v_cnt, s_off, s_cnt = vs_select_both(vlog, slog, mass, cap_v, cap_s, workspace=ws, stream=stream)
     out, lse = vs_sparse_attn_prefill(q, k, v, v_idx, v_cnt, s_off, s_cnt, scale=scale, stream=stream)
-    if stream is not None:  # the temporaries are freed on return, while `stream` may still use them
-        for t in (vlog, slog, ws):
-            t.record_stream(stream)
     return out, lse, (v_idx, v_cnt, s_off, s_cnt)

@@ -262,6 +262,12 @@ size_t aggregate_workspace_bytes(int h_kv, int n) {
   return o + AttnWsLayout(h_kv, n, 1, n).total;
 }
 
+bool aggregate_grid_fits(int h_q, int h_kv, long long n) {
+  const long long bp = agg_positions(h_q / h_kv);
+  return (n + bp - 1) / bp * h_kv * kAggThreads < (1LL << 32) &&
+         (n + 255) / 256 * 256 < (1LL << 32);
+}
+
 hipError_t launch_aggregate(const void* q, const void* k, const void* v, int h_q, int h_kv, int n,
                             int d, float scale, void* out, float* lse, float* a_v, float* a_s,
                             void* ws, hipStream_t stream) {

@@ -20,6 +20,17 @@ bool group_ok(int h_q, int h_kv) {
 
 vs_status from_hip(hipError_t e) { return e == hipSuccess ? VS_OK : VS_ERR_HIP; }
 
+// a launch of `wgs` workgroups of `threads` work-items fits one grid dimension
+bool grid_fits(long long wgs, int threads) { return wgs >= 0 && wgs * threads < kGridItems; }
+
+// The tile builder runs one workgroup per index-set row, and the attention
+// kernel one per (row, query block); both grids must fit.
+vs_status attn_grid_status(int group, int rows, long long n) {
+  if (!grid_fits(rows, kBuildThreads)) return VS_ERR_UNSUPPORTED;
+  if (!grid_fits(attn_workgroups(group, rows, n), kAttnThreads)) return VS_ERR_UNSUPPORTED;
+  return VS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -41,10 +52,10 @@ vs_status vs_index(const void* k_rope, const void* v, int h_kv, int n, int d, in
   if (!k_rope || !v || !w1 || !w2 || !vlog || !slog) return VS_ERR_INVALID;
   if (h_kv <= 0 || n <= 0 || d <= 0 || hidden <= 0) return VS_ERR_INVALID;
   if ((long long)h_kv * n > (1LL << 40)) return VS_ERR_INVALID;
-  if (d != 128 || hidden != 128) return VS_ERR_UNSUPPORTED;
+  if ((d != 64 && d != 128) || hidden % 32 || hidden > kIdxMaxHidden) return VS_ERR_UNSUPPORTED;
   // K and V are each read through one buffer resource with a 32-bit range
   if ((long long)h_kv * n * d * 2 >= (1LL << 32)) return VS_ERR_UNSUPPORTED;
-  return from_hip(launch_index(k_rope, v, h_kv, n, w1, w2, vlog, slog, stream));
+  return from_hip(launch_index(k_rope, v, h_kv, n, d, hidden, w1, w2, vlog, slog, stream));
 }
 
 size_t vs_select_workspace_bytes(int heads, int n) {
@@ -111,12 +122,13 @@ vs_status vs_sparse_attn_prefill(const void* q, const void* k, const void* v, vs
   if (h_q <= 0 || h_kv <= 0 || n <= 0 || d <= 0) return VS_ERR_INVALID;
   if (h_q % h_kv) return VS_ERR_INVALID;
   if (cap_v < 1 || cap_s < 1) return VS_ERR_INVALID;
-  if (!(scale > 0.f) || !isfinite(scale)) return VS_ERR_INVALID;
+  if (!isfinite(scale)) return VS_ERR_INVALID;
   if ((long long)n > (1LL << 30) || (long long)h_kv * n * d > (1LL << 40)) return VS_ERR_INVALID;
   if (!group_ok(h_q, h_kv)) return VS_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return VS_ERR_UNSUPPORTED;
   // one KV head must fit a 32-bit buffer range
   if ((long long)n * d * (dt == VS_F32 ? 4 : 2) >= (1LL << 31)) return VS_ERR_UNSUPPORTED;
+  if (attn_grid_status(h_q / h_kv, h_kv, n) != VS_OK) return VS_ERR_UNSUPPORTED;
   if (ws_bytes < vs_attn_workspace_bytes(h_kv, n, cap_v, cap_s)) return VS_ERR_WORKSPACE;
   return from_hip(launch_attn(q, k, v, dt == VS_F32, h_q, h_kv, n, d, scale, v_idx, v_cnt, cap_v,
                               s_off, s_cnt, cap_s, out, lse, ws, stream));
@@ -132,7 +144,7 @@ vs_status check_attn_common(const void* q, const void* k, const void* v, vs_dtyp
   if (dt != VS_BF16 && dt != VS_F32) return VS_ERR_INVALID;
   if (h_q <= 0 || h_kv <= 0 || d <= 0 || h_q % h_kv) return VS_ERR_INVALID;
   if (cap_v < 1 || cap_s < 1) return VS_ERR_INVALID;
-  if (!(scale > 0.f) || !isfinite(scale)) return VS_ERR_INVALID;
+  if (!isfinite(scale)) return VS_ERR_INVALID;
   if (!group_ok(h_q, h_kv)) return VS_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return VS_ERR_UNSUPPORTED;
   return VS_OK;
@@ -151,6 +163,7 @@ vs_status vs_sparse_attn_prefill_qh(const void* q, const void* k, const void* v,
   if (st != VS_OK) return st;
   if (n <= 0 || (long long)n > (1LL << 30) || (long long)h_q * n * d > (1LL << 40)) return VS_ERR_INVALID;
   if ((long long)n * d * (dt == VS_F32 ? 4 : 2) >= (1LL << 31)) return VS_ERR_UNSUPPORTED;
+  if (attn_grid_status(1, h_q, n) != VS_OK) return VS_ERR_UNSUPPORTED;
   if (ws_bytes < vs_attn_workspace_bytes(h_q, n, cap_v, cap_s)) return VS_ERR_WORKSPACE;
   AttnLayout lay;
   lay.kvdiv = h_q / h_kv;
@@ -170,15 +183,20 @@ vs_status vs_sparse_attn_prefill_varlen(const void* q, const void* k, const void
   if (st != VS_OK) return st;
   if (nseq <= 0 || total_n <= 0 || (long long)h_q * total_n * d > (1LL << 40)) return VS_ERR_INVALID;
   if (cu_seqlens[0] != 0 || cu_seqlens[nseq] != total_n) return VS_ERR_INVALID;
+  const int sets = sets_per_query_head ? h_q : h_kv;
+  const int group = h_q / sets;
   int max_len = 0;
+  long long wgs = 0;
   for (int s = 0; s < nseq; ++s) {
     const int len = cu_seqlens[s + 1] - cu_seqlens[s];
     if (len < 0) return VS_ERR_INVALID;
     if (len > max_len) max_len = len;
+    wgs += attn_workgroups(group, sets, len);
   }
   if ((long long)max_len * d * (dt == VS_F32 ? 4 : 2) >= (1LL << 31)) return VS_ERR_UNSUPPORTED;
-  const int sets = sets_per_query_head ? h_q : h_kv;
   if ((long long)nseq * sets > INT_MAX / 2) return VS_ERR_UNSUPPORTED;
+  if (!grid_fits((long long)nseq * sets, kBuildThreads) || !grid_fits(wgs, kAttnThreads))
+    return VS_ERR_UNSUPPORTED;
   if (ws_bytes < vs_attn_varlen_workspace_bytes(sets, nseq, max_len, cap_v, cap_s))
     return VS_ERR_WORKSPACE;
   return from_hip(launch_attn_varlen(q, k, v, dt == VS_F32, h_q, sets,
@@ -203,11 +221,13 @@ vs_status vs_attn_aggregate(const void* q, const void* k, const void* v, int h_q
                             void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !out || !lse || !a_v || !a_s || !ws) return VS_ERR_INVALID;
   if (h_q <= 0 || h_kv <= 0 || n <= 0 || d <= 0 || h_q % h_kv) return VS_ERR_INVALID;
-  if (!(scale > 0.f) || !isfinite(scale)) return VS_ERR_INVALID;
+  if (!isfinite(scale)) return VS_ERR_INVALID;
   if ((long long)n > (1LL << 30) || (long long)h_kv * n * d > (1LL << 40)) return VS_ERR_INVALID;
   if (!group_ok(h_q, h_kv)) return VS_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return VS_ERR_UNSUPPORTED;
   if ((long long)n * d * 2 >= (1LL << 31)) return VS_ERR_UNSUPPORTED;
+  if (h_kv > 65535 || !aggregate_grid_fits(h_q, h_kv, n)) return VS_ERR_UNSUPPORTED;
+  if (attn_grid_status(h_q / h_kv, h_kv, n) != VS_OK) return VS_ERR_UNSUPPORTED;
   if (ws_bytes < vs_aggregate_workspace_bytes(h_kv, n)) return VS_ERR_WORKSPACE;
   return from_hip(launch_aggregate(q, k, v, h_q, h_kv, n, d, scale, out, lse, a_v, a_s, ws, stream));
 }
@@ -222,7 +242,7 @@ vs_status vs_block_discover(const void* q, const void* k, int h_q, int h_kv, int
                             float* score, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !mask || !ws) return VS_ERR_INVALID;
   if (h_q <= 0 || h_kv <= 0 || n <= 0 || d <= 0 || h_q % h_kv) return VS_ERR_INVALID;
-  if (!(scale > 0.f) || !isfinite(scale)) return VS_ERR_INVALID;
+  if (!isfinite(scale)) return VS_ERR_INVALID;
   if (!(alpha > 0.f && alpha <= 1.f)) return VS_ERR_INVALID;
   if (skel < 1 || skel > kBN || kBN % skel) return VS_ERR_INVALID;
   if ((long long)n > (1LL << 30) || (long long)h_q * n * d > (1LL << 40)) return VS_ERR_INVALID;
@@ -232,6 +252,7 @@ vs_status vs_block_discover(const void* q, const void* k, int h_q, int h_kv, int
   if (d != 64 && d != 128) return VS_ERR_UNSUPPORTED;
   if ((h_q / h_kv) * skel > 32) return VS_ERR_UNSUPPORTED;
   if (nb > kBlkMaxBlocks) return VS_ERR_UNSUPPORTED;
+  if (h_kv > 65535 || !block_discover_grid_fits(h_kv, n)) return VS_ERR_UNSUPPORTED;
   if (ws_bytes < vs_block_workspace_bytes(h_kv, n, d)) return VS_ERR_WORKSPACE;
   return from_hip(launch_block_discover(q, k, h_q, h_kv, n, d, scale, skel, alpha, mask,
                                         words_per_row, score, ws, stream));
@@ -246,7 +267,7 @@ vs_status vs_block_attn_prefill(const void* q, const void* k, const void* v, vs_
   if (!q || !k || !v || !mask || !out || !ws) return VS_ERR_INVALID;
   if (dt != VS_BF16 && dt != VS_F32) return VS_ERR_INVALID;
   if (h_q <= 0 || h_kv <= 0 || n <= 0 || d <= 0 || h_q % h_kv) return VS_ERR_INVALID;
-  if (!(scale > 0.f) || !isfinite(scale)) return VS_ERR_INVALID;
+  if (!isfinite(scale)) return VS_ERR_INVALID;
   // block indices travel in 24 bits beside per-query-block flags
   if ((long long)n > (1LL << 30) - kBN || (long long)h_kv * n * d > (1LL << 40)) return VS_ERR_INVALID;
   const long long nb = ((long long)n + kBN - 1) / kBN;
@@ -254,6 +275,7 @@ vs_status vs_block_attn_prefill(const void* q, const void* k, const void* v, vs_
   if (!group_ok(h_q, h_kv)) return VS_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return VS_ERR_UNSUPPORTED;
   if ((long long)n * d * (dt == VS_F32 ? 4 : 2) >= (1LL << 31)) return VS_ERR_UNSUPPORTED;
+  if (!grid_fits(attn_workgroups(h_q / h_kv, h_kv, n), kAttnThreads)) return VS_ERR_UNSUPPORTED;
   if (ws_bytes < vs_block_attn_workspace_bytes()) return VS_ERR_WORKSPACE;
   return from_hip(launch_attn_blocks(q, k, v, dt == VS_F32, h_q, h_kv, n, d, scale, mask,
                                      words_per_row, out, lse, ws, stream));

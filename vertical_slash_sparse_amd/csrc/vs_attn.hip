@@ -120,17 +120,19 @@ __global__ void ws_setbits_kernel(const int32_t* __restrict__ v_idx, const int32
                                   const int* __restrict__ lens, int sets,
                                   uint32_t* bitO, uint32_t* bitV, int stride) {
   const int g = blockIdx.x;
-  const int t = blockIdx.y * blockDim.x + threadIdx.x;
   if (lens) n = lens[g / sets];
   const int cv = min(max(v_cnt[g], 0), cap_v);
   const int cs = min(max(s_cnt[g], 0), cap_s);
-  if (t < cv) {
-    int x = v_idx[(size_t)g * cap_v + t];
-    if (x >= 0 && x < n) atomicOr(&bitV[(size_t)g * stride + kPrePad + (x >> 5)], 1u << (x & 31));
-  }
-  if (t < cs) {
-    int x = s_off[(size_t)g * cap_s + t];
-    if (x >= 0 && x < n) atomicOr(&bitO[(size_t)g * stride + kPrePad + (x >> 5)], 1u << (x & 31));
+  const int step = gridDim.y * blockDim.x;
+  for (int t = blockIdx.y * blockDim.x + threadIdx.x; t < max(cv, cs); t += step) {
+    if (t < cv) {
+      int x = v_idx[(size_t)g * cap_v + t];
+      if (x >= 0 && x < n) atomicOr(&bitV[(size_t)g * stride + kPrePad + (x >> 5)], 1u << (x & 31));
+    }
+    if (t < cs) {
+      int x = s_off[(size_t)g * cap_s + t];
+      if (x >= 0 && x < n) atomicOr(&bitO[(size_t)g * stride + kPrePad + (x >> 5)], 1u << (x & 31));
+    }
   }
 }
 
@@ -222,7 +224,12 @@ struct AttnParams {
   void* out;
   float* lse;
   int n, hkv, group, hpw, nsplit, nblocks, bmp;
-  float c;  // scale * log2(e)
+  float c;  // |scale| * log2(e), or log2(e) when scale is 0
+  // The sign of the scale is folded into Q as it is loaded: each bf16 pair
+  // of Q becomes (q & qand) ^ qxor, so that the scores the softmax sees are
+  // scale * q.k with a positive multiplier c (qxor flips both signs for a
+  // negative scale; qand = 0 makes every score 0 for a zero scale).
+  uint32_t qand, qxor;
   const uint32_t* bitO;
   const uint32_t* bitV;
   int stride;
@@ -397,6 +404,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 raw = load8<F32>(p.q, ro + 16 * s + 8 * half);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw[e] = (raw[e] & p.qand) ^ p.qxor;
       if (qrow >= n) raw = u32x4{0u, 0u, 0u, 0u};
       qf[s] = as_bf16x8(raw);
     }
@@ -1196,11 +1205,24 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 
 int heads_per_block(int group) { return group < kWaves ? group : kWaves; }
 
+// the softmax multiplier and the Q transform of a (finite) scale
+void set_scale(AttnParams& prm, float scale) {
+  prm.c = (scale == 0.f ? 1.f : fabsf(scale)) * kLog2e;
+  prm.qand = scale == 0.f ? 0u : ~0u;
+  prm.qxor = scale < 0.f ? 0x80008000u : 0u;
+}
+
 }  // namespace
 
 int attn_query_rows_per_block(int group) {
   (void)group;
   return 32 * kWaves;
+}
+
+long long attn_workgroups(int group, int sets, long long n) {
+  const int hpw = heads_per_block(group);
+  const int bmp = 32 * (kWaves / hpw);
+  return (n + bmp - 1) / bmp * sets * (group / hpw);
 }
 
 namespace {
@@ -1246,7 +1268,7 @@ hipError_t run_attn(const void* q, const void* k, const void* v, bool f32, int h
                        dim3(256), 0, stream, bitO, bitV, nwords, stats);
   }
   const int capm = std::max(cap_v, cap_s);
-  hipLaunchKernelGGL(ws_setbits_kernel, dim3((unsigned)rows, (unsigned)((capm + 255) / 256)),
+  hipLaunchKernelGGL(ws_setbits_kernel, dim3((unsigned)rows, (unsigned)std::min((capm + 255) / 256, 4096)),
                      dim3(256), 0, stream, v_idx, v_cnt, cap_v, s_off, s_cnt, cap_s, n, pk.lens,
                      pk.sets, bitO, bitV, L.stride);
   hipLaunchKernelGGL(ws_scan_kernel, dim3((unsigned)rows), dim3(1024), 0, stream, bitO, bitV,
@@ -1271,7 +1293,7 @@ hipError_t run_attn(const void* q, const void* k, const void* v, bool f32, int h
   prm.nsplit = nsplit;
   prm.bmp = bmp;
   prm.nblocks = (n + bmp - 1) / bmp;
-  prm.c = scale * kLog2e;
+  set_scale(prm, scale);
   prm.bitO = bitO;
   prm.bitV = bitV;
   prm.stride = L.stride;
@@ -1417,7 +1439,7 @@ hipError_t launch_attn_blocks(const void* q, const void* k, const void* v, bool 
   prm.nsplit = nsplit;
   prm.bmp = bmp;
   prm.nblocks = (n + bmp - 1) / bmp;
-  prm.c = scale * kLog2e;
+  set_scale(prm, scale);
   prm.stats = stats;
   prm.blk = blk;
   prm.blk_wpr = wpr;

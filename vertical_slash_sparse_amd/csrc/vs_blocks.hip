@@ -300,6 +300,11 @@ size_t block_workspace_bytes(int h_kv, int n, int d) {
          align_up(sizeof(float) * (size_t)h_kv * nb * nb, 256);
 }
 
+bool block_discover_grid_fits(int h_kv, long long n) {
+  const long long nb = (n + kBN - 1) / kBN;
+  return (nb + kBlkWaves - 1) / kBlkWaves * h_kv * kBlkThreads < (1LL << 32) && nb * 256 < (1LL << 32);
+}
+
 hipError_t launch_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,
                                  float scale, int skel, float alpha, uint32_t* mask, int wpr,
                                  float* score, void* ws, hipStream_t stream) {

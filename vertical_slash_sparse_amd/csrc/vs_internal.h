@@ -91,8 +91,17 @@ hipError_t launch_attn_varlen(const void* q, const void* k, const void* v, bool 
                               float* lse, void* ws, hipStream_t stream);
 
 int attn_query_rows_per_block(int group);
+// workgroups of one attention launch over `sets` index-set rows of n
+// positions each (G = group query heads per set)
+long long attn_workgroups(int group, int sets, long long n);
+constexpr int kAttnThreads = 512;      // threads per attention workgroup
+constexpr int kBuildThreads = 1024;    // threads per workgroup of the per-row builder passes
+// a launch's work-items along one grid dimension must stay below 2^32
+constexpr long long kGridItems = 1LL << 32;
 
 size_t aggregate_workspace_bytes(int h_kv, int n);
+// the aggregation's own pass fits one grid dimension
+bool aggregate_grid_fits(int h_q, int h_kv, long long n);
 // block-sparse mode of the attention kernel: ws holds 32 bytes of counters
 hipError_t launch_attn_blocks(const void* q, const void* k, const void* v, bool f32, int h_q,
                               int h_kv, int n, int d, float scale, const uint32_t* blk, int wpr,
@@ -101,6 +110,7 @@ hipError_t launch_attn_blocks(const void* q, const void* k, const void* v, bool 
 // FlashPrefill block discovery
 constexpr int kBlkMaxBlocks = 16384;  // key blocks a discovery call may have
 size_t block_workspace_bytes(int h_kv, int n, int d);
+bool block_discover_grid_fits(int h_kv, long long n);
 hipError_t launch_block_discover(const void* q, const void* k, int h_q, int h_kv, int n, int d,
                                  float scale, int skel, float alpha, uint32_t* mask, int wpr,
                                  float* score, void* ws, hipStream_t stream);
@@ -127,7 +137,11 @@ hipError_t launch_select(const float* logit, int heads, int n, int kind, double 
                          unsigned long long thresh, int cap, int32_t* idx, int32_t* count, void* ws,
                          hipStream_t stream);
 
-hipError_t launch_index(const void* k, const void* v, int h_kv, int n, const void* w1,
-                        const void* w2, float* vlog, float* slog, hipStream_t stream);
+// VSIndexer: d in {64, 128}; hidden a multiple of 32 up to kIdxMaxHidden
+// (its first-layer weights are held in registers)
+constexpr int kIdxMaxHidden = 256;
+hipError_t launch_index(const void* k, const void* v, int h_kv, int n, int d, int hidden,
+                        const void* w1, const void* w2, float* vlog, float* slog,
+                        hipStream_t stream);
 
 }  // namespace vs
