@@ -38,6 +38,7 @@
 //    needed anyway, bounds each of them, so the tile's own maximum is
 //    computed only when that sum is over 2^8.
 #include <algorithm>
+#include <cfloat>
 #include <climits>
 
 #include <type_traits>
@@ -224,12 +225,12 @@ struct AttnParams {
   void* out;
   float* lse;
   int n, hkv, group, hpw, nsplit, nblocks, bmp;
-  float c;  // |scale| * log2(e), or log2(e) when scale is 0
-  // The sign of the scale is folded into Q as it is loaded: each bf16 pair
-  // of Q becomes (q & qand) ^ qxor, so that the scores the softmax sees are
-  // scale * q.k with a positive multiplier c (qxor flips both signs for a
-  // negative scale; qand = 0 makes every score 0 for a zero scale).
-  uint32_t qand, qxor;
+  // scale * log2(e) carried as a positive multiplier |c| and a sign: the sign
+  // of c is folded into Q as it is loaded (every Q element flips), so that
+  // the softmax sees scale * q.k through |c|, a free operand modifier.  A
+  // zero scale is carried as the smallest normal float: every score then
+  // rounds to 0 in the exponent, which is what a zero scale means.
+  float c;
   const uint32_t* bitO;
   const uint32_t* bitV;
   int stride;
@@ -372,7 +373,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   const int i0w = i0 + 32 * (wave / p.hpw);
   const int qrow = i0w + ql;
   const bool wave_rows = i0w < n;
-  const size_t kv_head = (size_t)(g / p.kvdiv) * p.hstride + row0;  // first K/V row of the sequence
+  const size_t hstride = (size_t)p.hstride;
+  const float cpos = fabsf(p.c);  // the softmax multiplier (an operand modifier)
+  const size_t kv_head = (size_t)(g / p.kvdiv) * hstride + row0;  // first K/V row of the sequence
 
   const uint32_t* bo = p.bitO + (size_t)wr * p.stride + kPrePad;
   const uint32_t* bv = p.bitV + (size_t)wr * p.stride + kPrePad;
@@ -400,12 +403,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   auto load_q = [&]() {
     if (q_ready) return;
     q_ready = true;
-    const size_t ro = ((size_t)head * p.hstride + row0 + min(qrow, n - 1)) * D;
+    const size_t ro = ((size_t)head * hstride + row0 + min(qrow, n - 1)) * D;
+    // a negative scale flips the sign of Q; the mask is formed here, not
+    // ahead of time (the empty asm keeps the compiler from hoisting it into a
+    // register held across the kernel)
+    uint32_t cbits = __float_as_uint(p.c);
+    asm volatile("" : "+s"(cbits));
+    const uint32_t qx = (cbits >> 31) * 0x80008000u;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 raw = load8<F32>(p.q, ro + 16 * s + 8 * half);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) raw[e] = (raw[e] & p.qand) ^ p.qxor;
+      for (int e = 0; e < 4; ++e) raw[e] ^= qx;
       if (qrow >= n) raw = u32x4{0u, 0u, 0u, 0u};
       qf[s] = as_bf16x8(raw);
     }
@@ -642,10 +651,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     const float nm = -m_run;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pk[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c0[2 * e], p.c, nm)),
-                        __builtin_amdgcn_exp2f(fmaf(c0[2 * e + 1], p.c, nm)));
-      pk[8 + e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c1[2 * e], p.c, nm)),
-                            __builtin_amdgcn_exp2f(fmaf(c1[2 * e + 1], p.c, nm)));
+      pk[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c0[2 * e], cpos, nm)),
+                        __builtin_amdgcn_exp2f(fmaf(c0[2 * e + 1], cpos, nm)));
+      pk[8 + e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c1[2 * e], cpos, nm)),
+                            __builtin_amdgcn_exp2f(fmaf(c1[2 * e + 1], cpos, nm)));
     }
     float ts[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -679,7 +688,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = __builtin_elementwise_maximum(mx, c1[e]);
       mx = half_max(mx);
-      const float mnew = fmaxf(m_run, mx * p.c);
+      const float mnew = fmaxf(m_run, mx * cpos);
       const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
       l_run *= alpha;
 #pragma unroll
@@ -1156,7 +1165,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if constexpr (F32) {
     if (wave_rows && qrow < n) {
-      const size_t ro = ((size_t)head * p.hstride + row0 + qrow) * D;
+      const size_t ro = ((size_t)head * hstride + row0 + qrow) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -1192,11 +1201,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(ob + r * ROWB + 16 * (c ^ (r & (OCH - 1))));
       if (wave_rows && i0w + r < n)
         *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) +
-                                  ((size_t)head * p.hstride + row0 + i0w + r) * D + 8 * c) = val;
+                                  ((size_t)head * hstride + row0 + i0w + r) * D + 8 * c) = val;
     }
   }
   if (wave_rows && qrow < n && half == 0 && p.lse)
-    p.lse[(size_t)head * p.hstride + row0 + qrow] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -__builtin_inff();
+    p.lse[(size_t)head * hstride + row0 + qrow] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -__builtin_inff();
   if (tid == 0 && p.stats) {
     atomicAdd(&p.stats[0], (unsigned long long)n_dense);
     atomicAdd(&p.stats[1], (unsigned long long)n_gath);
@@ -1205,11 +1214,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 
 int heads_per_block(int group) { return group < kWaves ? group : kWaves; }
 
-// the softmax multiplier and the Q transform of a (finite) scale
+// the signed softmax multiplier of a finite scale (see AttnParams::c)
 void set_scale(AttnParams& prm, float scale) {
-  prm.c = (scale == 0.f ? 1.f : fabsf(scale)) * kLog2e;
-  prm.qand = scale == 0.f ? 0u : ~0u;
-  prm.qxor = scale < 0.f ? 0x80008000u : 0u;
+  prm.c = scale == 0.f ? FLT_MIN : scale * kLog2e;
 }
 
 }  // namespace
@@ -1293,7 +1300,6 @@ hipError_t run_attn(const void* q, const void* k, const void* v, bool f32, int h
   prm.nsplit = nsplit;
   prm.bmp = bmp;
   prm.nblocks = (n + bmp - 1) / bmp;
-  set_scale(prm, scale);
   prm.bitO = bitO;
   prm.bitV = bitV;
   prm.stride = L.stride;
@@ -1310,6 +1316,7 @@ hipError_t run_attn(const void* q, const void* k, const void* v, bool f32, int h
   prm.blk_wpr = 0;
   prm.kvdiv = lay.kvdiv;
   prm.hstride = lay.hstride ? lay.hstride : n;
+  set_scale(prm, scale);
   prm.row0 = lay.row0;
   prm.seq_tab = pk.tab;
   prm.nseq = pk.nrun;
@@ -1439,12 +1446,12 @@ hipError_t launch_attn_blocks(const void* q, const void* k, const void* v, bool 
   prm.nsplit = nsplit;
   prm.bmp = bmp;
   prm.nblocks = (n + bmp - 1) / bmp;
-  set_scale(prm, scale);
   prm.stats = stats;
   prm.blk = blk;
   prm.blk_wpr = wpr;
   prm.kvdiv = 1;
   prm.hstride = n;
+  set_scale(prm, scale);
   prm.row0 = 0;
   const dim3 grid((unsigned)((long long)prm.nblocks * h_kv * nsplit));
   if (d == 128) {
