@@ -165,6 +165,27 @@ vs_status vs_sparse_attn_prefill(const void* q, const void* k, const void* v, vs
                                  void* out, float* lse, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* The same call for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no `ws` argument -- the workspace is a static device array of the library,
+ * VS_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held by every GPU the library
+ * runs on until the process ends.  The call allocates and frees nothing.
+ * Shapes whose vs_attn_workspace_bytes() exceeds that return
+ * VS_ERR_WORKSPACE before anything is launched (8 KV heads at n = 262144
+ * with uncapped lists need about 34 MiB).  Every call on a GPU shares that
+ * GPU's one array: calls that overlap on one GPU (other streams, other host
+ * threads) race and give wrong results; calls on one stream are ordered.
+ * The array keeps the last call's contents; the call clears what it needs
+ * with its own kernels.  Outputs and other arguments as for
+ * vs_sparse_attn_prefill; VS_ERR_HIP if the array's address cannot be had
+ * on the current device. */
+#define VS_NOALLOC_SCRATCH_BYTES (64u << 20)
+vs_status vs_sparse_attn_prefill_noalloc(const void* q, const void* k, const void* v, vs_dtype dt,
+                                         int h_q, int h_kv, int n, int d, float scale,
+                                         const int32_t* v_idx, const int32_t* v_cnt, int cap_v,
+                                         const int32_t* s_off, const int32_t* s_cnt, int cap_s,
+                                         void* out, float* lse, hipStream_t stream);
+
 /* Per-query-head index sets (the other reading of "per head": every query
  * head h has its own columns and offsets, S_i^h = { j <= i : j in V_h or
  * i - j in O_h }).  Arguments as vs_sparse_attn_prefill except that the

@@ -209,6 +209,22 @@ def test_binding_rejects_cpu_tensors():
         vsa.vs_index(x, x, torch.zeros(128, 256, dtype=torch.bfloat16), torch.zeros(2, 128, dtype=torch.bfloat16))
 
 
+def test_noalloc_checks_before_launch():
+    """The allocation-free attention entry point: null pointers, and shapes
+    whose workspace exceeds its static array, are rejected before anything
+    touches a device."""
+    L = vsa.lib()
+    p = _fake()
+    n = 1 << 20
+    assert vsa.vs_attn_workspace_bytes(8, n, n, n) > vsa.NOALLOC_SCRATCH_BYTES
+    assert L.vs_sparse_attn_prefill_noalloc(p, p, p, 0, 32, 8, n, 128, ctypes.c_float(0.1), p, p, n,
+                                            p, p, n, p, None, None) == vsa.VS_ERR_WORKSPACE
+    assert L.vs_sparse_attn_prefill_noalloc(None, p, p, 0, 32, 8, 1024, 128, ctypes.c_float(0.1), p, p, 4,
+                                            p, p, 4, p, None, None) == vsa.VS_ERR_INVALID
+    assert L.vs_sparse_attn_prefill_noalloc(p, p, p, 0, 32, 8, 1024, 128, ctypes.c_float(0.1), p, p, 0,
+                                            p, p, 4, p, None, None) == vsa.VS_ERR_INVALID
+
+
 def test_grid_limits_are_rejected_before_launch():
     """Shapes whose launches would not fit 2^32 work-items along one grid
     dimension return VS_ERR_UNSUPPORTED; the largest shapes that fit pass on

@@ -42,7 +42,8 @@ _SYMBOLS = ("vs_index", "vs_select_workspace_bytes", "vs_select", "vs_select_thr
             "vs_select_both_workspace_bytes", "vs_select_both",
             "vs_attn_workspace_bytes", "vs_attn_varlen_workspace_bytes",
             "vs_aggregate_workspace_bytes", "vs_attn_aggregate",
-            "vs_sparse_attn_prefill", "vs_sparse_attn_prefill_qh", "vs_sparse_attn_prefill_varlen",
+            "vs_sparse_attn_prefill", "vs_sparse_attn_prefill_noalloc", "vs_sparse_attn_prefill_qh",
+            "vs_sparse_attn_prefill_varlen",
             "vs_attn_tile_counts", "vs_block_workspace_bytes",
             "vs_block_discover", "vs_block_attn_workspace_bytes", "vs_block_attn_prefill",
             "vs_status_str")
@@ -88,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.vs_sparse_attn_prefill.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P, i32, P, P,
                                              i32, P, P, P, sz, P]
         L.vs_sparse_attn_prefill.restype = i32
+        L.vs_sparse_attn_prefill_noalloc.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P, i32,
+                                                     P, P, i32, P, P, P]
+        L.vs_sparse_attn_prefill_noalloc.restype = i32
         L.vs_sparse_attn_prefill_qh.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, P, P, i32, P,
                                                 P, i32, P, P, P, sz, P]
         L.vs_sparse_attn_prefill_qh.restype = i32
@@ -348,6 +352,36 @@ def vs_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                       cap_s, _ptr(out), _ptr(lse), _ptr(workspace),
                                       workspace.numel(), _stream(q, stream))
     _check("vs_sparse_attn_prefill", st)
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # the static workspace of vs_sparse_attn_prefill_noalloc, per GPU
+
+
+@_on_stream
+def vs_sparse_attn_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                   v_idx: torch.Tensor, v_cnt: torch.Tensor, s_off: torch.Tensor,
+                                   s_cnt: torch.Tensor, out: torch.Tensor, lse: torch.Tensor | None,
+                                   scale: float | None = None, stream=None):
+    """vs_sparse_attn_prefill with the library's static workspace, for callers
+    that cannot allocate: the caller passes every output (out, and lse or
+    None) and nothing is allocated here or in the library.  Calls that overlap
+    on one GPU share that workspace and race."""
+    if out is None:
+        raise ValueError("vs_sparse_attn_prefill_noalloc: the caller passes `out` (nothing is allocated)")
+    dt, dev, h_q, h_kv, n, d, out, lse = _attn_common(q, k, v, out, lse, False, None)
+    for t, nm in ((v_idx, "v_idx"), (s_off, "s_off")):
+        _need(t, nm, torch.int32, 2, dev)
+    for t, nm in ((v_cnt, "v_cnt"), (s_cnt, "s_cnt")):
+        _need(t, nm, torch.int32, 1, dev)
+    if v_idx.shape[0] != h_kv or s_off.shape[0] != h_kv or v_cnt.shape != (h_kv,) or s_cnt.shape != (h_kv,):
+        raise ValueError("vs_sparse_attn_prefill_noalloc: index lists must have h_kv rows")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib().vs_sparse_attn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), dt, h_q, h_kv, n, d, scale,
+                                              _ptr(v_idx), _ptr(v_cnt), v_idx.shape[1], _ptr(s_off),
+                                              _ptr(s_cnt), s_off.shape[1], _ptr(out), _ptr(lse),
+                                              _stream(q, stream))
+    _check("vs_sparse_attn_prefill_noalloc", st)
     return out, lse
 
 

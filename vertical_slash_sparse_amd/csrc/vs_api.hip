@@ -5,12 +5,38 @@
 #include <limits.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "vs.h"
 #include "vs_internal.h"
 
 using namespace vs;
 
+// Device memory for callers that cannot allocate: the workspace of
+// vs_sparse_attn_prefill_noalloc.  Every GPU the library runs on holds its
+// own copy until the process ends.  Host code never names the array
+// directly (on the host the name is only a stand-in): each device's address
+// comes from hipGetSymbolAddress, taken once per device.
+static __device__ __align__(256) uint8_t scratch[VS_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's copy of `scratch` (null if it cannot be had)
+void* scratch_of_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 bool group_ok(int h_q, int h_kv) {
   if (h_q <= 0 || h_kv <= 0 || h_q % h_kv) return false;
@@ -132,6 +158,24 @@ vs_status vs_sparse_attn_prefill(const void* q, const void* k, const void* v, vs
   if (ws_bytes < vs_attn_workspace_bytes(h_kv, n, cap_v, cap_s)) return VS_ERR_WORKSPACE;
   return from_hip(launch_attn(q, k, v, dt == VS_F32, h_q, h_kv, n, d, scale, v_idx, v_cnt, cap_v,
                               s_off, s_cnt, cap_s, out, lse, ws, stream));
+}
+
+vs_status vs_sparse_attn_prefill_noalloc(const void* q, const void* k, const void* v, vs_dtype dt,
+                                         int h_q, int h_kv, int n, int d, float scale,
+                                         const int32_t* v_idx, const int32_t* v_cnt, int cap_v,
+                                         const int32_t* s_off, const int32_t* s_cnt, int cap_s,
+                                         void* out, float* lse, hipStream_t stream) {
+  // the same checks as vs_sparse_attn_prefill, with the static scratch as the
+  // workspace; sizes past it are rejected before anything is launched
+  if (!q || !k || !v || !v_idx || !v_cnt || !s_off || !s_cnt || !out) return VS_ERR_INVALID;
+  if (h_q <= 0 || h_kv <= 0 || n <= 0 || cap_v < 1 || cap_s < 1) return VS_ERR_INVALID;
+  if (vs_attn_workspace_bytes(h_kv, n, cap_v, cap_s) > (size_t)VS_NOALLOC_SCRATCH_BYTES)
+    return VS_ERR_WORKSPACE;
+  void* ws = scratch_of_current_device();
+  if (!ws) return VS_ERR_HIP;
+  return vs_sparse_attn_prefill(q, k, v, dt, h_q, h_kv, n, d, scale, v_idx, v_cnt, cap_v, s_off,
+                                s_cnt, cap_s, out, lse, ws, (size_t)VS_NOALLOC_SCRATCH_BYTES,
+                                stream);
 }
 
 namespace {
