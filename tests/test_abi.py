@@ -42,7 +42,11 @@ def test_status_strings():
 
 
 def test_workspace_sizes():
-    assert vsa.vs_select_workspace_bytes(8, 131072) >= 8 * 131072 * 12
+    # per row: each chunk's largest key and counts, the decision state and one
+    # (count, mass) histogram of 2048 bins per digit pass -- no per-candidate arrays
+    per_row = vsa.vs_select_workspace_bytes(1, 131072)
+    assert 3 * 2048 * 12 < per_row < 128 * 1024
+    assert vsa.vs_select_workspace_bytes(8, 131072) >= 8 * 3 * 2048 * 12
     assert vsa.vs_select_workspace_bytes(0, 10) == 0
     a = vsa.vs_attn_workspace_bytes(8, 131072, 4096, 8192)
     b = vsa.vs_attn_workspace_bytes(8, 262144, 262144, 262144)

@@ -42,23 +42,27 @@ struct AttnWsLayout {
   }
 };
 
-constexpr int kSelChunk = 4096;  // candidates per selection workgroup
+constexpr int kSelChunk = 4096;     // candidates per selection workgroup
+constexpr int kSelStateWords = 32;  // u64 decision-state words per selection row
 
-// Device workspace of vs_select: per-candidate keys and masses, per-head
-// decision state, two digit histograms per head, and per-chunk counts.
+// Device workspace of vs_select: per row, each chunk's largest key, the
+// decision state, one (count, mass) histogram of kSelBins bins per digit pass,
+// and each chunk's published counts of candidates above and tied with the
+// K-th.
+constexpr int kSelBins = 2048;
+constexpr int kSelDigitPasses = 3;
 struct SelectWsLayout {
-  int chunks;  // workgroups per head
-  size_t off_key, off_mass, off_state, off_hcnt, off_hmass, off_cc, total;
-  SelectWsLayout(int heads, int n) {
+  int chunks;  // workgroups per row
+  size_t off_cmax, off_state, off_hcnt, off_hmass, off_slot, total;
+  SelectWsLayout(int rows, int n) {
     chunks = (n + kSelChunk - 1) / kSelChunk;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
-    off_key = take(sizeof(uint32_t) * (size_t)heads * n);
-    off_mass = take(sizeof(uint64_t) * (size_t)heads * n);
-    off_state = take(sizeof(uint64_t) * 16 * (size_t)heads);
-    off_hcnt = take(sizeof(uint32_t) * 2 * 256 * (size_t)heads);
-    off_hmass = take(sizeof(uint64_t) * 2 * 256 * (size_t)heads);
-    off_cc = take(sizeof(int32_t) * 4 * (size_t)heads * chunks);
+    off_cmax = take(sizeof(uint32_t) * (size_t)rows * chunks);
+    off_state = take(sizeof(uint64_t) * kSelStateWords * (size_t)rows);
+    off_hcnt = take(sizeof(uint32_t) * kSelDigitPasses * kSelBins * (size_t)rows);
+    off_hmass = take(sizeof(uint64_t) * kSelDigitPasses * kSelBins * (size_t)rows);
+    off_slot = take(sizeof(uint64_t) * (size_t)rows * chunks);
     total = o;
   }
 };
