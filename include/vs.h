@@ -37,9 +37,16 @@
 
 #ifdef __cplusplus
 extern "C" {
+/* In C++ the enums below get a fixed underlying type, so that any int a C
+ * caller passes (also one that names no enumerator) is a valid value and the
+ * library's range checks are well defined; in C they are plain int-sized
+ * enums, the same ABI. */
+#define VS_ENUM_BASE : int
+#else
+#define VS_ENUM_BASE
 #endif
 
-typedef enum {
+typedef enum VS_ENUM_BASE {
   VS_OK = 0,
   VS_ERR_INVALID = 1,     /* null pointer, size out of range, bad enum     */
   VS_ERR_UNSUPPORTED = 2, /* valid but not built: head dim, group size     */
@@ -47,9 +54,9 @@ typedef enum {
   VS_ERR_HIP = 4          /* a HIP launch or runtime call failed           */
 } vs_status;
 
-typedef enum { VS_BF16 = 0, VS_F32 = 1 } vs_dtype;
+typedef enum VS_ENUM_BASE { VS_BF16 = 0, VS_F32 = 1 } vs_dtype;
 
-typedef enum { VS_VERTICAL = 0, VS_SLASH = 1 } vs_kind;
+typedef enum VS_ENUM_BASE { VS_VERTICAL = 0, VS_SLASH = 1 } vs_kind;
 
 /* ------------------------------------------------------------------ indexer
  * VSIndexer (English page, section 2, "Key Components 1. VSIndexer"): a

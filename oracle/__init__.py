@@ -22,20 +22,37 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "vs_oracle.c")
-_LIB = os.path.join(_HERE, "libvs_oracle.so")
+# VS_SANITIZE=1 selects a build instrumented with AddressSanitizer and
+# UndefinedBehaviorSanitizer (clang's runtime, which the process must preload;
+# see the sanitizer test in tests/)
+SANITIZE = os.environ.get("VS_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "libvs_oracle_san.so" if SANITIZE else "libvs_oracle.so")
+_CLANG = "/opt/rocm/llvm/bin/clang"
+_CLANG_LIB = "/opt/rocm/llvm/lib"
 
 BF16, F32, F64 = 0, 1, 2
 VERTICAL, SLASH = 0, 1
 
 
-def build(force: bool = True) -> str:
-    """Compile vs_oracle.c with gcc (fp64, no FMA contraction, OpenMP)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
-                               "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, sanitize: bool | None = None) -> str:
+    """Compile vs_oracle.c with gcc (fp64, no FMA contraction, OpenMP); with
+    ``sanitize`` (default: VS_SANITIZE=1), with clang and -fsanitize=address,
+    undefined into libvs_oracle_san.so instead."""
+    sanitize = SANITIZE if sanitize is None else sanitize
+    lib_path = os.path.join(_HERE, "libvs_oracle_san.so" if sanitize else "libvs_oracle.so")
+    if force or not os.path.exists(lib_path) or os.path.getmtime(lib_path) < os.path.getmtime(_SRC):
+        tmp = lib_path + ".tmp"
+        if sanitize:
+            cmd = [_CLANG, "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                   "-ffp-contract=off", "-fno-fast-math", "-fsanitize=address,undefined",
+                   "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", _SRC, "-o", tmp,
+                   "-L" + _CLANG_LIB, "-Wl,-rpath," + _CLANG_LIB, "-lm"]
+        else:
+            cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                   "-fno-fast-math", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, lib_path)
+    return lib_path
 
 
 _lib = None

@@ -32,7 +32,10 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvs.so")
+# VS_SANITIZE=1 loads the build whose host code is instrumented with
+# AddressSanitizer and UndefinedBehaviorSanitizer (python -m
+# vertical_slash_sparse_amd.build --sanitize; clang's ASan runtime preloaded)
+LIB_PATH = os.path.join(_HERE, "libvs_san.so" if os.environ.get("VS_SANITIZE") == "1" else "libvs.so")
 
 VS_OK, VS_ERR_INVALID, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_HIP = range(5)
 VS_BF16, VS_F32 = 0, 1
