@@ -143,14 +143,23 @@ def source_digest(files):
 # workload and the digest of the kernel sources they were taken on.
 ATTN_SOURCES = ("vs_attn.hip", "vs_common.h", "vs_internal.h")
 INDEX_SOURCES = ("vs_index.hip", "vs_common.h", "vs_internal.h")
+SELECT_SOURCES = ("vs_select.hip", "vs_common.h", "vs_internal.h")
+# attention (attn_kernel) per launch; the indexer (index_kernel) per launch
 MEASURED_TRAFFIC = {
-    "zipf128k": {"digest": "9dc6c3988fa56a3b", "bytes": 19648110100},
-    "indexer128k": {"digest": "578f8b71d5c4ddc0", "bytes": 545879672},
+    "zipf128k": {"digest": "1cf988c8d0af768f", "bytes": 19649736704},
+    "clustered128k": {"digest": "1cf988c8d0af768f", "bytes": 6547533824},
+    "indexer128k": {"digest": "b4aa71a219bfdbb0", "bytes": 545918976},
+}
+# the selection chain (its five sel_* launches) per vs_select_both call
+MEASURED_SELECT_TRAFFIC = {
+    "zipf128k": {"digest": "8792d9a1f3aed9e1", "bytes": 59633664},
+    "clustered128k": {"digest": "8792d9a1f3aed9e1", "bytes": 56541184},
+    "indexer128k": {"digest": "8792d9a1f3aed9e1", "bytes": 67790848},
 }
 
 
-def recorded_traffic(workload, sources):
-    rec = MEASURED_TRAFFIC.get(workload)
+def recorded_traffic(workload, sources, table=MEASURED_TRAFFIC):
+    rec = table.get(workload)
     if rec is None or rec["digest"] != source_digest(sources):
         return None
     return rec["bytes"]
@@ -320,6 +329,21 @@ def main():
                      "src_digest": source_digest(ATTN_SOURCES)},
         "wall_s": round(wall, 3),
     }
+    if mass is not None and w1d is None:
+        # the selection alone (vs_select_both) is the part of the step before
+        # the attention; its HBM bytes come from the counters
+        sel_ms = float(np.median(pre_ms))
+        sel_bytes = recorded_traffic(args.workload, SELECT_SOURCES, MEASURED_SELECT_TRAFFIC)
+        res["select"] = {"ms": round(sel_ms, 4), "hbm_bytes": sel_bytes,
+                         "hbm_gbs": None if sel_bytes is None else round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
+                         "src_digest": source_digest(SELECT_SOURCES)}
+    if gath_t:
+        # gathered vertical tiles: K and V rows at scattered columns
+        g_bytes = float(gath_t) * keys_t * 2 * d * (2 if q.dtype == np.uint16 else 4)
+        traffic = res["roofline"]["traffic"]
+        res["gather"] = {"tiles": gath_t, "alg_bytes": g_bytes,
+                         "alg_gbs": round(g_bytes / (attn_avg * 1e-3) / 1e9, 1),
+                         "attn_hbm_gbs": None if traffic is None else round(traffic / (attn_avg * 1e-3) / 1e9, 1)}
     copy_calibration(args, torch)
     if not args.no_cpu_baseline:
         lists_np_full = lists_np
@@ -413,6 +437,8 @@ def bench_indexer(args, w, torch, vsa, workloads):
         "select_two_calls_ms": round(ms_s2, 4),
         "graph_step_ms": round(ms_graph, 4), "graph_matches_eager": graph_budgets_ok,
         "select_gbs": round(sel_bytes / (ms_s * 1e-3) / 1e9, 1),
+        "select_hbm": {"bytes": recorded_traffic("indexer128k", SELECT_SOURCES, MEASURED_SELECT_TRAFFIC),
+                       "src_digest": source_digest(SELECT_SOURCES)},
         "threshold": {"alpha": alpha, "ms": round(ms_t, 4), "kept": kept_t},
         "index_tflops": round(flops / (ms_i * 1e-3) / 1e12, 3),
         "budgets": {"vertical": budgets_v.tolist(), "slash": budgets_s.tolist()},
@@ -421,6 +447,8 @@ def bench_indexer(args, w, torch, vsa, workloads):
                      "traffic": recorded_traffic("indexer128k", INDEX_SOURCES),
                      "src_digest": source_digest(INDEX_SOURCES)},
     }
+    hb = res["select_hbm"]["bytes"]
+    res["select_hbm"]["gbs"] = None if hb is None else round(hb / (ms_s * 1e-3) / 1e9, 1)
     copy_calibration(args, torch)
     print(json.dumps(res), flush=True)
 
