@@ -282,12 +282,17 @@ __device__ __forceinline__ T ldc(const T* ptr, long idx) {
 }
 
 // XOR swizzle of the 16-byte chunks of LDS row r, chosen so that both the
-// MFMA operand reads of K (16 consecutive rows, one chunk) and the transposing
-// reads of V (4 consecutive rows, two adjacent chunks) hit distinct banks
+// MFMA operand reads of K (16 consecutive rows, one chunk: the swizzles of
+// any 16 aligned rows are distinct) and the transposing reads of V (two
+// 16-lane groups together: 4 aligned rows, four adjacent chunks 4c .. 4c+3)
+// hit distinct banks.  At d = 128 a row is 16 chunks: the row's low two bits
+// pick the block of four chunks and the next two bits the chunk within it.
+// At d = 64 a row is 8 chunks and two rows share a 256-byte bank window, so
+// the bits above the row's parity do the same within each half.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // Scheduling groups for the matrix half: npv products whose operand takes
