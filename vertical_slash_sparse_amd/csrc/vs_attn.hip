@@ -634,15 +634,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     }
   };
   // online softmax of S = (c0, c1) under the key words, in two parts so
-  // that other work of the vector half can sit between them.  probs() masks
-  // S by mode:
+  // that other work of the vector half can sit between them.  probs() forms
+  // the probabilities against the running maximum as bf16 pairs in pk (the
+  // P^T operand), masks them by mode:
   //   kMasked  every tile is masked;
   //   kTested  a tile whose key words cover all its keys in every lane (the
   //            element bits 0x0F0F0F0F of both words) skips the masks;
   //   kNoMask  the caller knows every key of the tile is selected for every
   //            row, so the key words are not even formed;
-  // then forms the probabilities against the running maximum as bf16 pairs
-  // in pk (the P^T operand) and returns the sum of the lane's share of them.
+  // and returns the sum of the lane's share of them.
   // commit() makes sure none of them exceeded 2^kTau -- the lane's sum of
   // non-negative p bounds each, so the tile's own maximum is needed only
   // when a sum exceeds that (always on a row's first tile, where the running
@@ -652,7 +652,43 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   // the next tile's key word and loads are issued, keeps both the maxima and
   // the wait for the sums off the critical path.
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  auto form_probs = [&]() -> float {
+  // Masking.  Element e of c0 (c1) is key word bit 8*(e>>2) + (e&3) of kc0
+  // (kc1).  mask_s() sets the scores of unselected keys to -inf, for the
+  // maximum; the common path masks the packed probabilities instead, two at
+  // a time: pair e of pk (elements 2e, 2e+1) sits at bits b, b+1 with
+  // b = 8*(e>>1) + 2*(e&1), and pairs e and e+4 are 16 bits apart.  Shifted
+  // left by 15-b the word has bit b at 15 and b+16 at 31; by 14-b, bit b+1 at
+  // 15 and b+17 at 31.  v_perm's sign-replicating selectors (8, 9: bits 15
+  // and 31 of the low source; 10, 11: of the high source) spread each pair's
+  // two bits over the two bf16 halves of a mask word: 24 operations for 16
+  // elements instead of 32.
+  auto needs_mask = [&](uint32_t kc0, uint32_t kc1, auto mode_c) -> bool {
+    constexpr int MODE = decltype(mode_c)::value;
+    if constexpr (MODE == kTested)
+      return __builtin_amdgcn_ballot_w64((kc0 & kc1 & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) != 0;
+    return MODE == kMasked;
+  };
+  auto mask_s = [&](uint32_t kc0, uint32_t kc1) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int bpos = 8 * (e >> 2) + (e & 3);
+      const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, bpos, 1);
+      const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, bpos, 1);
+      c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
+      c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
+    }
+  };
+  auto mask_p = [&](uint32_t kc, uint32_t* w) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = 8 * (j >> 1) + 2 * (j & 1);
+      const uint32_t lo = kc << (15 - b), hi = kc << (14 - b);
+      w[j] &= __builtin_amdgcn_perm(hi, lo, 0x0A0A0808u);
+      w[j + 4] &= __builtin_amdgcn_perm(hi, lo, 0x0B0B0909u);
+    }
+  };
+  // the probabilities of S, masked by the key words where `masked`
+  auto form_probs = [&](bool masked, uint32_t kc0, uint32_t kc1) -> float {
     const float nm = -m_run;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -661,6 +697,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       pk[8 + e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(c1[2 * e], cpos, nm)),
                             __builtin_amdgcn_exp2f(fmaf(c1[2 * e + 1], cpos, nm)));
     }
+    if (masked) {
+      mask_p(kc0, pk);
+      mask_p(kc1, pk + 8);
+    }
     float ts[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 16; ++e)
@@ -668,25 +708,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     return (ts[0] + ts[1]) + (ts[2] + ts[3]);
   };
   auto probs = [&](uint32_t kc0, uint32_t kc1, auto mode_c) -> float {
-    constexpr int MODE = decltype(mode_c)::value;
-    auto mask = [&]() {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int bpos = 8 * (e >> 2) + (e & 3);
-        const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)kc0, bpos, 1);
-        const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)kc1, bpos, 1);
-        c0[e] = __uint_as_float((m0 & __float_as_uint(c0[e])) | (~m0 & 0xff800000u));
-        c1[e] = __uint_as_float((m1 & __float_as_uint(c1[e])) | (~m1 & 0xff800000u));
-      }
-    };
-    if constexpr (MODE == kTested) {
-      if (__builtin_amdgcn_ballot_w64((kc0 & kc1 & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) != 0) mask();
-    }
-    if constexpr (MODE == kMasked) mask();
-    return form_probs();
+    return form_probs(needs_mask(kc0, kc1, mode_c), kc0, kc1);
   };
-  auto commit = [&](float t) {
+  auto commit = [&](float t, uint32_t kc0, uint32_t kc1, auto mode_c) {
     if (__builtin_amdgcn_ballot_w64(!(t <= kPMax))) {
+      if (needs_mask(kc0, kc1, mode_c)) mask_s(kc0, kc1);
       float mx = c0[0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) mx = __builtin_elementwise_maximum(mx, c0[e]);
@@ -701,7 +727,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
       m_run = mnew;
-      t = form_probs();
+      t = form_probs(false, 0u, 0u);  // S is masked already
     }
     l_run += t;
   };
@@ -752,10 +778,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
       __builtin_amdgcn_s_setprio(3);
       src.begin();
       const float tsum = probs(kc0, kc1, mode_c);
+      const uint32_t tk0 = kc0, tk1 = kc1;  // tile t's key words, for commit()
       if constexpr (MODE != kNoMask) src.key_word(kc0, kc1);
       src.stage_k(KREG + ((S + 3) % NST) * TILEB);
       src.stage_v(VREG + ((S + 2) % NST) * TILEB);
-      commit(tsum);
+      commit(tsum, tk0, tk1, mode_c);
       hold_dma_offsets();
       src.rotate();
       // P(t) is finished here, in the vector half, not under the products
