@@ -38,6 +38,7 @@
 //    needed anyway, bounds each of them, so the tile's own maximum is
 //    computed only when that sum is over 2^8.
 #include <algorithm>
+#include <atomic>
 #include <cfloat>
 #include <climits>
 
@@ -97,7 +98,7 @@ __global__ void ws_clear_kernel(uint32_t* bitO, uint32_t* bitV, size_t nwords,
     bitO[i] = 0u;
     bitV[i] = 0u;
   }
-  if (blockIdx.x == 0 && threadIdx.x < 4) stats[threadIdx.x] = 0ull;
+  if (blockIdx.x == 0 && threadIdx.x < kStatWords) stats[threadIdx.x] = 0ull;
 }
 
 // A packed batch's rows: sequence r / sets has lens[r / sets] positions, and
@@ -111,7 +112,7 @@ __global__ void ws_clear_rows_kernel(uint32_t* bitO, uint32_t* bitV, int stride,
     bitO[(size_t)r * stride + w] = 0u;
     bitV[(size_t)r * stride + w] = 0u;
   }
-  if (r == 0 && threadIdx.x < 4) stats[threadIdx.x] = 0ull;
+  if (r == 0 && threadIdx.x < kStatWords) stats[threadIdx.x] = 0ull;
 }
 
 // lens (packed batch) null: every row covers positions [0, n)
@@ -217,6 +218,7 @@ constexpr int kWaves = 8;               // waves per workgroup (two per SIMD)
 constexpr int kRotRows = 32;            // blocks per XCD between head rotations
 constexpr int kMasked = 0, kTested = 1, kNoMask = 2;  // softmax masking modes (see softmax)
 constexpr int kThreads = kWaves * 64;
+constexpr int kQueues = 8;  // item classes: one per XCD
 
 struct AttnParams {
   const void* q;
@@ -261,6 +263,13 @@ struct AttnParams {
   // set heads use workspace rows s * hkv .. s * hkv + hkv - 1.
   const int* seq_tab;
   int nseq;
+  // Work items (one per 64-position block of a set head and head split, in
+  // the order the mapping below gives) and their queues: workgroup w starts
+  // with item w, then claims items of its class w % 8 (the XCD it runs on
+  // when workgroups are dealt round-robin) from queue[w % 8], and once its
+  // class is exhausted, items of the other classes.
+  int nitems;
+  unsigned* queue;  // kQueues counters, zero at launch
 };
 
 template <bool F32>
@@ -343,9 +352,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   lds_u8* const kv_base = (lds_u8*)kv_lds;
 
-  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, ql = lane & 31;
+  __shared__ int next_item;
+
+  // ---- persistent loop over work items.  The claim of the next item is
+  // issued as an item starts and read when it ends, so its latency stays
+  // hidden; only when a class runs dry does the search wait on atomics.
+  const int cls = blockIdx.x % kQueues;
+  const int nwg = gridDim.x;
+  // item k of class c past the ones the grid starts with
+  auto class_item = [&](int c, unsigned k) -> long long {
+    const long long first = c < nwg ? (nwg - c + kQueues - 1) / kQueues : 0;
+    return c + (long long)kQueues * (first + k);
+  };
+  for (int item = blockIdx.x; item < p.nitems;) {
+  // lane-dependent values are formed afresh per item: hoisted out of the
+  // loop they would stay live through every pipeline
+  int tid_o = threadIdx.x;
+  asm volatile("" : "+v"(tid_o));
+  const int tid = tid_o, lane = tid & 63, half = lane >> 5, ql = lane & 31;
   const int wave = wave_uniform(tid >> 6);  // keep everything derived from it in SGPRs
-  int n = p.n, nblocks = p.nblocks, bid = blockIdx.x, wrow0 = 0;
+  unsigned claim = 0;
+  if (tid == 0) claim = atomicAdd(&p.queue[cls], 1u);
+  int n = p.n, nblocks = p.nblocks, bid = item, wrow0 = 0;
   long long row0 = p.row0;
   if (p.seq_tab) {  // the sequence of this workgroup: the last one starting at or before it
     const int* tw = p.seq_tab;
@@ -1242,9 +1270,46 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     atomicAdd(&p.stats[0], (unsigned long long)n_dense);
     atomicAdd(&p.stats[1], (unsigned long long)n_gath);
   }
+  // the next item; LDS (the rings, the list) is reused only after every
+  // wave is past this item's last read of it
+  if (tid == 0) {
+    long long nx = class_item(cls, claim);
+    for (int j = 1; nx >= p.nitems && j < kQueues; ++j) {
+      const int c = (cls + j) % kQueues;
+      nx = class_item(c, atomicAdd(&p.queue[c], 1u));
+    }
+    next_item = (int)min(nx, (long long)p.nitems);
+  }
+  __syncthreads();
+  item = __builtin_amdgcn_readfirstlane(next_item);
+  }
 }
 
 int heads_per_block(int group) { return group < kWaves ? group : kWaves; }
+
+// Workgroups of a persistent launch of `kern`: as many as the device holds
+// at once (per device, computed once), at most `items`.
+template <void (*KERN)(AttnParams)>
+unsigned persistent_grid(long long items) {
+  static std::atomic<int> slots[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int s = slots[dev].load(std::memory_order_relaxed);
+  if (s <= 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, KERN, kThreads, 0) != hipSuccess) occ = 0;
+    s = cus > 0 && occ > 0 ? cus * occ : 1024;
+    slots[dev].store(s, std::memory_order_relaxed);
+  }
+  return (unsigned)std::min<long long>(items, s);
+}
+
+template <int D, bool F32, bool BLK, bool FULL>
+void launch_attn_kernel(const AttnParams& prm, hipStream_t stream) {
+  constexpr auto kern = attn_kernel<D, F32, BLK, FULL>;
+  hipLaunchKernelGGL(kern, dim3(persistent_grid<kern>(prm.nitems)), dim3(kThreads), 0, stream, prm);
+}
 
 // the signed softmax multiplier of a finite scale (see AttnParams::c)
 void set_scale(AttnParams& prm, float scale) {
@@ -1354,25 +1419,26 @@ hipError_t run_attn(const void* q, const void* k, const void* v, bool f32, int h
   prm.nseq = pk.nrun;
   const long long wgs = pk.tab ? pk.wgs : (long long)prm.nblocks * h_kv * nsplit;
   if (wgs <= 0) return hipSuccess;
-  const dim3 grid((unsigned)wgs);
+  prm.nitems = (int)wgs;
+  prm.queue = reinterpret_cast<unsigned*>(stats + 4);
   // a caller that knows most tiles are full (every offset selected) takes
   // the instantiation that skips their masks
   const bool dense = lay.full_tiles;
   if (d == 128) {
     if (dense) {
-      if (f32) hipLaunchKernelGGL((attn_kernel<128, true, false, true>), grid, dim3(kThreads), 0, stream, prm);
-      else hipLaunchKernelGGL((attn_kernel<128, false, false, true>), grid, dim3(kThreads), 0, stream, prm);
+      if (f32) launch_attn_kernel<128, true, false, true>(prm, stream);
+      else launch_attn_kernel<128, false, false, true>(prm, stream);
     } else {
-      if (f32) hipLaunchKernelGGL((attn_kernel<128, true, false, false>), grid, dim3(kThreads), 0, stream, prm);
-      else hipLaunchKernelGGL((attn_kernel<128, false, false, false>), grid, dim3(kThreads), 0, stream, prm);
+      if (f32) launch_attn_kernel<128, true, false, false>(prm, stream);
+      else launch_attn_kernel<128, false, false, false>(prm, stream);
     }
   } else {
     if (dense) {
-      if (f32) hipLaunchKernelGGL((attn_kernel<64, true, false, true>), grid, dim3(kThreads), 0, stream, prm);
-      else hipLaunchKernelGGL((attn_kernel<64, false, false, true>), grid, dim3(kThreads), 0, stream, prm);
+      if (f32) launch_attn_kernel<64, true, false, true>(prm, stream);
+      else launch_attn_kernel<64, false, false, true>(prm, stream);
     } else {
-      if (f32) hipLaunchKernelGGL((attn_kernel<64, true, false, false>), grid, dim3(kThreads), 0, stream, prm);
-      else hipLaunchKernelGGL((attn_kernel<64, false, false, false>), grid, dim3(kThreads), 0, stream, prm);
+      if (f32) launch_attn_kernel<64, true, false, false>(prm, stream);
+      else launch_attn_kernel<64, false, false, false>(prm, stream);
     }
   }
   return hipGetLastError();
@@ -1485,13 +1551,16 @@ hipError_t launch_attn_blocks(const void* q, const void* k, const void* v, bool 
   prm.hstride = n;
   set_scale(prm, scale);
   prm.row0 = 0;
-  const dim3 grid((unsigned)((long long)prm.nblocks * h_kv * nsplit));
+  const long long wgs = (long long)prm.nblocks * h_kv * nsplit;
+  if (wgs <= 0) return hipSuccess;
+  prm.nitems = (int)wgs;
+  prm.queue = reinterpret_cast<unsigned*>(stats + 4);
   if (d == 128) {
-    if (f32) hipLaunchKernelGGL((attn_kernel<128, true, true, true>), grid, dim3(kThreads), 0, stream, prm);
-    else hipLaunchKernelGGL((attn_kernel<128, false, true, true>), grid, dim3(kThreads), 0, stream, prm);
+    if (f32) launch_attn_kernel<128, true, true, true>(prm, stream);
+    else launch_attn_kernel<128, false, true, true>(prm, stream);
   } else {
-    if (f32) hipLaunchKernelGGL((attn_kernel<64, true, true, true>), grid, dim3(kThreads), 0, stream, prm);
-    else hipLaunchKernelGGL((attn_kernel<64, false, true, true>), grid, dim3(kThreads), 0, stream, prm);
+    if (f32) launch_attn_kernel<64, true, true, true>(prm, stream);
+    else launch_attn_kernel<64, false, true, true>(prm, stream);
   }
   return hipGetLastError();
 }

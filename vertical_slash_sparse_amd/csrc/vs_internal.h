@@ -12,6 +12,9 @@ constexpr int kBN = 64;          // keys per attention tile
 constexpr int kPrePad = 4;       // zero words before each bitmap (windows may start below 0)
 constexpr int kPostPad = 8;      // zero words after each bitmap (windows may run past n)
 constexpr int kListCap = 2048;   // LDS list of gathered columns per refill
+// u64 words of an attention call's counters: tile counts [0, 2), unused
+// [2, 4), the work-item queues (8 u32) [4, 8)
+constexpr int kStatWords = 8;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -36,7 +39,7 @@ struct AttnWsLayout {
     off_clLo = take(sizeof(int32_t) * (size_t)h_kv * cap_s);
     off_clHi = take(sizeof(int32_t) * (size_t)h_kv * cap_s);
     off_counts = take(sizeof(int32_t) * 4 * (size_t)h_kv);
-    off_stats = take(sizeof(unsigned long long) * 4);
+    off_stats = take(sizeof(unsigned long long) * kStatWords);
     off_tab = take(sizeof(int32_t) * (size_t)tab_ints);
     total = o;
   }
