@@ -129,13 +129,20 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
   const bool probe = active && slot_head < p.group && prow < n;
   const int rows_in = active ? min(p.skel, (n - I * kBN + step - 1) / step) : 1;
   const float weight = 1.f / (float)(p.group * rows_in);
+  // The probes enter with the sign of the scale folded in (every element
+  // flips when it is negative), so that logits are products with |c| and a
+  // chunk's largest logit is |c| times its largest product.
+  const float cpos = fabsf(p.c);
   bf16x8 qf[KS];
   {
     const int h = g * p.group + min(slot_head, p.group - 1);
     const size_t ro = ((size_t)h * n + min(prow, n - 1)) * D;
+    const uint32_t qx = p.c < 0.f ? 0x80008000u : 0u;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 raw = *reinterpret_cast<const u32x4*>(p.q + ro + 16 * s + 8 * half);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw[e] ^= qx;
       if (!probe) raw = u32x4{0u, 0u, 0u, 0u};
       qf[s] = as_bf16x8(raw);
     }
@@ -206,18 +213,29 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
     for (int s = 0; s < KS; ++s) acc = mfma32(kfrag(st, 0, s), qf[s], acc);
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = mfma32(kfrag(st, 1, s), qf[s], acc);
-    float z[16];
-    float mloc = kNegBig;
+    float mn, add = 0.f;
+    if (32 * c + 32 <= I) {
+      // every block of the chunk lies below I: no masks
+      float a = acc[0];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int J = c * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-      z[e] = J < I ? acc[e] * p.c : kNegBig;
-      mloc = fmaxf(mloc, z[e]);
+      for (int e = 1; e < 16; ++e) a = fmaxf(a, acc[e]);
+      mn = fmaxf(m2, a * cpos);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) add += __builtin_amdgcn_exp2f(fmaf(acc[e], cpos, -mn));
+    } else {
+      float mloc = kNegBig;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int J = c * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (J < I) mloc = fmaxf(mloc, acc[e] * cpos);
+      }
+      mn = fmaxf(m2, mloc);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int J = c * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+        add += J < I ? __builtin_amdgcn_exp2f(fmaf(acc[e], cpos, -mn)) : 0.f;
+      }
     }
-    const float mn = fmaxf(m2, mloc);
-    float add = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) add += z[e] > kNegBig ? __builtin_amdgcn_exp2f(z[e] - mn) : 0.f;
     l = l * __builtin_amdgcn_exp2f(m2 - mn) + add;
     m2 = mn;
   });
@@ -257,7 +275,7 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
     for (int s = 0; s < KS; ++s) acc = mfma32(qf[s], kfrag(st, 1, s), acc);
     float t = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) t = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[e], p.c, nm[e])), wl[e], t);
+    for (int e = 0; e < 16; ++e) t = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[e], cpos, nm[e])), wl[e], t);
     return half_sum(t);
   };
   // pass 2 keeps each score in its lane's slot of the workspace row (lanes
