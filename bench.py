@@ -166,15 +166,15 @@ INDEX_SOURCES = ("vs_index.hip", "vs_common.h", "vs_internal.h")
 SELECT_SOURCES = ("vs_select.hip", "vs_common.h", "vs_internal.h")
 # attention (attn_kernel) per launch; the indexer (index_kernel) per launch
 MEASURED_TRAFFIC = {
-    "zipf128k": {"digest": "1cf988c8d0af768f", "bytes": 19649736704},
-    "clustered128k": {"digest": "1cf988c8d0af768f", "bytes": 6547533824},
-    "indexer128k": {"digest": "b4aa71a219bfdbb0", "bytes": 545918976},
+    "zipf128k": {"digest": "2ee22cd71b586e4e", "bytes": 19811851519},
+    "clustered128k": {"digest": "2ee22cd71b586e4e", "bytes": 6605272034},
+    "indexer128k": {"digest": "445b0619712ee8ee", "bytes": 545910520},
 }
 # the selection chain (its five sel_* launches) per vs_select_both call
 MEASURED_SELECT_TRAFFIC = {
-    "zipf128k": {"digest": "8792d9a1f3aed9e1", "bytes": 59633664},
-    "clustered128k": {"digest": "8792d9a1f3aed9e1", "bytes": 56541184},
-    "indexer128k": {"digest": "8792d9a1f3aed9e1", "bytes": 67790848},
+    "zipf128k": {"digest": "296dd528ad02ad74", "bytes": 59621332},
+    "clustered128k": {"digest": "296dd528ad02ad74", "bytes": 56550036},
+    "indexer128k": {"digest": "296dd528ad02ad74", "bytes": 67790356},
 }
 
 
