@@ -45,7 +45,7 @@ struct AttnWsLayout {
   }
 };
 
-constexpr int kSelChunk = 4096;     // candidates per selection workgroup
+constexpr int kSelChunk = 8192;     // candidates per selection workgroup
 constexpr int kSelStateWords = 32;  // u64 decision-state words per selection row
 
 // Device workspace of vs_select: per row, each chunk's largest key, the

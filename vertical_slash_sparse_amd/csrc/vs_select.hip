@@ -48,7 +48,7 @@ namespace vs {
 
 namespace {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kPasses = 3;        // digits of the 32-bit key: bits 21..31, 10..20, 0..9
 constexpr int kBins = kSelBins;   // histogram bins of a pass (the last uses 1024)
@@ -202,7 +202,7 @@ __device__ __forceinline__ RowRef row_ref(const SelArgs& a, int r) {
 }
 
 // The scores of one chunk, with -0 made +0, kPer per thread: thread t holds
-// candidates c0 + 256 j + t.  All the loads are issued before any is used,
+// candidates c0 + kSelThreads j + t.  All the loads are issued before any is used,
 // so a pass waits for one memory latency instead of kPer; slots past n hold
 // NaN (no comparison with NaN is true, so they are never candidates).
 constexpr int kPer = kSelChunk / kSelThreads;
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_write_kernel(SelArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const RowRef rr = row_ref(a, r);
   const unsigned long long* st = a.state + (size_t)kSelStateWords * r;
-  // the chunk's scores arrive coalesced (candidate c0 + 256 j + t in thread
+  // the chunk's scores arrive coalesced (candidate c0 + kSelThreads j + t in thread
   // t) and are moved through LDS to thread t's own run c0 + kPer t ..: the
   // element of run T at place J sits in slot kPer T + (J ^ (T >> 2)), which
   // keeps both the writes and the reads free of bank conflicts
