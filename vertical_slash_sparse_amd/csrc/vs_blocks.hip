@@ -18,11 +18,11 @@
 //    rows, then the row groups meet in LDS) and stores the mean as a bf16
 //    pair hi + lo (hi = bf16(mean), lo = bf16(mean - hi)), about 16
 //    significant bits, so the matrix cores can take it.
-//  * blk_score_kernel: one wave per query block, four per workgroup.  The
+//  * blk_score_kernel: one wave per query block, eight per workgroup.  The
 //    wave's 32 probe rows (G heads x skel rows, zero-padded) are one MFMA
 //    operand held in registers; the block means pass through LDS in chunks
 //    of 32 blocks (hi and lo, 16 KiB at d = 128), brought in once per
-//    workgroup by LDS-DMA two stages deep and read by all four waves, whose
+//    workgroup by LDS-DMA two stages deep and read by all eight waves, whose
 //    query blocks need nearly the same chunks.  Pass 1 runs
 //    S^T = Kbar Q^T, so each lane owns one probe and keeps its running max
 //    and sum over blocks; passes 2 and 3 run S = Q Kbar^T, so each lane owns
@@ -39,7 +39,7 @@ namespace vs {
 
 namespace {
 
-constexpr int kBlkWaves = 4;  // query blocks per workgroup
+constexpr int kBlkWaves = 8;  // query blocks per workgroup
 constexpr int kBlkThreads = kBlkWaves * 64;
 constexpr float kNegBig = -1.0e30f;
 
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kBlkThreads) void blk_score_kernel(BlkParams p) {
   }
 
   // chunk c = mean keys of blocks 32 c .. 32 c + 31 of head g, hi and lo,
-  // brought into stage st by the four waves (rows past nb arrive as zeros)
+  // brought into stage st by the eight waves (rows past nb arrive as zeros)
   const uint32_t tab_bytes = (uint32_t)((size_t)p.hkv * nb * ROWB);
   const u32x4 whi = buffer_words(p.khi, tab_bytes);
   const u32x4 wlo = buffer_words(p.klo, tab_bytes);
