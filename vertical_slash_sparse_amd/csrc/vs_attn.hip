@@ -52,8 +52,10 @@ namespace vs {
 
 namespace {
 
-constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
-constexpr float kPMax = 256.0f;         // 2^kTau: the largest p the running maximum allows
+// lazy rescale: the largest p (2^8, so 8 in log2 units above the running
+// maximum) a tile may reach before the maximum is moved; 2^16 measured the
+// same, as the maximum rarely moves after a row's first tile
+constexpr float kPMax = 256.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNoMax = -1.0e30f;      // running max before any key was seen
@@ -671,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     //   kNoMask  the caller knows every key of the tile is selected for every
     //            row, so the key words are not even formed;
     // and returns the sum of the lane's share of them.
-    // commit() makes sure none of them exceeded 2^kTau -- the lane's sum of
+    // commit() makes sure none of them exceeded kPMax -- the lane's sum of
     // non-negative p bounds each, so the tile's own maximum is needed only
     // when a sum exceeds that (always on a row's first tile, where the running
     // maximum is still kNoMax, and rarely afterwards); then it moves the
