@@ -132,6 +132,30 @@ def test_value_ones_gives_ones():
     assert (out[~nonempty] == 0).all()
 
 
+def _grid_cases():
+    # work items are (KV head, 64-row block) pairs; the kernel's persistent
+    # grid holds one workgroup per CU: item counts just past one and two
+    # grids (the per-XCD queues, then stealing), and fewer items than queues
+    cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+    m1 = cus // 8 + 1
+    return [(8, 32, 64 * m1), (8, 32, 64 * (2 * m1) - 17), (1, 4, 64 * 5 - 3)]
+
+
+@pytest.mark.parametrize("case", _grid_cases(), ids=lambda c: f"h{c[1]}x{c[0]}-n{c[2]}")
+def test_item_counts_around_the_persistent_grid(case):
+    """Every item is taken exactly once: item counts past one and two grids
+    of workgroups and below the number of queues, with uneven work per item
+    (random sets), compared in full with the oracle."""
+    hkv, hq, n = case
+    _log(f"case: persistent grid items {case}")
+    rng = np.random.default_rng(n + hkv)
+    q, k, v = _inputs(rng, hq, hkv, n, 128, "bf16")
+    lists = _random_sets(rng, hkv, n, 0.03, 0.05)
+    out, lse = _run_gpu(q, k, v, *lists)
+    ro, rl = oracle.attn(q, k, v, *lists)
+    assert_attn_close(out, lse, ro, rl, f"grid items {case}")
+
+
 def test_index_list_contract():
     """Lists may come in any order; duplicates and out-of-range entries are
     ignored; counts beyond the capacity are clamped."""
