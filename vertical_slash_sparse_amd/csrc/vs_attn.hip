@@ -291,6 +291,11 @@ template <typename T>
 __device__ __forceinline__ T ldc(const T* ptr, long idx) {
   return ((const __attribute__((address_space(4))) T*)ptr)[idx];
 }
+// the same at a 32-bit byte offset, which the load takes as a register offset
+template <typename T>
+__device__ __forceinline__ T ldc_at(const T* ptr, unsigned byte_off) {
+  return *(const __attribute__((address_space(4))) T*)((const __attribute__((address_space(4))) char*)ptr + byte_off);
+}
 
 // XOR swizzle of the 16-byte chunks of LDS row r, chosen so that both the
 // MFMA operand reads of K (16 consecutive rows, one chunk: the swizzles of
@@ -346,7 +351,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   static_assert(NDMA >= 1 && NDMA * RPD * kWaves == kBN, "tile split");
   // K stages at [0, NST*TILEB), V stages at [NST*TILEB, 2*NST*TILEB)
   __shared__ __align__(16) uint8_t kv_lds[2 * NST * TILEB];
-  __shared__ __align__(16) int glist[kListCap];
+  // four spare entries: the pipelines read the code of step t+4 without a clamp
+  __shared__ __align__(16) int glist[kListCap + 4];
   __shared__ int wcnt[kWaves + 1];
   // per cluster of one batch while a window of the tile list is written: its
   // first slot in the window, and its tiles as ranges [a, a + b) then c ..
@@ -512,12 +518,38 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         }
       }
     };
-    // contiguous tile `code` (keys code*64 ..)
-    auto stage_tile = [&](int which, int code, int dst) {
-      int key[NDMA];
+    // contiguous tile `code` (keys code*64 ..): the lane's offset within a
+    // tile is fixed, so only the tile's wave-uniform base changes per call
+    unsigned dma_lane[NDMA];
 #pragma unroll
-      for (int i = 0; i < NDMA; ++i) key[i] = code * kBN + dma_row[i];
-      stage_keys(which, key, dst);
+    for (int i = 0; i < NDMA; ++i) dma_lane[i] = (unsigned)dma_row[i] * GROWB + dma_col[i];
+    auto stage_tile = [&](int which, int code, int dst) {
+      if constexpr (BLK) {  // block mode measured 2 % faster with per-lane keys
+        int key[NDMA];
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) key[i] = code * kBN + dma_row[i];
+        stage_keys(which, key, dst);
+        return;
+      }
+      const unsigned tb = (unsigned)__builtin_amdgcn_readfirstlane(code) * (unsigned)(kBN * GROWB);
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int kbase = dst + (wave * (kBN / kWaves) + i * RPD) * ROWB;
+        const unsigned off = tb + dma_lane[i];
+        if constexpr (F32) {
+          const __amdgpu_buffer_rsrc_t rs = which ? rsv : rsk;
+          const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+          const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 16), 0, 0);
+          *(__attribute__((address_space(3))) u32x4*)(kv_base + kbase + 16 * lane) =
+              u32x4{pack_bf16(__uint_as_float(a[0]), __uint_as_float(a[1])),
+                    pack_bf16(__uint_as_float(a[2]), __uint_as_float(a[3])),
+                    pack_bf16(__uint_as_float(c[0]), __uint_as_float(c[1])),
+                    pack_bf16(__uint_as_float(c[2]), __uint_as_float(c[3]))};
+        } else {
+          dma16(which ? wv : wk, (uint32_t)(uintptr_t)(kv_base + kbase), off);
+          dma_off[which][i] = off;
+        }
+      }
     };
 
     // ---- key words.  Per lane, a 64-bit word K with bit kk set when key kk
@@ -531,13 +563,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     // scalar loads for contiguous tile `code`: the wave's rows need offsets
     // [i0w - j0 - 63, i0w - j0 + 31], which lie in four consecutive words
     auto load_words = [&](int code, BitWords& w) {
-      const int j0 = code * kBN;
+      const int j0 = __builtin_amdgcn_readfirstlane(code) * kBN;
       const int wq = (i0w - j0 - (kBN - 1)) >> 5;
-      const int wc = max(wq, -kPrePad);  // further below, the window holds only zeros
+      // word index counted from the start of the zero pre-pad (further
+      // below, the window holds only zeros), as a 32-bit byte offset
+      const unsigned wc = (unsigned)__builtin_amdgcn_readfirstlane((max(wq, -kPrePad) + kPrePad) * 4);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x4 o = ldc_at(reinterpret_cast<const u32x4*>(bo - kPrePad), wc);
+      const u32x2 v = ldc_at(reinterpret_cast<const u32x2*>(bv), (unsigned)j0 >> 3);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) w.o[k] = ldc(bo, wc + k);
-      w.v[0] = ldc(bv, j0 >> 5);
-      w.v[1] = ldc(bv, (j0 >> 5) + 1);
+      for (int k = 0; k < 4; ++k) w.o[k] = o[k];
+      w.v[0] = v[0];
+      w.v[1] = v[1];
     };
     auto key_word_tile = [&](int code, const BitWords& w, uint32_t& kh0, uint32_t& kh1) {
       const int j0 = code * kBN;
@@ -1019,10 +1056,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         T_total += tot;
         T_full += totf;
       }
-      // Tile codes for steps t+1, t+2, t+3 live in scalar registers; the code
-      // of t+4 is read from the LDS list one step ahead (unconditionally, from a
-      // clamped index) and the bitmap words of tile t+1 are requested at the
-      // start of the V half, so neither wait sits on the critical path.
+      // Tile codes for steps t+1, t+2, t+3 are carried from step to step; the
+      // code of t+4 is read from the LDS list one step ahead (unconditionally:
+      // past the end it reads a spare entry and is replaced by tend) and the
+      // bitmap words of tile t+1 are requested first thing in the V half, so
+      // neither wait sits on the critical path.
       struct TileSrc {
         decltype(stage_tile)& stage_fn;
         decltype(load_words)& load_fn;
@@ -1051,7 +1089,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         __device__ void key_word_first(uint32_t& k0, uint32_t& k1) { key_fn(code(0), w, k0, k1); }
         __device__ void begin() {
           load_fn(c1, w);
-          pref = list[min(t + 4, T - 1)];
+          pref = list[t + 4];
+          __builtin_amdgcn_sched_barrier(0);  // both requests go out first
         }
         __device__ void key_word(uint32_t& k0, uint32_t& k1) { key_fn(c1, w, k0, k1); }
         __device__ void stage_k(int dst) { stage_fn(0, c3, dst); }
