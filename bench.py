@@ -168,6 +168,7 @@ SELECT_SOURCES = ("vs_select.hip", "vs_common.h", "vs_internal.h")
 MEASURED_TRAFFIC = {
     "zipf128k": {"digest": "167b68659fe06d0b", "bytes": 20249448893},
     "clustered128k": {"digest": "167b68659fe06d0b", "bytes": 6617351308},
+    "e2e256k": {"digest": "167b68659fe06d0b", "bytes": 75260898592},
     "indexer128k": {"digest": "a77dd4b15c9cc635", "bytes": 545910315},
 }
 # the selection chain (its five sel_* launches) per vs_select_both call
