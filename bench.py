@@ -36,8 +36,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, the published figure
 # the same peak from unit counts: 256 CUs x 2.4 GHz x 4096 bf16 flop per clock
-# per CU; percentages are reported against both, the >= 50 % target is judged
-# on this one (the stricter)
+# per CU; percentages are reported against both, and the stricter one is the
+# one the >= 50 %-on-tiles goal is stated against
 PEAK_BF16_UNITS_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "ms/layer + effective TFLOP/s (% bf16 MFMA peak), VS sparse prefill @128K"
